@@ -1,0 +1,146 @@
+"""Oracle for block-diagonal (causal) attention over a packed THD buffer, fp64.
+
+Test infrastructure only (see the package docstring).
+
+Definition followed ([charlestar] "EOS is content": allow() and the masked
+softmax equation; [compass] "cross-contamination": the block-diagonal mask):
+  allow(i, j) = seg(i) == seg(j) and j <= i   (causal)
+  allow(i, j) = seg(i) == seg(j)              (non-causal: a reading; the pages
+                                               define only the causal mask)
+  O = softmax(Q K^T / sqrt(d) + M) V,  M = 0 where allowed, -inf elsewhere.
+
+Three forms are provided:
+  attention_rows   the C loop (attn_oracle.c) for any list of query rows, used
+                   at full size on sampled rows and for the CPU baseline;
+  attention_brute  an explicit T x T additive mask in numpy, for tiny T
+                   ([charlestar] "varlen interface": an explicit 9x9 block-causal
+                   mask defines the correct result);
+  attention_unpacked  each segment run alone as one ordinary sequence
+                   ([m020] "08": packed vs per-sample execution;
+                   [charlestar] "change A, not B").
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+from .pack import segment_of
+from .rope import bf16_bits_to_f64
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIBPATH = os.path.join(_HERE, "liboracle_attn.so")
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIBPATH):
+            from .build import build
+            build()
+        lib = ctypes.CDLL(_LIBPATH)
+        p = ctypes.c_void_p
+        lib.oracle_attn_rows.argtypes = [p, p, p, p, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_int32, p, ctypes.c_int64,
+                                         p, p, p]
+        lib.oracle_attn_rows.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def attention_rows(q, k, v, cu, rows, causal: bool = True, threads: int = 1):
+    """fp64 outputs [n, H, d] and lse [n, H] for query ``rows`` (all heads).
+
+    q, k, v: uint16 bf16 bits [T, H, d].  Rows are split over ``threads`` host
+    threads; each thread runs the same plain loop on its own rows.
+    """
+    lib = _load()
+    q = np.ascontiguousarray(q, np.uint16)
+    k = np.ascontiguousarray(k, np.uint16)
+    v = np.ascontiguousarray(v, np.uint16)
+    cu32 = np.ascontiguousarray(cu, np.int32)
+    rows = np.ascontiguousarray(rows, np.int64)
+    T, H, d = q.shape
+    nseg = cu32.shape[0] - 1
+    maxlen = int((cu32[1:].astype(np.int64) - cu32[:-1]).max()) if nseg else 1
+    out = np.empty((rows.shape[0], H, d), np.float64)
+    lse = np.empty((rows.shape[0], H), np.float64)
+
+    def run(lo, hi):
+        if hi <= lo:
+            return 0
+        scratch = np.empty(max(maxlen, 1), np.float64)
+        sub_rows = rows[lo:hi]
+        o = out[lo:hi]
+        ls = lse[lo:hi]
+        return lib.oracle_attn_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(cu32), nseg, H, d,
+                                    int(bool(causal)), _ptr(sub_rows), hi - lo,
+                                    _ptr(o), _ptr(ls), _ptr(scratch))
+
+    n = rows.shape[0]
+    threads = max(1, min(int(threads), n))
+    if threads == 1:
+        rc = [run(0, n)]
+    else:
+        # interleave work in small chunks so long and short rows spread evenly
+        chunk = max(1, min(64, n // (threads * 8) or 1))
+        bounds = [(s, min(n, s + chunk)) for s in range(0, n, chunk)]
+        with ThreadPoolExecutor(threads) as ex:
+            rc = list(ex.map(lambda b: run(*b), bounds))
+    if any(rc):
+        raise ValueError("a query row lies outside every segment")
+    return out, lse
+
+
+def attention(q, k, v, cu, causal: bool = True, threads: int = 1):
+    """Every row of the buffer."""
+    T = q.shape[0]
+    return attention_rows(q, k, v, cu, np.arange(T, dtype=np.int64), causal, threads)
+
+
+def allow_matrix(cu, causal: bool = True) -> np.ndarray:
+    """bool [T, T]: allow(i, j) from segment ids and positions, element by element."""
+    cu = np.asarray(cu, np.int64)
+    T = int(cu[-1])
+    seg = [segment_of(cu, i) for i in range(T)]
+    A = np.zeros((T, T), bool)
+    for i in range(T):
+        for j in range(T):
+            A[i, j] = seg[i] == seg[j] and (j <= i or not causal)
+    return A
+
+
+def attention_brute(q, k, v, cu, causal: bool = True):
+    """Explicit additive mask: softmax(Q K^T / sqrt(d) + M) V per head, fp64 (tiny T)."""
+    Q, K, V = (bf16_bits_to_f64(x) for x in (q, k, v))
+    T, H, d = Q.shape
+    M = np.where(allow_matrix(cu, causal), 0.0, -np.inf)
+    out = np.empty((T, H, d))
+    lse = np.empty((T, H))
+    for h in range(H):
+        S = Q[:, h, :] @ K[:, h, :].T / np.sqrt(d) + M
+        m = S.max(axis=1, keepdims=True)
+        E = np.exp(S - m)
+        out[:, h, :] = (E @ V[:, h, :]) / E.sum(axis=1, keepdims=True)
+        lse[:, h] = m[:, 0] + np.log(E.sum(axis=1))
+    return out, lse
+
+
+def attention_unpacked(q, k, v, cu, causal: bool = True, threads: int = 1):
+    """Each segment alone, as a standalone sequence with cu = [0, L]."""
+    cu = np.asarray(cu, np.int64)
+    outs, lses = [], []
+    for r in range(cu.shape[0] - 1):
+        s, e = int(cu[r]), int(cu[r + 1])
+        o, ls = attention(q[s:e], k[s:e], v[s:e], np.asarray([0, e - s]), causal, threads)
+        outs.append(o)
+        lses.append(ls)
+    return np.concatenate(outs), np.concatenate(lses)
