@@ -1,0 +1,257 @@
+/*
+ * pvc.h — C ABI of libpvc: packed variable-length causal attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One packed buffer holds several independent samples back to back with no
+ * batch dimension (the THD layout: token-major [total_tokens, heads, head_dim]).
+ * Sample boundaries come from cu_seqlens, the prefix sum of the sample
+ * lengths: segment r is the token range [cu[r], cu[r+1]).  Attention is
+ * block-diagonal: a query sees only keys of its own segment, and with causal
+ * masking only keys at or before it.  Rotary positions restart at every
+ * segment: token i of segment r has position i - cu[r].
+ *
+ * Page tags used in the citations below (the pages specify the method):
+ *   [vllbc]      blog.vllbc.top  "long-context training: remove padding"
+ *   [compass]    brenchcc.github.io/llm-compass  "Sequence Packing"
+ *   [m020]       xuujii.github.io/ai-infra-kb  M020 "length grouping, de-padding, packing"
+ *   [opworld]    operatorworld.com  "packing and document boundaries"
+ *   [charlestar] charlestar.github.io  "sequence packing and variable-length attention"
+ *
+ * Conventions for every entry point
+ *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *     allocates no memory; entry points that need scratch space take a caller
+ *     workspace and report its size through a *_workspace_size query.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously; no entry point synchronizes the stream
+ *     or copies anything back to the host.
+ *   - The return value is a pvc_status for errors the host can see from the
+ *     arguments alone (null pointers, sizes, unsupported shapes, a too-small
+ *     workspace, a failed launch).  Nothing is enqueued when it is not PVC_OK.
+ *   - Errors that depend on device data (a malformed cu_seqlens) are OR-ed into
+ *     the caller's 32-bit device error word `dev_error` (PVC_DEV_* bits) when
+ *     that pointer is non-NULL; the caller zeroes it beforehand and reads it
+ *     after synchronizing.  Kernels clamp every index they derive from device
+ *     data, so bad data yields a set bit and unspecified outputs, never an
+ *     out-of-bounds access.
+ *   - bf16 tensors are IEEE bfloat16 bit patterns, row major, contiguous.
+ *   - cu_seqlens values and total_tokens fit in int32 ([charlestar] "nine
+ *     tokens, three identities": the interface takes int32 prefix sums).
+ *   - No global mutable state; per-device properties are cached once.
+ *   - Calls on different streams that write the same buffers race; the
+ *     library adds no ordering of its own beyond the stream.
+ */
+#ifndef PVC_H
+#define PVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status */
+
+typedef int32_t pvc_status;
+enum {
+    PVC_OK = 0,
+    PVC_ERR_NULL = 1,          /* a required pointer is NULL */
+    PVC_ERR_INVALID_ARG = 2,   /* a size or flag is out of range */
+    PVC_ERR_UNSUPPORTED = 3,   /* a shape the kernels do not implement (e.g. head_dim) */
+    PVC_ERR_WORKSPACE = 4,     /* workspace NULL or smaller than the size query */
+    PVC_ERR_HIP = 5            /* the HIP runtime reported an error (launch, device) */
+};
+
+/* Bits of the device error word.  The cu_seqlens contract is the one listed
+ * in [charlestar] "nine tokens, three identities": cu[0] == 0, strictly
+ * increasing (every length positive), cu[nseg] == total_tokens, max_seqlen
+ * equal to the largest difference, all values representable in int32. */
+enum {
+    PVC_DEV_CU0 = 1u,             /* cu[0] != 0 */
+    PVC_DEV_NOT_INCREASING = 2u,  /* some cu[r+1] <= cu[r] */
+    PVC_DEV_TOTAL = 4u,           /* cu[nseg] (or the sum of lengths) != total_tokens */
+    PVC_DEV_MAXSEQ = 8u,          /* a segment is longer than max_seqlen (a larger
+                                     max_seqlen is accepted) */
+    PVC_DEV_LENGTH = 16u,         /* pack_build: a sample length <= 0 */
+    PVC_DEV_MISMATCH = 32u,       /* validate: cu disagrees with the given lengths
+                                     ([charlestar]: [0,4,5,9] looks like a prefix sum
+                                     of [3,2,4] but moves b0 into A) */
+    PVC_DEV_RANGE = 64u,          /* the sum of lengths does not fit in int32 */
+    PVC_DEV_PLAN = 128u           /* attention run with a plan built for other arguments */
+};
+
+/* Static text for a status code (never NULL). */
+const char* pvc_status_string(pvc_status status);
+
+/* Library version string, e.g. "pvc 0.1.0 gfx950". */
+const char* pvc_version(void);
+
+/* ------------------------------------------------------------ pack_build */
+
+/* Bytes of device workspace pvc_pack_build needs for `nseg` samples. */
+size_t pvc_pack_build_workspace_size(int32_t nseg);
+
+/*
+ * Packing metadata for one buffer of `nseg` samples laid end to end.
+ *
+ * Computes, for r < nseg and i < total_tokens:
+ *   cu_seqlens[0] = 0, cu_seqlens[r+1] = cu_seqlens[r] + lengths[r]
+ *       ([vllbc] "three things": prefix sum of the lengths; [charlestar]
+ *        "nine tokens, three identities")
+ *   segment_ids[i]   = the r with cu[r] <= i < cu[r+1]
+ *   position_ids[i]  = i - cu[segment_ids[i]]            (reset per segment)
+ *   shifted_labels[i]= tokens[i+1] when i+1 < cu[r+1] and !is_pad[r], else
+ *                      ignore_index: next-token targets aligned to the input
+ *                      position, so a sample's last token predicts nothing
+ *                      ([m020] "06 positions and labels"; [charlestar]
+ *                      "cross-boundary prediction pairs": the pre-shifted form)
+ *   loss_mask[i]     = shifted_labels[i] != ignore_index
+ *   *num_targets     = sum of loss_mask (int64; [charlestar] "distributed
+ *                      denominator": an int64 count of valid targets)
+ *   *max_seqlen      = max(lengths)  (the longest segment, not the total)
+ * A segment with is_pad[r] != 0 is a pad tail: it keeps its own entry in
+ * cu_seqlens and all its labels are ignore_index ([compass] "implementation
+ * notes": the pad tail is closed off as its own segment with labels -100).
+ *
+ * lengths   [nseg] int32, every value > 0 (else PVC_DEV_LENGTH)
+ * is_pad    [nseg] uint8 or NULL (no pad segments)
+ * tokens    [total_tokens] int32 token ids; must not equal ignore_index.  May be
+ *           NULL when shifted_labels and loss_mask are NULL.
+ * total_tokens  the caller's T; the device checks sum(lengths) == T
+ *           (PVC_DEV_TOTAL; tokens past the last segment get segment -1,
+ *           position 0 and an ignored label)
+ * outputs   cu_seqlens [nseg+1] required; segment_ids, position_ids,
+ *           shifted_labels [T] int32, loss_mask [T] uint8, num_targets (int64
+ *           scalar), max_seqlen (int32 scalar) each optional (NULL = skip)
+ * Bit-exact: integer results only.
+ */
+pvc_status pvc_pack_build(const int32_t* lengths, const uint8_t* is_pad,
+                          const int32_t* tokens, int32_t nseg, int64_t total_tokens,
+                          int32_t ignore_index, int32_t* cu_seqlens, int32_t* segment_ids,
+                          int32_t* position_ids, int32_t* shifted_labels, uint8_t* loss_mask,
+                          int64_t* num_targets, int32_t* max_seqlen, uint32_t* dev_error,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Check a caller-supplied cu_seqlens [nseg+1] against the contract above and
+ * OR the failing PVC_DEV_* bits into *dev_error (required here).  With
+ * `lengths` [nseg] non-NULL it also checks cu[r+1] - cu[r] == lengths[r]
+ * (PVC_DEV_MISMATCH).
+ */
+pvc_status pvc_validate_cu_seqlens(const int32_t* cu_seqlens, int32_t nseg,
+                                   int64_t total_tokens, int32_t max_seqlen,
+                                   const int32_t* lengths, uint32_t* dev_error, void* stream);
+
+/* -------------------------------------------------------------- RoPE */
+
+/*
+ * Rotary position embedding with positions reset per segment, on q and
+ * (optionally) k, never v ([charlestar] "varlen interface": q and k carry the
+ * rotation before attention; [vllbc] THD RoPE recovers local positions from
+ * cu_seqlens; [opworld] "pitfall two": reset positions per document).
+ *
+ * Token i finds its segment r by binary search in cu_seqlens, position
+ * p = i - cu[r].  For each head and pair j < head_dim/2 (rotate-half pairing):
+ *   f_j   = base^(-2j/head_dim), computed in double and rounded to fp32
+ *   theta = fp32(p) * f_j                 (one fp32 product)
+ *   y_j          = x_j cos(theta) - x_{j+d/2} sin(theta)
+ *   y_{j+d/2}    = x_{j+d/2} cos(theta) + x_j sin(theta)
+ * computed in fp32 and rounded to bf16 (nearest even).  Position 0 is the
+ * identity, bit for bit.
+ *
+ * q_in/q_out  [total_tokens, heads, head_dim] bf16; q_out may equal q_in
+ * k_in/k_out  same shape, both NULL to rotate q only; k_out may equal k_in
+ * head_dim    even, 2..256
+ * A token outside every segment (malformed cu) is copied unrotated and sets
+ * PVC_DEV_TOTAL or PVC_DEV_NOT_INCREASING.
+ */
+pvc_status pvc_rope_thd_apply(const void* q_in, void* q_out, const void* k_in, void* k_out,
+                              int64_t total_tokens, int32_t heads, int32_t head_dim,
+                              const int32_t* cu_seqlens, int32_t nseg, float base,
+                              uint32_t* dev_error, void* stream);
+
+/* ------------------------------------------------------- attention */
+
+/* Output element types of the attention entry points. */
+enum { PVC_OUT_BF16 = 0, PVC_OUT_F32 = 1 };
+
+/* Bytes of workspace for a plan over `total_tokens` tokens in `nseg` segments. */
+size_t pvc_attn_workspace_size(int64_t total_tokens, int32_t nseg);
+
+/*
+ * Build the tile plan for one cu_seqlens: the list of work items (segment,
+ * query tile, key range) that covers exactly the same-segment, on-or-below-
+ * diagonal blocks ([charlestar] "EOS is content": allow(i,j) = same segment
+ * and p_j <= p_i; [opworld] "pitfall one": cross-document blocks are pure
+ * waste, which the varlen kernel never computes).  Items are ordered longest
+ * first.  cu_seqlens is read on the device only; it is validated as
+ * pvc_validate_cu_seqlens would (without lengths) and an invalid cu yields an
+ * empty plan plus the error bits.  The plan depends only on
+ * (cu_seqlens, nseg, total_tokens, causal), so one plan serves every layer
+ * and head that shares the boundaries.
+ */
+pvc_status pvc_attn_plan(const int32_t* cu_seqlens, int32_t nseg, int64_t total_tokens,
+                         int32_t max_seqlen, int32_t causal, void* workspace,
+                         size_t workspace_bytes, uint32_t* dev_error, void* stream);
+
+/*
+ * Attention forward with an existing plan:
+ *   out[i,h,:] = sum_j softmax_j(q_i.k_j / sqrt(head_dim) + M_ij) v_j
+ * with M_ij = 0 where segment(i) == segment(j) and (j <= i or !causal), -inf
+ * elsewhere, applied before normalising ([charlestar] "EOS is content": the
+ * masked softmax equation; [compass] "cross-contamination": block-diagonal
+ * mask).  causal == 0 lets a query see its whole segment.  The softmax scale is
+ * fixed at 1/sqrt(head_dim) ([charlestar]: QK^T / sqrt(d)).
+ *
+ * q, k, v    [total_tokens, heads, head_dim] bf16 (same head count)
+ * out        [total_tokens, heads, head_dim], bf16 (out_dtype PVC_OUT_BF16) or
+ *            fp32 (PVC_OUT_F32: the same schedule and accumulators, written
+ *            before the final bf16 rounding); must not alias q, k or v
+ * lse        NULL or [heads, total_tokens] fp32: natural-log sum of exponentials
+ *            of the scaled scores of each row
+ * head_dim   64 or 128
+ * total_tokens and causal must be those the plan was built with; otherwise
+ * PVC_DEV_PLAN is set and nothing is written.
+ * Arithmetic: bf16 MFMA products with fp32 accumulation; probabilities are
+ * rounded to bf16 for the P.V product and the row sums use those rounded
+ * values.  Deterministic: no atomics, results do not depend on scheduling.
+ */
+pvc_status pvc_varlen_attn_fwd_planned(const void* q, const void* k, const void* v, void* out,
+                                       float* lse, int64_t total_tokens, int32_t heads,
+                                       int32_t head_dim, int32_t causal, int32_t out_dtype,
+                                       const void* workspace, size_t workspace_bytes,
+                                       uint32_t* dev_error, void* stream);
+
+/*
+ * pvc_attn_plan followed by pvc_varlen_attn_fwd_planned: the varlen interface
+ * of [charlestar] "varlen interface" for self-attention (one cu_seqlens for q
+ * and k, max_seqlen = the longest segment, no dropout).
+ */
+pvc_status pvc_varlen_attn_fwd(const void* q, const void* k, const void* v, void* out,
+                               float* lse, const int32_t* cu_seqlens, int32_t nseg,
+                               int64_t total_tokens, int32_t max_seqlen, int32_t heads,
+                               int32_t head_dim, int32_t causal, int32_t out_dtype,
+                               void* workspace, size_t workspace_bytes, uint32_t* dev_error,
+                               void* stream);
+
+/*
+ * Padded comparison layout, for measurement: the same attention kernel on a
+ * padded SBHD buffer [max_len, batch, heads, head_dim] (bf16) in which sample
+ * b occupies rows s < seqlens[b].  Every sample is processed over all max_len
+ * rows; keys at or beyond seqlens[b] are masked to -inf but still computed, and
+ * padded query rows are computed too ([vllbc] "padding waste": the key-padding
+ * mask sets scores to -inf without removing the token, the kernel still sees
+ * L).  Only blocks wholly above the causal diagonal are skipped.  out has the
+ * input's shape; its padded rows hold attention over the sample's valid keys.
+ * seqlens [batch] int32 on the device, each in 1..max_len.  out_dtype as for
+ * pvc_varlen_attn_fwd_planned.
+ */
+pvc_status pvc_padded_attn_fwd_sbhd(const void* q, const void* k, const void* v, void* out,
+                                    const int32_t* seqlens, int32_t batch, int32_t max_len,
+                                    int32_t heads, int32_t head_dim, int32_t causal,
+                                    int32_t out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PVC_H */

@@ -1,0 +1,314 @@
+"""Packed variable-length causal attention for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libpvc.so`` (declared in
+``include/pvc.h``).  This module only marshals arguments: it checks tensor
+shapes and dtypes, allocates outputs with PyTorch and passes device pointers
+and the current HIP stream to the library.  Every step of the computation runs
+in the library's HIP kernels; there is no fallback path, and importing the
+package fails if the library has not been built.
+
+Entry points (same names as the C ABI without the ``pvc_`` prefix):
+  pack_build            cu_seqlens, segment ids, positions, shifted labels,
+                        loss mask, int64 target count, max_seqlen
+  validate_cu_seqlens   device-side check of a caller cu_seqlens
+  rope_thd_apply        per-segment rotary embedding on q and k
+  attn_plan             tile plan for one cu_seqlens (reusable across layers)
+  varlen_attn_fwd       block-diagonal (causal) attention over THD q/k/v
+  padded_attn_fwd_sbhd  the same kernel on a padded SBHD buffer (measurement)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "PvcError", "DEV_ERROR_BITS", "lib_path", "pack_build", "validate_cu_seqlens",
+    "rope_thd_apply", "AttnPlan", "attn_plan", "varlen_attn_fwd", "padded_attn_fwd_sbhd",
+    "error_names", "attn_workspace_size",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libpvc.so")
+
+OK, ERR_NULL, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(6)
+OUT_BF16, OUT_F32 = 0, 1
+DEV_ERROR_BITS = {
+    1: "CU0", 2: "NOT_INCREASING", 4: "TOTAL", 8: "MAXSEQ", 16: "LENGTH",
+    32: "MISMATCH", 64: "RANGE", 128: "PLAN",
+}
+
+
+class PvcError(RuntimeError):
+    """A libpvc entry point returned a non-zero status, or device data was invalid."""
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(lib_path):
+        raise ImportError(
+            f"{lib_path} is missing: build the HIP library first "
+            "(python -m packed_varlen_causal_amd.build or __graft_entry__.build())")
+    lib = ctypes.CDLL(lib_path)
+    P, I32, I64, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    sig = {
+        "pvc_status_string": ([I32], ctypes.c_char_p),
+        "pvc_version": ([], ctypes.c_char_p),
+        "pvc_pack_build_workspace_size": ([I32], SZ),
+        "pvc_pack_build": ([P, P, P, I32, I64, I32, P, P, P, P, P, P, P, P, P, SZ, P], I32),
+        "pvc_validate_cu_seqlens": ([P, I32, I64, I32, P, P, P], I32),
+        "pvc_rope_thd_apply": ([P, P, P, P, I64, I32, I32, P, I32, F32, P, P], I32),
+        "pvc_attn_workspace_size": ([I64, I32], SZ),
+        "pvc_attn_plan": ([P, I32, I64, I32, I32, P, SZ, P, P], I32),
+        "pvc_varlen_attn_fwd_planned": ([P, P, P, P, P, I64, I32, I32, I32, I32, P, SZ, P, P], I32),
+        "pvc_varlen_attn_fwd": ([P, P, P, P, P, P, I32, I64, I32, I32, I32, I32, I32, P, SZ, P, P], I32),
+        "pvc_padded_attn_fwd_sbhd": ([P, P, P, P, P, I32, I32, I32, I32, I32, I32, P], I32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_lib = _load()
+
+
+def version() -> str:
+    return _lib.pvc_version().decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != OK:
+        raise PvcError(f"{what}: {_lib.pvc_status_string(status).decode()} (status {status})")
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _require(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int | None = None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def error_names(bits: int) -> list[str]:
+    return [n for b, n in DEV_ERROR_BITS.items() if bits & b]
+
+
+def _raise_dev(err: torch.Tensor, what: str) -> None:
+    bits = int(err.item())
+    if bits:
+        raise PvcError(f"{what}: invalid device data ({', '.join(error_names(bits))})")
+
+
+def _new_error_word(device) -> torch.Tensor:
+    return torch.zeros(1, dtype=torch.int32, device=device)
+
+
+# ------------------------------------------------------------------ packing
+
+def pack_build(lengths: torch.Tensor, tokens: torch.Tensor | None = None,
+               is_pad: torch.Tensor | None = None, ignore_index: int = -100,
+               total_tokens: int | None = None, dev_error: torch.Tensor | None = None,
+               check: bool = False, stream=None) -> dict:
+    """Packing metadata on the GPU.
+
+    lengths int32 [nseg] (device), tokens int32 [T] (device, optional),
+    is_pad uint8 [nseg] (optional).  ``total_tokens`` defaults to tokens.numel().
+    Returns a dict of device tensors.  ``check=True`` synchronizes and raises on
+    device error bits.
+    """
+    _require(lengths, "lengths", torch.int32, 1)
+    dev = lengths.device
+    nseg = lengths.numel()
+    if tokens is not None:
+        _require(tokens, "tokens", torch.int32, 1)
+        T = tokens.numel() if total_tokens is None else int(total_tokens)
+        if tokens.numel() != T:
+            raise ValueError("tokens.numel() must equal total_tokens")
+    elif total_tokens is None:
+        raise ValueError("total_tokens is required when tokens is not given")
+    else:
+        T = int(total_tokens)
+    if is_pad is not None:
+        _require(is_pad, "is_pad", torch.uint8, 1)
+        if is_pad.numel() != nseg:
+            raise ValueError("is_pad must have one flag per segment")
+    err = _new_error_word(dev) if dev_error is None else dev_error
+    out = {
+        "cu_seqlens": torch.empty(nseg + 1, dtype=torch.int32, device=dev),
+        "segment_ids": torch.empty(T, dtype=torch.int32, device=dev),
+        "position_ids": torch.empty(T, dtype=torch.int32, device=dev),
+        "max_seqlen": torch.empty(1, dtype=torch.int32, device=dev),
+        "dev_error": err,
+    }
+    if tokens is not None:
+        out["shifted_labels"] = torch.empty(T, dtype=torch.int32, device=dev)
+        out["loss_mask"] = torch.empty(T, dtype=torch.uint8, device=dev)
+        out["num_targets"] = torch.empty(1, dtype=torch.int64, device=dev)
+    ws_bytes = _lib.pvc_pack_build_workspace_size(nseg)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    st = _lib.pvc_pack_build(
+        _ptr(lengths), _ptr(is_pad), _ptr(tokens), nseg, T, ignore_index, _ptr(out["cu_seqlens"]),
+        _ptr(out["segment_ids"]), _ptr(out["position_ids"]), _ptr(out.get("shifted_labels")),
+        _ptr(out.get("loss_mask")), _ptr(out.get("num_targets")), _ptr(out["max_seqlen"]),
+        _ptr(err), _ptr(ws), ws_bytes, _stream(stream))
+    _check(st, "pack_build")
+    if check:
+        _raise_dev(err, "pack_build")
+    return out
+
+
+def validate_cu_seqlens(cu_seqlens: torch.Tensor, total_tokens: int, max_seqlen: int,
+                        lengths: torch.Tensor | None = None, dev_error: torch.Tensor | None = None,
+                        stream=None) -> torch.Tensor:
+    """OR the contract violations of cu_seqlens into an int32 error word (returned)."""
+    _require(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    if lengths is not None:
+        _require(lengths, "lengths", torch.int32, 1)
+    err = _new_error_word(cu_seqlens.device) if dev_error is None else dev_error
+    st = _lib.pvc_validate_cu_seqlens(_ptr(cu_seqlens), cu_seqlens.numel() - 1, int(total_tokens),
+                                      int(max_seqlen), _ptr(lengths), _ptr(err), _stream(stream))
+    _check(st, "validate_cu_seqlens")
+    return err
+
+
+# --------------------------------------------------------------------- RoPE
+
+def rope_thd_apply(q: torch.Tensor, k: torch.Tensor | None, cu_seqlens: torch.Tensor,
+                   base: float = 10000.0, q_out: torch.Tensor | None = None,
+                   k_out: torch.Tensor | None = None, dev_error: torch.Tensor | None = None,
+                   stream=None):
+    """Per-segment RoPE on bf16 [T, H, d] q (and k).  In place unless outputs are given."""
+    _require(q, "q", torch.bfloat16, 3)
+    _require(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    T, H, D = q.shape
+    q_out = q if q_out is None else q_out
+    _require(q_out, "q_out", torch.bfloat16, 3)
+    if q_out.shape != q.shape:
+        raise ValueError("q_out must match q")
+    if k is not None:
+        _require(k, "k", torch.bfloat16, 3)
+        if k.shape != q.shape:
+            raise ValueError("k must have q's shape")
+        k_out = k if k_out is None else k_out
+        _require(k_out, "k_out", torch.bfloat16, 3)
+    err = dev_error
+    st = _lib.pvc_rope_thd_apply(_ptr(q), _ptr(q_out), _ptr(k), _ptr(k_out if k is not None else None),
+                                 T, H, D, _ptr(cu_seqlens), cu_seqlens.numel() - 1, float(base),
+                                 _ptr(err), _stream(stream))
+    _check(st, "rope_thd_apply")
+    return q_out, (k_out if k is not None else None)
+
+
+# ---------------------------------------------------------------- attention
+
+def attn_workspace_size(total_tokens: int, nseg: int) -> int:
+    return int(_lib.pvc_attn_workspace_size(int(total_tokens), int(nseg)))
+
+
+class AttnPlan:
+    """Device tile plan for one cu_seqlens; reusable by every layer and head."""
+
+    def __init__(self, cu_seqlens: torch.Tensor, total_tokens: int, max_seqlen: int,
+                 causal: bool = True, dev_error: torch.Tensor | None = None, stream=None,
+                 workspace: torch.Tensor | None = None):
+        _require(cu_seqlens, "cu_seqlens", torch.int32, 1)
+        self.total_tokens = int(total_tokens)
+        self.nseg = cu_seqlens.numel() - 1
+        self.causal = bool(causal)
+        self.cu_seqlens = cu_seqlens
+        self.dev_error = _new_error_word(cu_seqlens.device) if dev_error is None else dev_error
+        self.ws_bytes = attn_workspace_size(self.total_tokens, self.nseg)
+        if workspace is None:
+            workspace = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=cu_seqlens.device)
+        elif workspace.numel() < self.ws_bytes:
+            raise ValueError("workspace too small")
+        self.workspace = workspace
+        st = _lib.pvc_attn_plan(_ptr(cu_seqlens), self.nseg, self.total_tokens, int(max_seqlen),
+                                int(self.causal), _ptr(workspace), self.ws_bytes, _ptr(self.dev_error),
+                                _stream(stream))
+        _check(st, "attn_plan")
+
+
+def attn_plan(cu_seqlens, total_tokens, max_seqlen, causal=True, **kw) -> AttnPlan:
+    return AttnPlan(cu_seqlens, total_tokens, max_seqlen, causal, **kw)
+
+
+def varlen_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    cu_seqlens: torch.Tensor | None = None, max_seqlen: int | None = None,
+                    causal: bool = True, return_lse: bool = False,
+                    out_dtype: torch.dtype = torch.bfloat16, plan: AttnPlan | None = None,
+                    out: torch.Tensor | None = None, check: bool = False, stream=None):
+    """Block-diagonal attention over THD bf16 q, k, v [T, H, d] (d = 64 or 128).
+
+    Either ``cu_seqlens`` + ``max_seqlen`` (a plan is built) or a ready ``plan``.
+    Returns out [T, H, d] (bf16, or fp32 with out_dtype=torch.float32) and,
+    with ``return_lse``, lse fp32 [H, T].
+    """
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(t, name, torch.bfloat16, 3)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must share the shape [T, H, d]")
+    T, H, D = q.shape
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+    if plan is None:
+        if cu_seqlens is None or max_seqlen is None:
+            raise ValueError("give cu_seqlens and max_seqlen, or a plan")
+        plan = AttnPlan(cu_seqlens, T, max_seqlen, causal, stream=stream)
+    elif plan.total_tokens != T or plan.causal != bool(causal):
+        raise ValueError("plan was built for other total_tokens / causal")
+    if out is None:
+        out = torch.empty((T, H, D), dtype=out_dtype, device=q.device)
+    else:
+        _require(out, "out", out_dtype, 3)
+    lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if return_lse else None
+    st = _lib.pvc_varlen_attn_fwd_planned(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), T, H, D, int(bool(causal)),
+        OUT_F32 if out_dtype == torch.float32 else OUT_BF16, _ptr(plan.workspace), plan.ws_bytes,
+        _ptr(plan.dev_error), _stream(stream))
+    _check(st, "varlen_attn_fwd")
+    if check:
+        _raise_dev(plan.dev_error, "varlen_attn_fwd")
+    return (out, lse) if return_lse else out
+
+
+def padded_attn_fwd_sbhd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seqlens: torch.Tensor,
+                         causal: bool = True, out_dtype: torch.dtype = torch.bfloat16,
+                         out: torch.Tensor | None = None, stream=None):
+    """The attention kernel on a padded SBHD bf16 buffer [L, B, H, d] (measurement layout)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(t, name, torch.bfloat16, 4)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must share the shape [L, B, H, d]")
+    _require(seqlens, "seqlens", torch.int32, 1)
+    L, B, H, D = q.shape
+    if seqlens.numel() != B:
+        raise ValueError("one length per sample")
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    else:
+        _require(out, "out", out_dtype, 4)
+    st = _lib.pvc_padded_attn_fwd_sbhd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(seqlens), B, L, H, D,
+                                       int(bool(causal)),
+                                       OUT_F32 if out_dtype == torch.float32 else OUT_BF16, _stream(stream))
+    _check(st, "padded_attn_fwd_sbhd")
+    return out

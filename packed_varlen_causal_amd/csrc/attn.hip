@@ -1,0 +1,615 @@
+// Block-diagonal causal attention over a packed THD buffer, for gfx950.
+//
+// Definition ([charlestar] "EOS is content": allow(i,j) = same segment and
+// p_j <= p_i, additive -inf mask applied before the softmax,
+// O = softmax(Q K^T / sqrt(d) + M) V; [compass] "cross-contamination":
+// block-diagonal visibility; [opworld] "pitfall one": the varlen kernel skips
+// cross-document blocks instead of masking them).
+//
+// Plan (two launches, device-side only, no host synchronization):
+//   plan_rows_kernel   every token i gets its segment's key range
+//                      [cu[r], cu[r+1]) by binary search (8 B per token);
+//   plan_sort_kernel   one block validates cu_seqlens, prices every 128-row
+//                      query tile by its key span and orders the tiles
+//                      longest first (counting sort), then seals the header.
+// Query tiles are aligned to the buffer, not to segments: tile w covers rows
+// [128w, 128w+128).  A tile may hold the tail of one segment and the head of
+// the next, or many short segments; every row carries its own key range, so
+// tiles need no per-segment padding.
+//
+// Forward kernel: one 256-thread workgroup (four wave64s) per (head, tile).
+// Wave w owns query rows [128w' + 32w, +32).  Keys stream through LDS in
+// stages of 64 (double buffered: the next stage is fetched into registers
+// while the current one is consumed).  Per 32-key block a wave
+//   S^T = K Q^T      8 (d=128) v_mfma_f32_32x32x16_bf16, K from LDS as the A
+//                    operand, Q^T held in registers as the B operand; each
+//                    lane then owns one query and 16 of the 32 keys
+//   mask             only on blocks that cross a segment edge or the diagonal
+//   online softmax   running max and sum per query in exp2 units; the row max
+//                    needs one lane-pair exchange (lane l <-> l^32)
+//   O^T += V^T P^T   the probabilities, rounded to bf16, are already in the B
+//                    operand layout; V^T is read from an LDS copy that was
+//                    transposed while staging
+// and skips any 32-key block that lies wholly outside its rows' segments or
+// above their diagonal, so cross-segment and above-diagonal blocks are never
+// computed.
+//
+// Grid to hardware: workgroups are dealt round-robin to the 8 XCDs, so the
+// block index is remapped to give each XCD a contiguous range of the
+// (head, tile) space; an XCD then works through a few heads, and the query
+// tiles that share a head's K/V run together on one L2.
+#include <math.h>
+
+#include "pvc_internal.h"
+
+namespace pvc {
+namespace {
+
+constexpr int kBM = 128;        // query rows per tile
+constexpr int kBN = 64;         // keys per LDS stage
+constexpr int kThreads = 256;   // 4 waves x 32 rows
+constexpr int kNumBuckets = 4096;
+constexpr int kSortThreads = 1024;
+constexpr int kNumXcd = 8;
+constexpr int32_t kPlanMagic = 0x31435650;   // "PVC1"
+
+enum { HDR_MAGIC = 0, HDR_T = 1, HDR_CAUSAL = 2, HDR_NTILES = 3, HDR_ERR = 4, HDR_VALID = 5 };
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct PlanLayout {
+    size_t header, order, rows, total;
+    int64_t ntiles;
+};
+
+PlanLayout plan_layout(int64_t T) {
+    PlanLayout L;
+    L.ntiles = (T + kBM - 1) / kBM;
+    size_t off = 0;
+    L.header = off;
+    off += align_up(16 * sizeof(int32_t));
+    L.order = off;
+    off += align_up((size_t)L.ntiles * sizeof(int32_t));
+    L.rows = off;
+    off += align_up((size_t)T * sizeof(int2));
+    L.total = off;
+    return L;
+}
+
+// ------------------------------------------------------------------ plan
+
+__global__ __launch_bounds__(256) void plan_rows_kernel(const int32_t* __restrict__ cu, int32_t nseg,
+                                                        int64_t T, int2* __restrict__ rows) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= T) return;
+    const int32_t r = upper_segment(cu, nseg, i);
+    const int64_t st = max<int64_t>(cu[r], 0), en = min<int64_t>(cu[r + 1], T);
+    const bool ok = st <= i && i < en;
+    rows[i] = ok ? make_int2((int)st, (int)en) : make_int2((int)i, (int)(i + 1));
+}
+
+__device__ int block_exclusive_scan_int(int x, int* sh, int& total) {
+    const int t = threadIdx.x;
+    sh[t] = x;
+    __syncthreads();
+    for (int off = 1; off < (int)blockDim.x; off <<= 1) {
+        int y = (t >= off) ? sh[t - off] : 0;
+        __syncthreads();
+        sh[t] += y;
+        __syncthreads();
+    }
+    total = sh[blockDim.x - 1];
+    const int excl = sh[t] - x;
+    __syncthreads();
+    return excl;
+}
+
+__global__ __launch_bounds__(kSortThreads) void plan_sort_kernel(
+        const int32_t* __restrict__ cu, int32_t nseg, int64_t T, int32_t max_seqlen, int32_t causal,
+        const int2* __restrict__ rows, int32_t* __restrict__ header, int32_t* __restrict__ order,
+        int32_t ntiles, uint32_t* dev_error) {
+    __shared__ int hist[kNumBuckets];
+    __shared__ int offs[kNumBuckets];
+    __shared__ int scan_sh[kSortThreads];
+    __shared__ unsigned s_err;
+    const int t = threadIdx.x;
+    if (t == 0) s_err = 0;
+    for (int b = t; b < kNumBuckets; b += kSortThreads) hist[b] = 0;
+    __syncthreads();
+
+    // 1. the cu_seqlens contract
+    uint32_t err = 0;
+    for (int64_t r = t; r < nseg; r += kSortThreads) {
+        const int64_t a = cu[r], b = cu[r + 1];
+        if (b <= a) err |= PVC_DEV_NOT_INCREASING;
+        if (b - a > max_seqlen) err |= PVC_DEV_MAXSEQ;
+    }
+    if (t == 0) {
+        if (cu[0] != 0) err |= PVC_DEV_CU0;
+        if ((int64_t)cu[nseg] != T) err |= PVC_DEV_TOTAL;
+    }
+    if (err) atomicOr(&s_err, err);
+
+    // 2. price every tile by its key span in 64-key stages
+    auto bucket_of = [&](int w) {
+        const int64_t f = (int64_t)w * kBM;
+        const int64_t l = min<int64_t>(f + kBM, T) - 1;
+        const int64_t lo = rows[f].x;
+        const int64_t hi = causal ? l + 1 : (int64_t)rows[l].y;
+        const int64_t stages = (hi - lo + kBN - 1) / kBN;
+        return (int)min<int64_t>(stages, kNumBuckets - 1);
+    };
+    for (int w = t; w < ntiles; w += kSortThreads) atomicAdd(&hist[bucket_of(w)], 1);
+    __syncthreads();
+
+    // 3. descending exclusive scan: offs[b] = number of tiles in buckets > b
+    constexpr int kPer = kNumBuckets / kSortThreads;
+    int local[kPer];
+    int sum = 0;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        local[k] = hist[kNumBuckets - 1 - (t * kPer + k)];
+        sum += local[k];
+    }
+    int total = 0;
+    int run = block_exclusive_scan_int(sum, scan_sh, total);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+        offs[kNumBuckets - 1 - (t * kPer + k)] = run;
+        run += local[k];
+    }
+    for (int b = t; b < kNumBuckets; b += kSortThreads) hist[b] = 0;   // reuse as cursors
+    __syncthreads();
+
+    // 4. scatter (order inside a bucket is arbitrary; results do not depend on it)
+    for (int w = t; w < ntiles; w += kSortThreads) {
+        const int b = bucket_of(w);
+        order[offs[b] + atomicAdd(&hist[b], 1)] = w;
+    }
+    __syncthreads();
+    if (t == 0) {
+        header[HDR_MAGIC] = kPlanMagic;
+        header[HDR_T] = (int32_t)T;
+        header[HDR_CAUSAL] = causal ? 1 : 0;
+        header[HDR_NTILES] = ntiles;
+        header[HDR_ERR] = (int32_t)s_err;
+        header[HDR_VALID] = s_err == 0 ? 1 : 0;
+        raise_error(dev_error, s_err);
+    }
+}
+
+// --------------------------------------------------------------- forward
+
+struct AttnParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    void* out;
+    float* lse;
+    const int32_t* header;     // THD: plan header
+    const int32_t* order;      // THD: tile order
+    const int2* rows;          // THD: per-row key range
+    const int32_t* seqlens;    // SBHD: valid length per sample
+    int64_t T;                 // THD: total tokens
+    int32_t H;
+    int32_t ntiles;            // THD: tiles; SBHD: tiles per sample
+    int32_t items;             // heads x tiles (x batch for SBHD)
+    int32_t B, L;              // SBHD: batch and padded length
+    float scale_log2;          // log2(e) / sqrt(d)
+    uint32_t* dev_error;
+};
+
+__device__ inline f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline float lane_pair_max(float x) {
+    return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+
+template <int D, bool CAUSAL, bool OUT_F32, bool SBHD>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(AttnParams p) {
+    static_assert(D == 64 || D == 128, "head_dim");
+    constexpr int KPAD = D + 8;              // K row stride in LDS (bf16), 16 B pad
+    constexpr int VPAD = kBN + 4;            // V^T row stride in LDS (bf16), 8 B pad
+    constexpr int NS = D / 16;               // MFMA k-steps for q.k
+    constexpr int ND = D / 32;               // 32-wide d blocks of the output
+    constexpr int KCH = kBN * D / 8 / kThreads;      // 16-B K chunks per thread
+    constexpr int VKPT = D / 32;             // keys per thread in the V^T staging
+    __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBN * KPAD];
+    __shared__ __attribute__((aligned(16))) uint16_t sVt[2][D * VPAD];
+
+    // ---- which (head, tile): XCD-contiguous remap of the block index
+    const int nblk = gridDim.x;
+    const int per_xcd = nblk / kNumXcd;
+    const int logical = (blockIdx.x % kNumXcd) * per_xcd + blockIdx.x / kNumXcd;
+    if (logical >= p.items) return;
+    int head, b = 0, r0, r1, last_row;
+    if constexpr (SBHD) {
+        const int per_head = p.B * p.ntiles;
+        head = logical / per_head;
+        const int rem = logical - head * per_head;
+        b = rem / p.ntiles;
+        const int tile = p.ntiles - 1 - (rem - b * p.ntiles);   // heavy tiles first
+        r0 = tile * kBM;
+        r1 = min(r0 + kBM, p.L);
+        last_row = p.L - 1;
+    } else {
+        if (p.header[HDR_MAGIC] != kPlanMagic || p.header[HDR_T] != (int32_t)p.T ||
+            p.header[HDR_CAUSAL] != (CAUSAL ? 1 : 0) || p.header[HDR_NTILES] != p.ntiles) {
+            if (threadIdx.x == 0) raise_error(p.dev_error, PVC_DEV_PLAN);
+            return;
+        }
+        if (p.header[HDR_VALID] != 1) return;
+        head = logical / p.ntiles;
+        const int tile = min(max(p.order[logical - head * p.ntiles], 0), p.ntiles - 1);
+        r0 = tile * kBM;
+        r1 = (int)min<int64_t>((int64_t)r0 + kBM, p.T);
+        last_row = (int)(p.T - 1);
+    }
+    const int H = p.H;
+    const int seq_len = SBHD ? p.seqlens[b] : 0;
+
+    // token row -> element offset of (row, head, 0)
+    auto row_off = [&](int row) -> int64_t {
+        if constexpr (SBHD) return (((int64_t)row * p.B + b) * H + head) * D;
+        else return ((int64_t)row * H + head) * D;
+    };
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int c = lane & 31;
+    const int g = lane >> 5;
+
+    // ---- wave and lane row ranges
+    const int wr0 = r0 + 32 * wave;
+    const int wr1 = min(wr0 + 32, r1);
+    const bool wave_active = wr0 < r1;
+    const int row = min(wr0 + c, r1 - 1);
+    int start_l, end_l, w_lo, w_hi, max_start, min_end;
+    if constexpr (SBHD) {
+        start_l = 0;
+        end_l = seq_len;
+        w_lo = 0;
+        w_hi = CAUSAL ? wr1 : p.L;
+        max_start = 0;
+        min_end = seq_len;
+    } else {
+        const int2 mine = p.rows[row];
+        start_l = mine.x;
+        end_l = mine.y;
+        const int2 first = p.rows[min(wr0, r1 - 1)];
+        const int2 last = p.rows[max(wr1 - 1, 0)];
+        w_lo = first.x;
+        w_hi = CAUSAL ? wr1 : last.y;
+        max_start = last.x;
+        min_end = first.y;
+    }
+    // block key range
+    int k_lo, k_hi;
+    if constexpr (SBHD) {
+        k_lo = 0;
+        k_hi = CAUSAL ? r1 : p.L;
+    } else {
+        k_lo = p.rows[r0].x;
+        k_hi = CAUSAL ? r1 : p.rows[r1 - 1].y;
+    }
+    const int nstages = (k_hi - k_lo + kBN - 1) / kBN;
+
+    // ---- Q^T operand in registers: lane (c, g) holds Q[row][16s + 8g .. +8]
+    bf16x8 qreg[NS];
+    {
+        const uint16_t* qp = p.q + row_off(row) + 8 * g;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+    }
+
+    // ---- staging registers
+    u32x4 kreg[KCH];
+    u32x4 vreg[VKPT];
+    const int v_dch = tid % (D / 8);                 // 8-wide d chunk of this thread's V rows
+    const int v_kg = tid / (D / 8);                  // key group: keys VKPT*v_kg ..
+    auto fetch = [&](int stage) {
+        const int kt = k_lo + stage * kBN;
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int ci = tid + i * kThreads;
+            const int kr = ci / (D / 8), ch = ci % (D / 8);
+            const int krow = min(kt + kr, last_row);
+            kreg[i] = *reinterpret_cast<const u32x4*>(p.k + row_off(krow) + ch * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < VKPT; ++i) {
+            const int vrow = min(kt + VKPT * v_kg + i, last_row);
+            vreg[i] = *reinterpret_cast<const u32x4*>(p.v + row_off(vrow) + v_dch * 8);
+        }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int ci = tid + i * kThreads;
+            const int kr = ci / (D / 8), ch = ci % (D / 8);
+            *reinterpret_cast<u32x4*>(&sK[buf][kr * KPAD + ch * 8]) = kreg[i];
+        }
+        // transpose: V[key][d] -> V^T[d][key]; VKPT consecutive keys per write
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int w = e >> 1, sh = (e & 1) * 16;
+            uint16_t* dst = &sVt[buf][(v_dch * 8 + e) * VPAD + VKPT * v_kg];
+            if constexpr (VKPT == 4) {
+                u32x2 pk;
+                pk.x = ((vreg[0][w] >> sh) & 0xFFFFu) | (((vreg[1][w] >> sh) & 0xFFFFu) << 16);
+                pk.y = ((vreg[2][w] >> sh) & 0xFFFFu) | (((vreg[3][w] >> sh) & 0xFFFFu) << 16);
+                *reinterpret_cast<u32x2*>(dst) = pk;
+            } else {
+                const uint32_t pk = ((vreg[0][w] >> sh) & 0xFFFFu) | (((vreg[1][w] >> sh) & 0xFFFFu) << 16);
+                *reinterpret_cast<uint32_t*>(dst) = pk;
+            }
+        }
+    };
+
+    // ---- running state (one query per lane; the lane pair (c, 0)/(c, 1)
+    // shares the query and keeps identical m, disjoint halves of l and acc rows)
+    f32x16 acc[ND];
+#pragma unroll
+    for (int j = 0; j < ND; ++j) acc[j] = f32x16(0.0f);
+    float m_run = -INFINITY;
+    float l_run = 0.0f;
+    const float sl2 = p.scale_log2;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+
+    if (nstages > 0) {
+        fetch(0);
+        stash(0);
+    }
+    __syncthreads();
+    for (int st = 0; st < nstages; ++st) {
+        const int buf = st & 1;
+        if (st + 1 < nstages) fetch(st + 1);
+        const int kt = k_lo + st * kBN;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int kbase = kt + 32 * kb;
+            // wave-uniform skip: block outside every row's key range
+            if (!wave_active || kbase >= w_hi || kbase + 32 <= w_lo) continue;
+            f32x16 S = f32x16(0.0f);
+            const uint16_t* kp = &sK[buf][(32 * kb + c) * KPAD + 8 * g];
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                S = mfma32(*reinterpret_cast<const bf16x8*>(kp + 16 * s), qreg[s], S);
+            // S[r] = score of key kbase + 8(r/4) + 4g + r%4 for this lane's query
+            const bool full = kbase >= max_start && kbase + 32 <= min_end &&
+                              (!CAUSAL || kbase + 31 <= wr0);
+            if (!full) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kbase + 8 * (r >> 2) + 4 * g + (r & 3);
+                    const bool ok = key >= start_l && key < end_l && (!CAUSAL || key <= row);
+                    S[r] = ok ? S[r] : -INFINITY;
+                }
+            }
+            float mx = S[0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+            mx = lane_pair_max(mx);
+            const float m_new = fmaxf(m_run, mx * sl2);
+            const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+            bf16x2 pk[8];
+            float rs = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(S[2 * i], sl2, -m_use));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(S[2 * i + 1], sl2, -m_use));
+                pk[i] = bf16x2{(__bf16)p0, (__bf16)p1};
+                rs = __builtin_amdgcn_fdot2_f32_bf16(pk[i], ones, rs, false);
+            }
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+                for (int j = 0; j < ND; ++j) acc[j] *= alpha;
+            }
+            l_run = l_run * alpha + rs;
+            m_run = m_new;
+            // O^T[d][q] += V^T[d][key] P^T[key][q], two 16-key steps
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const bf16x8 pb = {pk[4 * ks][0], pk[4 * ks][1], pk[4 * ks + 1][0], pk[4 * ks + 1][1],
+                                   pk[4 * ks + 2][0], pk[4 * ks + 2][1], pk[4 * ks + 3][0], pk[4 * ks + 3][1]};
+                const int col = 32 * kb + 16 * ks + 4 * g;
+#pragma unroll
+                for (int j = 0; j < ND; ++j) {
+                    const uint16_t* vp = &sVt[buf][(32 * j + c) * VPAD + col];
+                    const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
+                    const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 8);
+                    const u32x4 av = {lo.x, lo.y, hi.x, hi.y};
+                    acc[j] = mfma32(__builtin_bit_cast(bf16x8, av), pb, acc[j]);
+                }
+            }
+        }
+        if (st + 1 < nstages) stash(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: lane (c, g) holds O^T rows d = 32j + 8(r/4) + 4g + r%4
+    if (!wave_active || wr0 + c >= r1) return;
+    const float l = l_run + __shfl_xor(l_run, 32, 64);
+    const float inv = 1.0f / l;
+    const int64_t ob = row_off(row);
+#pragma unroll
+    for (int j = 0; j < ND; ++j) {
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+            const int d0 = 32 * j + 8 * rq + 4 * g;
+            const float o0 = acc[j][4 * rq] * inv, o1 = acc[j][4 * rq + 1] * inv;
+            const float o2 = acc[j][4 * rq + 2] * inv, o3 = acc[j][4 * rq + 3] * inv;
+            if constexpr (OUT_F32) {
+                *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + ob + d0) = f32x4{o0, o1, o2, o3};
+            } else {
+                const bf16x2 a = {(__bf16)o0, (__bf16)o1};
+                const bf16x2 bb = {(__bf16)o2, (__bf16)o3};
+                const u32x2 w = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, bb)};
+                *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + ob + d0) = w;
+            }
+        }
+    }
+    if constexpr (!SBHD) {
+        if (p.lse != nullptr && g == 0)
+            p.lse[(int64_t)head * p.T + row] = (m_run + __log2f(l)) * 0.69314718055994530942f;
+    }
+}
+
+template <int D, bool SBHD>
+pvc_status launch_fwd(const AttnParams& prm, bool causal, bool out_f32, hipStream_t s) {
+    const int64_t grid = ((int64_t)prm.items + kNumXcd - 1) / kNumXcd * kNumXcd;
+    if (grid > 0x7fffffffLL) return PVC_ERR_INVALID_ARG;
+    dim3 g((unsigned)grid), blk(kThreads);
+    if (causal) {
+        if (out_f32) hipLaunchKernelGGL((attn_fwd_kernel<D, true, true, SBHD>), g, blk, 0, s, prm);
+        else hipLaunchKernelGGL((attn_fwd_kernel<D, true, false, SBHD>), g, blk, 0, s, prm);
+    } else {
+        if (out_f32) hipLaunchKernelGGL((attn_fwd_kernel<D, false, true, SBHD>), g, blk, 0, s, prm);
+        else hipLaunchKernelGGL((attn_fwd_kernel<D, false, false, SBHD>), g, blk, 0, s, prm);
+    }
+    return launch_status();
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+}  // namespace
+}  // namespace pvc
+
+using namespace pvc;
+
+extern "C" size_t pvc_attn_workspace_size(int64_t total_tokens, int32_t nseg) {
+    (void)nseg;
+    if (total_tokens < 1 || total_tokens > 0x7fffffffLL) return 0;
+    return plan_layout(total_tokens).total;
+}
+
+extern "C" pvc_status pvc_attn_plan(const int32_t* cu_seqlens, int32_t nseg, int64_t total_tokens,
+                                    int32_t max_seqlen, int32_t causal, void* workspace,
+                                    size_t workspace_bytes, uint32_t* dev_error, void* stream) {
+    if (cu_seqlens == nullptr || workspace == nullptr) return PVC_ERR_NULL;
+    if (nseg < 1 || total_tokens < 1 || total_tokens > 0x7fffffffLL || max_seqlen < 1)
+        return PVC_ERR_INVALID_ARG;
+    const PlanLayout L = plan_layout(total_tokens);
+    if (workspace_bytes < L.total) return PVC_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    auto* header = reinterpret_cast<int32_t*>(ws + L.header);
+    auto* order = reinterpret_cast<int32_t*>(ws + L.order);
+    auto* rows = reinterpret_cast<int2*>(ws + L.rows);
+    hipStream_t s = as_stream(stream);
+    const int64_t nblk = (total_tokens + 255) / 256;
+    hipLaunchKernelGGL(plan_rows_kernel, dim3((unsigned)nblk), dim3(256), 0, s, cu_seqlens, nseg,
+                       total_tokens, rows);
+    hipLaunchKernelGGL(plan_sort_kernel, dim3(1), dim3(kSortThreads), 0, s, cu_seqlens, nseg,
+                       total_tokens, max_seqlen, causal ? 1 : 0, rows, header, order,
+                       (int32_t)L.ntiles, dev_error);
+    return launch_status();
+}
+
+extern "C" pvc_status pvc_varlen_attn_fwd_planned(const void* q, const void* k, const void* v, void* out,
+                                                  float* lse, int64_t total_tokens, int32_t heads,
+                                                  int32_t head_dim, int32_t causal, int32_t out_dtype,
+                                                  const void* workspace, size_t workspace_bytes,
+                                                  uint32_t* dev_error, void* stream) {
+    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || workspace == nullptr)
+        return PVC_ERR_NULL;
+    if (total_tokens < 1 || total_tokens > 0x7fffffffLL || heads < 1) return PVC_ERR_INVALID_ARG;
+    if (out_dtype != PVC_OUT_BF16 && out_dtype != PVC_OUT_F32) return PVC_ERR_INVALID_ARG;
+    if (head_dim != 64 && head_dim != 128) return PVC_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PVC_ERR_INVALID_ARG;
+    const PlanLayout L = plan_layout(total_tokens);
+    if (workspace_bytes < L.total) return PVC_ERR_WORKSPACE;
+    const size_t in_bytes = (size_t)total_tokens * heads * head_dim * 2;
+    const size_t out_bytes = in_bytes * (out_dtype == PVC_OUT_F32 ? 2 : 1);
+    if (overlaps(out, out_bytes, q, in_bytes) || overlaps(out, out_bytes, k, in_bytes) ||
+        overlaps(out, out_bytes, v, in_bytes))
+        return PVC_ERR_INVALID_ARG;
+    if (L.ntiles * (int64_t)heads > 0x7ffffff0LL) return PVC_ERR_INVALID_ARG;
+    const char* ws = static_cast<const char*>(workspace);
+    AttnParams prm{};
+    prm.q = static_cast<const uint16_t*>(q);
+    prm.k = static_cast<const uint16_t*>(k);
+    prm.v = static_cast<const uint16_t*>(v);
+    prm.out = out;
+    prm.lse = lse;
+    prm.header = reinterpret_cast<const int32_t*>(ws + L.header);
+    prm.order = reinterpret_cast<const int32_t*>(ws + L.order);
+    prm.rows = reinterpret_cast<const int2*>(ws + L.rows);
+    prm.T = total_tokens;
+    prm.H = heads;
+    prm.ntiles = (int32_t)L.ntiles;
+    prm.items = (int32_t)(L.ntiles * heads);
+    prm.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
+    prm.dev_error = dev_error;
+    hipStream_t s = as_stream(stream);
+    const bool f32 = out_dtype == PVC_OUT_F32;
+    if (head_dim == 128) return launch_fwd<128, false>(prm, causal != 0, f32, s);
+    return launch_fwd<64, false>(prm, causal != 0, f32, s);
+}
+
+extern "C" pvc_status pvc_varlen_attn_fwd(const void* q, const void* k, const void* v, void* out,
+                                          float* lse, const int32_t* cu_seqlens, int32_t nseg,
+                                          int64_t total_tokens, int32_t max_seqlen, int32_t heads,
+                                          int32_t head_dim, int32_t causal, int32_t out_dtype,
+                                          void* workspace, size_t workspace_bytes, uint32_t* dev_error,
+                                          void* stream) {
+    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return PVC_ERR_NULL;
+    if (head_dim != 64 && head_dim != 128) return PVC_ERR_UNSUPPORTED;
+    if (heads < 1 || (out_dtype != PVC_OUT_BF16 && out_dtype != PVC_OUT_F32)) return PVC_ERR_INVALID_ARG;
+    pvc_status st = pvc_attn_plan(cu_seqlens, nseg, total_tokens, max_seqlen, causal, workspace,
+                                  workspace_bytes, dev_error, stream);
+    if (st != PVC_OK) return st;
+    return pvc_varlen_attn_fwd_planned(q, k, v, out, lse, total_tokens, heads, head_dim, causal,
+                                       out_dtype, workspace, workspace_bytes, dev_error, stream);
+}
+
+extern "C" pvc_status pvc_padded_attn_fwd_sbhd(const void* q, const void* k, const void* v, void* out,
+                                               const int32_t* seqlens, int32_t batch, int32_t max_len,
+                                               int32_t heads, int32_t head_dim, int32_t causal,
+                                               int32_t out_dtype, void* stream) {
+    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || seqlens == nullptr)
+        return PVC_ERR_NULL;
+    if (batch < 1 || max_len < 1 || heads < 1) return PVC_ERR_INVALID_ARG;
+    if (out_dtype != PVC_OUT_BF16 && out_dtype != PVC_OUT_F32) return PVC_ERR_INVALID_ARG;
+    if (head_dim != 64 && head_dim != 128) return PVC_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PVC_ERR_INVALID_ARG;
+    const int64_t elems = (int64_t)max_len * batch * heads * head_dim;
+    if (elems > (int64_t)1 << 46) return PVC_ERR_INVALID_ARG;
+    const size_t bytes = (size_t)elems * 2;
+    const size_t out_bytes = bytes * (out_dtype == PVC_OUT_F32 ? 2 : 1);
+    if (overlaps(out, out_bytes, q, bytes) || overlaps(out, out_bytes, k, bytes) ||
+        overlaps(out, out_bytes, v, bytes))
+        return PVC_ERR_INVALID_ARG;
+    const int64_t tiles = (max_len + kBM - 1) / kBM;
+    const int64_t items = tiles * batch * heads;
+    if (items > 0x7ffffff0LL) return PVC_ERR_INVALID_ARG;
+    AttnParams prm{};
+    prm.q = static_cast<const uint16_t*>(q);
+    prm.k = static_cast<const uint16_t*>(k);
+    prm.v = static_cast<const uint16_t*>(v);
+    prm.out = out;
+    prm.seqlens = seqlens;
+    prm.H = heads;
+    prm.ntiles = (int32_t)tiles;
+    prm.items = (int32_t)items;
+    prm.B = batch;
+    prm.L = max_len;
+    prm.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
+    hipStream_t s = as_stream(stream);
+    const bool f32 = out_dtype == PVC_OUT_F32;
+    if (head_dim == 128) return launch_fwd<128, true>(prm, causal != 0, f32, s);
+    return launch_fwd<64, true>(prm, causal != 0, f32, s);
+}

@@ -1,0 +1,171 @@
+// Rotary position embedding over a packed THD buffer with positions reset per
+// segment ([vllbc] THD RoPE recovers local positions from cu_seqlens;
+// [charlestar] "nine tokens, three identities": p_i = i - cu_r; [opworld]
+// "pitfall two": reset positions per document).
+//
+// Rotate-half pairing (j, j + d/2), angle theta_j = fp32(p) * f_j with the fp32
+// frequency table f_j = base^(-2j/d) computed on the host in double.  sin and
+// cos come from the device's full-range sincosf; the rotation runs in fp32 and
+// rounds once to bf16.
+//
+// Work layout: one thread owns one token, eight consecutive pairs (16 bytes of
+// each half-row) and kHeadsPerThread heads of q and of k.  It evaluates its
+// eight sin/cos pairs once and streams the heads; the d/16 threads of a token
+// together read and write whole 2*d-byte head rows, so every access is a
+// coalesced 16-byte vector.  The kernel moves 2 B in + 2 B out per element and
+// is bound by HBM bandwidth.
+#include <math.h>
+
+#include "pvc_internal.h"
+
+namespace pvc {
+namespace {
+
+constexpr int kRopeThreads = 256;
+constexpr int kHeadsPerThread = 8;
+constexpr int kMaxHalf = 128;
+
+struct RopeFreqs {
+    float f[kMaxHalf];
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline void rotate8(const u32x4& a, const u32x4& b, const float* c, const float* s,
+                               u32x4& ya, u32x4& yb) {
+    // a holds x_j .. x_{j+7}, b holds x_{j+d/2} .. x_{j+d/2+7}; two bf16 per dword
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        uint32_t ra = 0, rb = 0;
+#pragma unroll
+        for (int hlf = 0; hlf < 2; ++hlf) {
+            const int e = 2 * w + hlf;
+            const float x1 = bf16_to_f32(uint16_t(a[w] >> (16 * hlf)));
+            const float x2 = bf16_to_f32(uint16_t(b[w] >> (16 * hlf)));
+            const float y1 = x1 * c[e] - x2 * s[e];
+            const float y2 = x2 * c[e] + x1 * s[e];
+            ra |= uint32_t(f32_to_bf16_rne(y1)) << (16 * hlf);
+            rb |= uint32_t(f32_to_bf16_rne(y2)) << (16 * hlf);
+        }
+        ya[w] = ra;
+        yb[w] = rb;
+    }
+}
+
+// head_dim a multiple of 16: vectorized path.
+__global__ __launch_bounds__(kRopeThreads) void rope_vec_kernel(
+        const uint16_t* q_in, uint16_t* q_out, const uint16_t* k_in, uint16_t* k_out, int64_t T,
+        int32_t H, int32_t D, const int32_t* __restrict__ cu, int32_t nseg, RopeFreqs freqs,
+        uint32_t* dev_error) {
+    const int chunks = D >> 4;                        // 8-pair chunks per head row
+    const int hgroups = (H + kHeadsPerThread - 1) / kHeadsPerThread;
+    const int64_t gid = (int64_t)blockIdx.x * kRopeThreads + threadIdx.x;
+    const int64_t per_token = (int64_t)chunks * hgroups;
+    const int64_t i = gid / per_token;
+    if (i >= T) return;
+    const int rem = (int)(gid - i * per_token);
+    const int hg = rem / chunks;
+    const int ch = rem - hg * chunks;
+
+    const int32_t r = upper_segment(cu, nseg, i);
+    const int64_t st = cu[r], en = cu[r + 1];
+    const bool ok = st <= i && i < en;
+    if (!ok && ch == 0 && hg == 0) raise_error(dev_error, i >= en ? PVC_DEV_TOTAL : PVC_DEV_NOT_INCREASING);
+    const float p = ok ? (float)(i - st) : 0.0f;     // malformed cu: identity (copy through)
+
+    float c[8], s[8];
+    const int j0 = ch * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float theta = p * freqs.f[j0 + e];      // one fp32 product
+        sincosf(theta, &s[e], &c[e]);
+    }
+    const int half = D >> 1;
+    const int h_lo = hg * kHeadsPerThread;
+    const int h_hi = min(H, h_lo + kHeadsPerThread);
+#pragma unroll 1
+    for (int t = 0; t < 2; ++t) {
+        const uint16_t* src = t == 0 ? q_in : k_in;
+        uint16_t* dst = t == 0 ? q_out : k_out;
+        if (src == nullptr) break;
+        for (int h = h_lo; h < h_hi; ++h) {
+            const int64_t row = (i * H + h) * (int64_t)D;
+            const u32x4 a = *reinterpret_cast<const u32x4*>(src + row + j0);
+            const u32x4 b = *reinterpret_cast<const u32x4*>(src + row + half + j0);
+            u32x4 ya, yb;
+            rotate8(a, b, c, s, ya, yb);
+            *reinterpret_cast<u32x4*>(dst + row + j0) = ya;
+            *reinterpret_cast<u32x4*>(dst + row + half + j0) = yb;
+        }
+    }
+}
+
+// Any even head_dim: one thread per (token, pair), heads looped.
+__global__ __launch_bounds__(kRopeThreads) void rope_scalar_kernel(
+        const uint16_t* q_in, uint16_t* q_out, const uint16_t* k_in, uint16_t* k_out, int64_t T,
+        int32_t H, int32_t D, const int32_t* __restrict__ cu, int32_t nseg, RopeFreqs freqs,
+        uint32_t* dev_error) {
+    const int half = D >> 1;
+    const int64_t gid = (int64_t)blockIdx.x * kRopeThreads + threadIdx.x;
+    const int64_t i = gid / half;
+    if (i >= T) return;
+    const int j = (int)(gid - i * half);
+    const int32_t r = upper_segment(cu, nseg, i);
+    const int64_t st = cu[r], en = cu[r + 1];
+    const bool ok = st <= i && i < en;
+    if (!ok && j == 0) raise_error(dev_error, i >= en ? PVC_DEV_TOTAL : PVC_DEV_NOT_INCREASING);
+    const float p = ok ? (float)(i - st) : 0.0f;
+    float sn, cs;
+    sincosf(p * freqs.f[j], &sn, &cs);
+    for (int t = 0; t < 2; ++t) {
+        const uint16_t* src = t == 0 ? q_in : k_in;
+        uint16_t* dst = t == 0 ? q_out : k_out;
+        if (src == nullptr) break;
+        for (int h = 0; h < H; ++h) {
+            const int64_t row = (i * H + h) * (int64_t)D;
+            const float x1 = bf16_to_f32(src[row + j]);
+            const float x2 = bf16_to_f32(src[row + half + j]);
+            dst[row + j] = f32_to_bf16_rne(x1 * cs - x2 * sn);
+            dst[row + half + j] = f32_to_bf16_rne(x2 * cs + x1 * sn);
+        }
+    }
+}
+
+}  // namespace
+}  // namespace pvc
+
+using namespace pvc;
+
+extern "C" pvc_status pvc_rope_thd_apply(const void* q_in, void* q_out, const void* k_in, void* k_out,
+                                         int64_t total_tokens, int32_t heads, int32_t head_dim,
+                                         const int32_t* cu_seqlens, int32_t nseg, float base,
+                                         uint32_t* dev_error, void* stream) {
+    if (q_in == nullptr || q_out == nullptr || cu_seqlens == nullptr) return PVC_ERR_NULL;
+    if ((k_in == nullptr) != (k_out == nullptr)) return PVC_ERR_NULL;
+    if (total_tokens < 1 || total_tokens > 0x7fffffffLL || heads < 1 || nseg < 1)
+        return PVC_ERR_INVALID_ARG;
+    if (!(base > 0.0f) || base != base) return PVC_ERR_INVALID_ARG;
+    if (head_dim < 2 || head_dim > 2 * kMaxHalf || (head_dim & 1)) return PVC_ERR_UNSUPPORTED;
+
+    RopeFreqs freqs;
+    for (int j = 0; j < head_dim / 2; ++j)
+        freqs.f[j] = (float)pow((double)base, -2.0 * j / (double)head_dim);
+    hipStream_t s = as_stream(stream);
+    const auto* qi = static_cast<const uint16_t*>(q_in);
+    auto* qo = static_cast<uint16_t*>(q_out);
+    const auto* ki = static_cast<const uint16_t*>(k_in);
+    auto* ko = static_cast<uint16_t*>(k_out);
+    if (head_dim % 16 == 0) {
+        const int64_t hgroups = (heads + kHeadsPerThread - 1) / kHeadsPerThread;
+        const int64_t threads = total_tokens * (head_dim / 16) * hgroups;
+        const int64_t nblk = (threads + kRopeThreads - 1) / kRopeThreads;
+        hipLaunchKernelGGL(rope_vec_kernel, dim3((unsigned)nblk), dim3(kRopeThreads), 0, s, qi, qo, ki,
+                           ko, total_tokens, heads, head_dim, cu_seqlens, nseg, freqs, dev_error);
+    } else {
+        const int64_t threads = total_tokens * (head_dim / 2);
+        const int64_t nblk = (threads + kRopeThreads - 1) / kRopeThreads;
+        hipLaunchKernelGGL(rope_scalar_kernel, dim3((unsigned)nblk), dim3(kRopeThreads), 0, s, qi, qo,
+                           ki, ko, total_tokens, heads, head_dim, cu_seqlens, nseg, freqs, dev_error);
+    }
+    return launch_status();
+}

@@ -1,0 +1,122 @@
+"""GPU parity for pack_build and validate_cu_seqlens: bit-exact against the oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import dev_i32, say
+from oracle import pack as P
+from workloads import CONFIG_NAMES, make_workload, token_ids
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pvc():
+    import packed_varlen_causal_amd as m
+    assert torch.cuda.is_available()
+    return m
+
+
+def _run_pack(pvc, lengths, tokens, is_pad, T=None):
+    lt = dev_i32(lengths)
+    tt = dev_i32(tokens) if tokens is not None else None
+    pt = torch.from_numpy(np.asarray(is_pad, np.uint8)).cuda() if is_pad is not None else None
+    out = pvc.pack_build(lt, tt, pt, total_tokens=T)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def _compare(got, ref):
+    assert got["dev_error"][0] == ref["error"] == 0
+    assert (got["cu_seqlens"] == ref["cu_seqlens"]).all()
+    assert got["max_seqlen"][0] == ref["max_seqlen"]
+    for key in ("segment_ids", "position_ids", "shifted_labels", "loss_mask"):
+        assert (got[key] == ref[key]).all(), key
+    assert got["num_targets"][0] == ref["num_targets"]
+
+
+def test_nine_token_example(pvc, golden):
+    case = golden("packing_examples.json")["cu_seqlens"][1]
+    say("  pack_build nine-token example")
+    toks = np.arange(100, 109, dtype=np.int32)
+    got = _run_pack(pvc, case["lengths"], toks, None)
+    assert got["cu_seqlens"].tolist() == case["cu_seqlens"]
+    assert got["segment_ids"].tolist() == case["segment_ids"]
+    assert got["position_ids"].tolist() == case["position_ids"]
+    assert got["max_seqlen"][0] == case["max_seqlen"]
+
+
+def test_labels_m020_example(pvc, golden):
+    case = golden("packing_examples.json")["labels"][0]
+    toks = np.asarray([t for s in case["samples"] for t in s], np.int32)
+    got = _run_pack(pvc, [3, 2], toks, None)
+    want = [-100 if x is None else x for x in case["pre_shifted_labels"]]
+    assert got["shifted_labels"].tolist() == want
+    assert got["num_targets"][0] == case["num_targets"]
+
+
+@pytest.mark.parametrize("name", CONFIG_NAMES)
+def test_workloads_full_size(pvc, name):
+    w = make_workload(name)
+    say(f"  pack_build {name}: T={w.total_tokens} nseg={w.nseg}")
+    toks = token_ids(w)
+    got = _run_pack(pvc, w.lengths, toks, w.is_pad)
+    _compare(got, P.pack_build(w.lengths, toks, w.is_pad))
+
+
+def test_many_segments_multi_chunk_scan(pvc):
+    """More than 8192 segments exercises the reduce / top-scan / apply path."""
+    w = make_workload("short", total=1 << 20)
+    assert w.nseg > 8192 * 1.5
+    say(f"  pack_build multi-chunk: T={w.total_tokens} nseg={w.nseg}")
+    toks = token_ids(w)
+    got = _run_pack(pvc, w.lengths, toks, w.is_pad)
+    _compare(got, P.pack_build(w.lengths, toks, w.is_pad))
+
+
+@pytest.mark.parametrize("lengths", [[1], [1] * 3000, [5000], [1, 2047, 1, 1, 3000, 7]])
+def test_edge_lengths(pvc, lengths):
+    T = sum(lengths)
+    toks = np.random.default_rng(T).integers(3, 32000, T).astype(np.int32)
+    say(f"  pack_build edge nseg={len(lengths)} T={T}")
+    got = _run_pack(pvc, lengths, toks, None)
+    _compare(got, P.pack_build(lengths, toks))
+
+
+def test_without_tokens(pvc):
+    got = _run_pack(pvc, [3, 2, 4], None, None, T=9)
+    assert got["cu_seqlens"].tolist() == [0, 3, 5, 9]
+    assert "shifted_labels" not in got
+
+
+@pytest.mark.parametrize("lengths,T,bits", [
+    ([3, 0, 4], 7, P.ERR_LENGTH),
+    ([3, -2, 4], 5, P.ERR_LENGTH),
+    ([3, 2, 4], 10, P.ERR_TOTAL),
+    ([3, 2, 4], 8, P.ERR_TOTAL),
+])
+def test_error_bits(pvc, lengths, T, bits):
+    toks = np.full(T, 7, np.int32)
+    say(f"  pack_build error case {lengths} T={T}")
+    got = _run_pack(pvc, lengths, toks, None)
+    assert got["dev_error"][0] & bits
+    assert P.pack_build(lengths, toks)["error"] & bits or bits == P.ERR_TOTAL
+
+
+def test_validate_bits(pvc, golden):
+    bad = golden("packing_examples.json")["bad_prefix"]
+    cases = [
+        ([0, 3, 5, 9], 9, 4, None),
+        ([1, 3, 5, 9], 9, 4, None),
+        ([0, 3, 3, 9], 9, 6, None),
+        ([0, 5, 3, 9], 9, 6, None),
+        ([0, 3, 5, 8], 9, 4, None),
+        ([0, 3, 5, 9], 9, 3, None),
+        (bad["cu_seqlens"], 9, 4, None),
+        (bad["cu_seqlens"], 9, 4, bad["lengths"]),
+    ]
+    for cu, T, mx, lens in cases:
+        err = pvc.validate_cu_seqlens(dev_i32(cu), T, mx, None if lens is None else dev_i32(lens))
+        torch.cuda.synchronize()
+        assert int(err.item()) == P.validate_cu(cu, T, mx, lens), (cu, T, mx, lens)

@@ -1,0 +1,148 @@
+"""The C ABI library loads and exports every symbol include/pvc.h declares, and
+its host-side argument checks reject bad calls before any GPU work (CPU only:
+every call here returns before a HIP runtime call)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pvc.h")
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pvc_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    path = os.path.join(ROOT, "packed_varlen_causal_amd", "libpvc.so")
+    if not os.path.exists(path):
+        from packed_varlen_causal_amd.build import build
+        build()
+    return ctypes.CDLL(path)
+
+
+def test_header_declares_the_hot_path():
+    names = declared_functions()
+    for must in ("pvc_pack_build", "pvc_validate_cu_seqlens", "pvc_rope_thd_apply", "pvc_attn_plan",
+                 "pvc_varlen_attn_fwd", "pvc_varlen_attn_fwd_planned", "pvc_padded_attn_fwd_sbhd",
+                 "pvc_attn_workspace_size", "pvc_pack_build_workspace_size", "pvc_status_string"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    path = os.path.join(ROOT, "packed_varlen_causal_amd", "libpvc.so")
+    dyn = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(pvc_\w+)", dyn))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_library_is_gfx950_code_object():
+    """The library built here embeds a device code object for gfx950 only."""
+    path = os.path.join(ROOT, "packed_varlen_causal_amd", "libpvc.so")
+    sections = subprocess.run(["/opt/rocm/lib/llvm/bin/llvm-readelf", "-S", path],
+                              capture_output=True, text=True, check=True).stdout
+    assert ".hip_fatbin" in sections
+    with open(path, "rb") as f:
+        blob = f.read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
+    assert b"gfx942" not in blob and b"gfx90a" not in blob
+
+
+def test_status_strings(lib):
+    lib.pvc_status_string.restype = ctypes.c_char_p
+    lib.pvc_version.restype = ctypes.c_char_p
+    assert lib.pvc_status_string(0) == b"ok"
+    assert b"NULL" in lib.pvc_status_string(1)
+    assert lib.pvc_status_string(99) == b"unknown status"
+    assert b"gfx950" in lib.pvc_version()
+
+
+def test_workspace_queries(lib):
+    lib.pvc_attn_workspace_size.restype = ctypes.c_size_t
+    lib.pvc_attn_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int32]
+    lib.pvc_pack_build_workspace_size.restype = ctypes.c_size_t
+    lib.pvc_pack_build_workspace_size.argtypes = [ctypes.c_int32]
+    small = lib.pvc_attn_workspace_size(9, 3)
+    big = lib.pvc_attn_workspace_size(131072, 57)
+    assert 0 < small < big
+    assert big >= 131072 * 8            # per-row key ranges
+    assert lib.pvc_attn_workspace_size(0, 1) == 0
+    assert lib.pvc_pack_build_workspace_size(100) == 0
+    assert lib.pvc_pack_build_workspace_size(1 << 20) > 0
+
+
+def _vp(x):
+    return ctypes.c_void_p(x)
+
+
+def test_null_and_range_checks_return_before_gpu_work(lib):
+    P = ctypes.c_void_p
+    I32, I64, SZ, F32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    lib.pvc_pack_build.restype = I32
+    lib.pvc_pack_build.argtypes = [P, P, P, I32, I64, I32, P, P, P, P, P, P, P, P, P, SZ, P]
+    fake = _vp(0x100000)  # never dereferenced: every call below fails its host checks first
+    # NULL lengths / cu
+    assert lib.pvc_pack_build(None, None, None, 3, 9, -100, fake, None, None, None, None, None, None,
+                              None, None, 0, None) == 1
+    # labels requested without tokens
+    assert lib.pvc_pack_build(fake, None, None, 3, 9, -100, fake, None, None, fake, None, None, None,
+                              None, None, 0, None) == 1
+    # nseg < 1, total out of int32 range
+    assert lib.pvc_pack_build(fake, None, None, 0, 9, -100, fake, None, None, None, None, None, None,
+                              None, None, 0, None) == 2
+    assert lib.pvc_pack_build(fake, None, None, 3, 1 << 31, -100, fake, None, None, None, None, None,
+                              None, None, None, 0, None) == 2
+    # large nseg needs a workspace
+    assert lib.pvc_pack_build(fake, None, None, 1 << 20, 1 << 22, -100, fake, None, None, None, None,
+                              None, None, None, None, 0, None) == 4
+
+    lib.pvc_rope_thd_apply.restype = I32
+    lib.pvc_rope_thd_apply.argtypes = [P, P, P, P, I64, I32, I32, P, I32, F32, P, P]
+    assert lib.pvc_rope_thd_apply(None, fake, None, None, 9, 2, 64, fake, 3, 1e4, None, None) == 1
+    assert lib.pvc_rope_thd_apply(fake, fake, fake, None, 9, 2, 64, fake, 3, 1e4, None, None) == 1
+    assert lib.pvc_rope_thd_apply(fake, fake, None, None, 9, 2, 63, fake, 3, 1e4, None, None) == 3
+    assert lib.pvc_rope_thd_apply(fake, fake, None, None, 9, 2, 512, fake, 3, 1e4, None, None) == 3
+    assert lib.pvc_rope_thd_apply(fake, fake, None, None, 9, 2, 64, fake, 3, -1.0, None, None) == 2
+
+    lib.pvc_attn_plan.restype = I32
+    lib.pvc_attn_plan.argtypes = [P, I32, I64, I32, I32, P, SZ, P, P]
+    assert lib.pvc_attn_plan(None, 3, 9, 4, 1, fake, 1 << 20, None, None) == 1
+    assert lib.pvc_attn_plan(fake, 3, 9, 4, 1, fake, 16, None, None) == 4
+    assert lib.pvc_attn_plan(fake, 3, 9, 0, 1, fake, 1 << 20, None, None) == 2
+
+    lib.pvc_varlen_attn_fwd_planned.restype = I32
+    lib.pvc_varlen_attn_fwd_planned.argtypes = [P, P, P, P, P, I64, I32, I32, I32, I32, P, SZ, P, P]
+    a, b, c, o = (_vp(0x100000 * (i + 1)) for i in range(4))
+    assert lib.pvc_varlen_attn_fwd_planned(a, b, c, o, None, 9, 2, 96, 1, 0, fake, 1 << 20, None, None) == 3
+    assert lib.pvc_varlen_attn_fwd_planned(a, b, c, o, None, 9, 2, 64, 1, 7, fake, 1 << 20, None, None) == 2
+    assert lib.pvc_varlen_attn_fwd_planned(a, b, c, None, None, 9, 2, 64, 1, 0, fake, 1 << 20, None, None) == 1
+    # misaligned q
+    assert lib.pvc_varlen_attn_fwd_planned(_vp(0x100002), b, c, o, None, 9, 2, 64, 1, 0, fake, 1 << 20,
+                                           None, None) == 2
+    # out aliasing q
+    assert lib.pvc_varlen_attn_fwd_planned(a, b, c, a, None, 9, 2, 64, 1, 0, fake, 1 << 20, None, None) == 2
+    # workspace too small for 9 tokens
+    assert lib.pvc_varlen_attn_fwd_planned(a, b, c, o, None, 9, 2, 64, 1, 0, fake, 8, None, None) == 4
+
+    lib.pvc_padded_attn_fwd_sbhd.restype = I32
+    lib.pvc_padded_attn_fwd_sbhd.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32, P]
+    assert lib.pvc_padded_attn_fwd_sbhd(a, b, c, o, None, 2, 4, 2, 64, 1, 0, None) == 1
+    assert lib.pvc_padded_attn_fwd_sbhd(a, b, c, o, fake, 0, 4, 2, 64, 1, 0, None) == 2
+    assert lib.pvc_padded_attn_fwd_sbhd(a, b, c, o, fake, 2, 4, 2, 64, 1, 5, None) == 2
+    assert lib.pvc_padded_attn_fwd_sbhd(a, b, c, o, fake, 2, 4, 2, 80, 1, 0, None) == 3
+
+
+def test_python_binding_imports_without_gpu():
+    import packed_varlen_causal_amd as pvc
+    assert "gfx950" in pvc.version()
+    assert pvc.error_names(1 | 32) == ["CU0", "MISMATCH"]
