@@ -1,0 +1,343 @@
+"""Benchmark of the packed varlen causal attention path on one MI355X.
+
+One step = the whole hot path over one packed batch already resident in HBM:
+  pack_build (cu_seqlens, segment ids, positions, shifted labels, loss mask,
+  target count) -> rope_thd_apply on q and k -> attn_plan -> varlen_attn_fwd.
+Default workload: 8 SFT packs of 4096 tokens (lognormal sample lengths packed
+first-fit-decreasing, pad tails as segments), 32 heads, head_dim 128, causal.
+
+Printed: ONE JSON line.  value = useful attention TFLOP/s over the whole step
+(useful FLOPs = 4 d H per same-segment causal pair of the real samples; pad
+segments are computed but not counted).  Per-kernel durations come from HIP
+events recorded on the stream the kernels run on.  Beside it, in the same
+process: the same kernel on the padded SBHD layout, the other workloads'
+attention rates, and the fp64 CPU oracle timed on a bounded sample of rows.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "varlen causal attn fwd useful TFLOP/s (% bf16 MFMA peak) + effective tokens/s"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+
+
+def useful_flops(lengths, is_pad, heads, head_dim, causal=True) -> float:
+    L = np.asarray(lengths, np.float64)[np.asarray(is_pad) == 0]
+    pairs = (L * (L + 1) / 2).sum() if causal else (L * L).sum()
+    return 4.0 * head_dim * heads * pairs
+
+
+def attn_bytes(T, heads, head_dim) -> float:
+    """Compulsory HBM bytes of one attention launch: read q, k, v, write o (bf16)."""
+    return 4.0 * T * heads * head_dim * 2
+
+
+def rope_bytes(T, heads, head_dim) -> float:
+    return 2.0 * 2 * T * heads * head_dim * 2          # q and k, read + write
+
+
+def pack_bytes(T, nseg) -> float:
+    return T * (4 + 4 + 4 + 4 + 1) + nseg * (4 + 1 + 4)   # tokens in; seg, pos, label, mask out
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Inputs:
+    def __init__(self, name, torch, pvc, scale="full", keep_host=False):
+        from workloads import make_workload
+        self.w = w = make_workload(name, scale=scale)
+        dev = torch.device("cuda")
+        t0 = time.time()
+        q, k, v = w.qkv()
+        to = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+        self.q, self.k, self.v = to(q), to(k), to(v)
+        self.host_qkv = (q, k, v) if keep_host else None
+        del q, k, v
+        self.lengths = torch.from_numpy(w.lengths).to(dev)
+        self.is_pad = torch.from_numpy(w.is_pad).to(dev)
+        self.tokens = torch.from_numpy(w.tokens()).to(dev)
+        self.q_rot = torch.empty_like(self.q)
+        self.k_rot = torch.empty_like(self.k)
+        self.T, self.H, self.D = w.total_tokens, w.heads, w.head_dim
+        self.max_seqlen = int(w.lengths.max())
+        self.flops = useful_flops(w.lengths, w.is_pad, w.heads, w.head_dim, w.causal)
+        self.real_tokens = int(w.real_lengths.sum())
+        self.out = torch.empty_like(self.q)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.ws = torch.empty(pvc.attn_workspace_size(self.T, w.nseg), dtype=torch.uint8, device=dev)
+        log(f"[bench] {name}: T={self.T} nseg={w.nseg} H={self.H} d={self.D} inputs in {time.time() - t0:.1f}s")
+
+
+def run_step(torch, pvc, x, ev=None):
+    """One pass of the hot path; ev = list of 5 events to bracket the four stages."""
+    rec = (lambda i: ev[i].record()) if ev is not None else (lambda i: None)  # noqa: E731
+    rec(0)
+    meta = pvc.pack_build(x.lengths, x.tokens, x.is_pad, dev_error=x.err)
+    rec(1)
+    pvc.rope_thd_apply(x.q, x.k, meta["cu_seqlens"], x.w.rope_base, q_out=x.q_rot, k_out=x.k_rot,
+                       dev_error=x.err)
+    rec(2)
+    plan = pvc.AttnPlan(meta["cu_seqlens"], x.T, x.max_seqlen, x.w.causal, dev_error=x.err, workspace=x.ws)
+    rec(3)
+    pvc.varlen_attn_fwd(x.q_rot, x.k_rot, x.v, plan=plan, causal=x.w.causal, out=x.out)
+    rec(4)
+
+
+def time_steps(torch, pvc, x, steps, warmup):
+    for _ in range(warmup):
+        run_step(torch, pvc, x)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        run_step(torch, pvc, x, evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    stage = np.asarray([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evs])
+    if int(x.err.item()) != 0:
+        raise RuntimeError(f"device error bits {pvc.error_names(int(x.err.item()))}")
+    return total_ms / steps, stage.mean(axis=0)
+
+
+def time_attn_only(torch, pvc, x, steps, warmup):
+    meta = pvc.pack_build(x.lengths, x.tokens, x.is_pad, dev_error=x.err)
+    pvc.rope_thd_apply(x.q, x.k, meta["cu_seqlens"], x.w.rope_base, q_out=x.q_rot, k_out=x.k_rot)
+    plan = pvc.AttnPlan(meta["cu_seqlens"], x.T, x.max_seqlen, x.w.causal, dev_error=x.err, workspace=x.ws)
+    for _ in range(warmup):
+        pvc.varlen_attn_fwd(x.q_rot, x.k_rot, x.v, plan=plan, out=x.out)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        pvc.varlen_attn_fwd(x.q_rot, x.k_rot, x.v, plan=plan, out=x.out)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def padded_baseline(torch, pvc, x, reps=3, max_chunk_bytes=24 << 30):
+    """Same kernel on padded SBHD [L, B, H, d]; large batches run in chunks of
+    samples (exact: samples are independent) and the chunk times are summed."""
+    w = x.w
+    L = int(w.pad_len)
+    real = w.real_lengths
+    B = len(real)
+    per_sample = 4 * L * x.H * x.D * 2
+    chunk = max(1, min(B, max_chunk_bytes // per_sample))
+    dev = torch.device("cuda")
+    total_ms, timed = 0.0, 0
+    nchunks = (B + chunk - 1) // chunk
+    chunks_to_time = min(nchunks, 2 if L > 16384 else nchunks)
+    for c in range(chunks_to_time):
+        nb = min(chunk, B - c * chunk)
+        g = torch.Generator(device=dev).manual_seed(1234 + c)
+        q, k, v = (torch.randn((L, nb, x.H, x.D), device=dev, generator=g).to(torch.bfloat16)
+                   for _ in range(3))
+        sl = torch.from_numpy(real[c * chunk: c * chunk + nb].astype(np.int32)).to(dev)
+        out = torch.empty_like(q)
+        pvc.padded_attn_fwd_sbhd(q, k, v, sl, True, out=out)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            pvc.padded_attn_fwd_sbhd(q, k, v, sl, True, out=out)
+        b.record()
+        torch.cuda.synchronize()
+        total_ms += a.elapsed_time(b) / reps
+        timed += nb
+        del q, k, v, out
+        torch.cuda.empty_cache()
+    ms = total_ms * B / timed
+    padded_pairs = B * L * (L + 1) / 2
+    real_pairs = (real.astype(np.float64) * (real + 1) / 2).sum()
+    return {
+        "layout": f"SBHD [{L}, {B}, {x.H}, {x.D}] bf16, key-padding mask, causal",
+        "ms": round(ms, 4),
+        "useful_tflops": round(x.flops / (ms * 1e-3) / 1e12, 2),
+        "speedup_of_varlen": None,
+        "computed_pairs_ratio": round(padded_pairs / real_pairs, 2),
+        "samples_timed": timed,
+        "extrapolated": timed < B,
+    }
+
+
+def cpu_baseline(x, seconds=12.0):
+    """The fp64 oracle on a bounded, seeded sample of query rows of the same workload.
+
+    Only the attention oracle is timed (it is the step's cost on the CPU too);
+    it runs on the workload's bf16 q/k/v as generated, since the arithmetic
+    per row does not depend on the values."""
+    from oracle import attention as A
+    from oracle import pack as P
+
+    w = x.w
+    threads = len(os.sched_getaffinity(0))
+    cu = P.pack_build(w.lengths)["cu_seqlens"]
+    pos = P.positions_from_cu(cu)
+    seg_pad = np.repeat(w.is_pad, w.lengths)
+    real_rows = np.nonzero(seg_pad == 0)[0]
+    q, k, v = x.host_qkv if x.host_qkv is not None else w.qkv()
+    rng = np.random.default_rng(99)
+    # calibrate on a small sample, then size the timed sample to ~`seconds`
+    probe = rng.choice(real_rows, size=min(64, real_rows.size), replace=False)
+    t0 = time.perf_counter()
+    A.attention_rows(q, k, v, cu, probe, True, threads=threads)
+    dt = time.perf_counter() - t0
+    n = int(min(real_rows.size, max(64, 64 * seconds / max(dt, 1e-3))))
+    rows = rng.choice(real_rows, size=n, replace=False)
+    t0 = time.perf_counter()
+    A.attention_rows(q, k, v, cu, rows, True, threads=threads)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.head_dim * w.heads * (pos[rows] + 1).sum()
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{n} random real query rows x {w.heads} heads of the {w.name} workload, "
+                  f"fp64 attention oracle (C loop, {threads} threads, {dt:.1f} s)",
+        "seconds": round(dt, 2),
+        "cpu": model,
+        "host": platform.node(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="sft")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip padded baseline and other workloads")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import packed_varlen_causal_amd as pvc
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+
+    x = Inputs(args.workload, torch, pvc, keep_host=not args.no_cpu_baseline)
+    ms_step, stage_ms = time_steps(torch, pvc, x, args.steps, args.warmup)
+    pack_ms, rope_ms, plan_ms, attn_ms = (float(v) for v in stage_ms)
+    value = x.flops / (ms_step * 1e-3) / 1e12
+    attn_tflops = x.flops / (attn_ms * 1e-3) / 1e12
+    a_bytes = attn_bytes(x.T, x.H, x.D)
+    ai = x.flops / a_bytes
+    hbm_roof = ai * PEAK_HBM_GBPS / 1e3
+    bound = "hbm" if hbm_roof < PEAK_BF16_TFLOPS else "mfma"
+    if bound == "hbm":
+        achieved, peak, unit, traffic_unit = a_bytes / (attn_ms * 1e-3) / 1e9, PEAK_HBM_GBPS, "GB/s", a_bytes
+    else:
+        achieved, peak, unit, traffic_unit = attn_tflops, PEAK_BF16_TFLOPS, "TFLOP/s", x.flops
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": x.w.name, "description": x.w.note, "total_tokens": x.T,
+            "real_tokens": x.real_tokens, "segments": x.w.nseg, "pad_segments": int(x.w.is_pad.sum()),
+            "max_seqlen": x.max_seqlen, "heads": x.H, "head_dim": x.D, "causal": True,
+            "step": "pack_build + rope_thd_apply(q,k) + attn_plan + varlen_attn_fwd",
+        },
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "effective_tokens_per_s": round(x.real_tokens / (ms_step * 1e-3), 1),
+        "kernels": {
+            "pack_build": {"ms": round(pack_ms, 4), "gbps": round(pack_bytes(x.T, x.w.nseg) / (pack_ms * 1e-3) / 1e9, 1)},
+            "rope_thd_apply": {"ms": round(rope_ms, 4),
+                               "gbps": round(rope_bytes(x.T, x.H, x.D) / (rope_ms * 1e-3) / 1e9, 1)},
+            "attn_plan": {"ms": round(plan_ms, 4)},
+            "varlen_attn_fwd": {"ms": round(attn_ms, 4), "useful_tflops": round(attn_tflops, 2),
+                                "pct_bf16_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
+                                "compulsory_gbps": round(a_bytes / (attn_ms * 1e-3) / 1e9, 1),
+                                "arith_intensity": round(ai, 1)},
+        },
+        "roofline": {
+            "kernel": "attn_fwd_kernel<128, causal, bf16 out>",
+            "bound": bound,
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": unit,
+            "frac": round(achieved / peak, 4),
+            "traffic": None,
+            "algorithmic_per_launch": traffic_unit,
+            "mfma_frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "hbm_roofline_tflops": round(min(hbm_roof, PEAK_BF16_TFLOPS), 1),
+        },
+    }
+    torch.cuda.synchronize()
+
+    if not args.no_extras:
+        res["padded_sbhd"] = padded_baseline(torch, pvc, x)
+        res["padded_sbhd"]["speedup_of_varlen"] = round(res["padded_sbhd"]["ms"] / attn_ms, 2)
+        others = {}
+        for name in ("pretrain", "longctx", "short"):
+            if name == x.w.name:
+                continue
+            y = Inputs(name, torch, pvc)
+            ms_s, st = time_steps(torch, pvc, y, max(3, args.steps // 2), 2)
+            a_ms = float(st[3])
+            tf = y.flops / (a_ms * 1e-3) / 1e12
+            yb = attn_bytes(y.T, y.H, y.D)
+            roof = min(PEAK_BF16_TFLOPS, y.flops / yb * PEAK_HBM_GBPS / 1e3)
+            others[name] = {
+                "T": y.T, "segments": y.w.nseg, "heads": y.H, "head_dim": y.D,
+                "step_ms": round(ms_s, 4), "attn_ms": round(a_ms, 4), "attn_useful_tflops": round(tf, 2),
+                "attn_pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+                "attn_pct_of_roofline": round(100 * tf / roof, 2), "roofline_tflops": round(roof, 1),
+                "rope_gbps": round(rope_bytes(y.T, y.H, y.D) / (float(st[1]) * 1e-3) / 1e9, 1),
+                "effective_tokens_per_s": round(int(y.w.real_lengths.sum()) / (ms_s * 1e-3), 1),
+            }
+            del y
+            torch.cuda.empty_cache()
+        res["other_workloads"] = others
+
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(x, args.cpu_seconds)
+        res["cpu_baseline"] = cb
+        res["gpu_over_cpu_oracle"] = round(attn_tflops / cb["value"], 1)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

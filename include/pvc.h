@@ -156,8 +156,8 @@ pvc_status pvc_validate_cu_seqlens(const int32_t* cu_seqlens, int32_t nseg,
  *   theta = fp32(p) * f_j                 (one fp32 product)
  *   y_j          = x_j cos(theta) - x_{j+d/2} sin(theta)
  *   y_{j+d/2}    = x_{j+d/2} cos(theta) + x_j sin(theta)
- * computed in fp32 and rounded to bf16 (nearest even).  Position 0 is the
- * identity, bit for bit.
+ * with sin, cos and the rotation in double and one rounding to bf16 (nearest
+ * even).  Position 0 is the identity, bit for bit.
  *
  * q_in/q_out  [total_tokens, heads, head_dim] bf16; q_out may equal q_in
  * k_in/k_out  same shape, both NULL to rotate q only; k_out may equal k_in

@@ -4,9 +4,17 @@
 // "pitfall two": reset positions per document).
 //
 // Rotate-half pairing (j, j + d/2), angle theta_j = fp32(p) * f_j with the fp32
-// frequency table f_j = base^(-2j/d) computed on the host in double.  sin and
-// cos come from the device's full-range sincosf; the rotation runs in fp32 and
-// rounds once to bf16.
+// frequency table f_j = base^(-2j/d) computed on the host in double.  The angle
+// stays that one fp32 product; sin, cos and the rotation are evaluated in
+// double and the result is rounded once to bf16.  fp32 rotation would lose
+// the result's leading bits whenever x_j cos and x_{j+d/2} sin nearly cancel;
+// in double the single bf16 rounding is the only one that matters.  The kernel
+// is bound by HBM traffic, and an fp64 FMA costs the same issue slot as an
+// unpacked fp32 one on this chip, so the wider arithmetic is free here.
+//
+// Double -> bf16 rounding: round to odd at fp32 precision (24 bits), then
+// round to nearest even at bf16 precision (8 bits); with at least two spare
+// bits the pair equals one direct round-to-nearest-even of the double.
 //
 // Work layout: one thread owns one token, eight consecutive pairs (16 bytes of
 // each half-row) and kHeadsPerThread heads of q and of k.  It evaluates its
@@ -31,7 +39,20 @@ struct RopeFreqs {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ inline void rotate8(const u32x4& a, const u32x4& b, const float* c, const float* s,
+// Round a double to bf16, nearest even, through fp32 round-to-odd.
+__device__ inline uint32_t f64_to_bf16_bits(double y) {
+    const float f = (float)y;                          // nearest even at fp32
+    uint32_t fb = __float_as_uint(f);
+    const double back = (double)f;
+    if (back != y) {
+        if (fabs(back) > fabs(y)) fb -= 1u;            // undo an outward rounding: truncate
+        fb |= 1u;                                      // sticky bit: round to odd
+    }
+    fb += 0x7FFFu + ((fb >> 16) & 1u);                 // nearest even at bf16
+    return fb >> 16;
+}
+
+__device__ inline void rotate8(const u32x4& a, const u32x4& b, const double* c, const double* s,
                                u32x4& ya, u32x4& yb) {
     // a holds x_j .. x_{j+7}, b holds x_{j+d/2} .. x_{j+d/2+7}; two bf16 per dword
 #pragma unroll
@@ -40,12 +61,12 @@ __device__ inline void rotate8(const u32x4& a, const u32x4& b, const float* c, c
 #pragma unroll
         for (int hlf = 0; hlf < 2; ++hlf) {
             const int e = 2 * w + hlf;
-            const float x1 = bf16_to_f32(uint16_t(a[w] >> (16 * hlf)));
-            const float x2 = bf16_to_f32(uint16_t(b[w] >> (16 * hlf)));
-            const float y1 = x1 * c[e] - x2 * s[e];
-            const float y2 = x2 * c[e] + x1 * s[e];
-            ra |= uint32_t(f32_to_bf16_rne(y1)) << (16 * hlf);
-            rb |= uint32_t(f32_to_bf16_rne(y2)) << (16 * hlf);
+            const double x1 = (double)bf16_to_f32(uint16_t(a[w] >> (16 * hlf)));
+            const double x2 = (double)bf16_to_f32(uint16_t(b[w] >> (16 * hlf)));
+            const double y1 = x1 * c[e] - x2 * s[e];
+            const double y2 = x2 * c[e] + x1 * s[e];
+            ra |= f64_to_bf16_bits(y1) << (16 * hlf);
+            rb |= f64_to_bf16_bits(y2) << (16 * hlf);
         }
         ya[w] = ra;
         yb[w] = rb;
@@ -73,12 +94,12 @@ __global__ __launch_bounds__(kRopeThreads) void rope_vec_kernel(
     if (!ok && ch == 0 && hg == 0) raise_error(dev_error, i >= en ? PVC_DEV_TOTAL : PVC_DEV_NOT_INCREASING);
     const float p = ok ? (float)(i - st) : 0.0f;     // malformed cu: identity (copy through)
 
-    float c[8], s[8];
+    double c[8], s[8];
     const int j0 = ch * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const float theta = p * freqs.f[j0 + e];      // one fp32 product
-        sincosf(theta, &s[e], &c[e]);
+        sincos((double)theta, &s[e], &c[e]);
     }
     const int half = D >> 1;
     const int h_lo = hg * kHeadsPerThread;
@@ -115,18 +136,19 @@ __global__ __launch_bounds__(kRopeThreads) void rope_scalar_kernel(
     const bool ok = st <= i && i < en;
     if (!ok && j == 0) raise_error(dev_error, i >= en ? PVC_DEV_TOTAL : PVC_DEV_NOT_INCREASING);
     const float p = ok ? (float)(i - st) : 0.0f;
-    float sn, cs;
-    sincosf(p * freqs.f[j], &sn, &cs);
+    const float theta = p * freqs.f[j];
+    double sn, cs;
+    sincos((double)theta, &sn, &cs);
     for (int t = 0; t < 2; ++t) {
         const uint16_t* src = t == 0 ? q_in : k_in;
         uint16_t* dst = t == 0 ? q_out : k_out;
         if (src == nullptr) break;
         for (int h = 0; h < H; ++h) {
             const int64_t row = (i * H + h) * (int64_t)D;
-            const float x1 = bf16_to_f32(src[row + j]);
-            const float x2 = bf16_to_f32(src[row + half + j]);
-            dst[row + j] = f32_to_bf16_rne(x1 * cs - x2 * sn);
-            dst[row + half + j] = f32_to_bf16_rne(x2 * cs + x1 * sn);
+            const double x1 = (double)bf16_to_f32(src[row + j]);
+            const double x2 = (double)bf16_to_f32(src[row + half + j]);
+            dst[row + j] = (uint16_t)f64_to_bf16_bits(x1 * cs - x2 * sn);
+            dst[row + half + j] = (uint16_t)f64_to_bf16_bits(x2 * cs + x1 * sn);
         }
     }
 }
@@ -155,7 +177,9 @@ extern "C" pvc_status pvc_rope_thd_apply(const void* q_in, void* q_out, const vo
     auto* qo = static_cast<uint16_t*>(q_out);
     const auto* ki = static_cast<const uint16_t*>(k_in);
     auto* ko = static_cast<uint16_t*>(k_out);
-    if (head_dim % 16 == 0) {
+    const bool aligned = ((reinterpret_cast<uintptr_t>(q_in) | reinterpret_cast<uintptr_t>(q_out) |
+                           reinterpret_cast<uintptr_t>(k_in) | reinterpret_cast<uintptr_t>(k_out)) & 15u) == 0;
+    if (head_dim % 16 == 0 && aligned) {
         const int64_t hgroups = (heads + kHeadsPerThread - 1) / kHeadsPerThread;
         const int64_t threads = total_tokens * (head_dim / 16) * hgroups;
         const int64_t nblk = (threads + kRopeThreads - 1) / kRopeThreads;

@@ -1,5 +1,6 @@
-"""GPU parity for rope_thd_apply: within one bf16 ulp of the fp64 oracle, and
-bit-exact where the pages fix the result (position 0, per-segment reset)."""
+"""GPU parity for rope_thd_apply: bit-exact against the fp64 oracle (both round
+the rotation, evaluated in double, once to bf16); an element whose exact value
+sits within the double evaluation error of a bf16 tie may differ by one ulp."""
 
 import numpy as np
 import pytest
@@ -28,11 +29,32 @@ def _ulp_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return np.abs(key(a) - key(b))
 
 
-def _check(got_bits, ref_bits, what):
+def _near_tie(x_bits: np.ndarray, positions, base: float) -> np.ndarray:
+    """Elements whose exact rotated value lies so close to a bf16 rounding
+    midpoint that two correct double evaluations may round to different
+    neighbours: distance to the midpoint below the double evaluation's error
+    bound, 8 * 2^-53 * (|x_j| + |x_{j+d/2}|), measured in bf16 ulps."""
+    d = x_bits.shape[-1]
+    x = R.bf16_bits_to_f64(x_bits)
+    y = R.rotate_f64(x, R.rope_angles(positions, d, base))
+    mag = np.abs(x[..., : d // 2]) + np.abs(x[..., d // 2:])
+    mag = np.concatenate([mag, mag], axis=-1)
+    ay = np.abs(y)
+    e = np.floor(np.log2(np.where(ay > 0, ay, 1.0)))
+    ulp = np.exp2(e - 7)
+    frac = ay / ulp - np.floor(ay / ulp)           # position between bf16 neighbours
+    tol = 8 * 2.0 ** -53 * mag / ulp
+    return np.abs(frac - 0.5) <= tol
+
+
+def _check(got_bits, ref_bits, what, x_bits=None, positions=None, base=10000.0):
+    """Bit-exact except near-tie elements (at most one ulp there)."""
     d = _ulp_diff(got_bits, ref_bits)
-    n1 = int((d == 1).sum())
-    say(f"    {what}: max ulp {int(d.max())}, elements off by 1 ulp: {n1} of {d.size}")
+    near = _near_tie(x_bits, positions, base) if x_bits is not None else np.zeros(d.shape, bool)
+    say(f"    {what}: {int((d > 0).sum())} of {d.size} elements differ (max {int(d.max())} ulp); "
+        f"near-tie elements {int(near.sum())}")
     assert d.max() <= 1, what
+    assert (d[~near] == 0).all(), what
 
 
 @pytest.mark.parametrize("name", CONFIG_NAMES)
@@ -45,8 +67,9 @@ def test_small_workloads_all_tokens(pvc, name):
     pvc.rope_thd_apply(qd, kd, dev_i32(cu), w.rope_base)
     torch.cuda.synchronize()
     gq, gk = host_bits(qd), host_bits(kd)
-    _check(gq, R.rope_apply(q, cu, w.rope_base), "q")
-    _check(gk, R.rope_apply(k, cu, w.rope_base), "k")
+    pos = P.positions_from_cu(cu)
+    _check(gq, R.rope_apply(q, cu, w.rope_base), "q", q, pos, w.rope_base)
+    _check(gk, R.rope_apply(k, cu, w.rope_base), "k", k, pos, w.rope_base)
     starts = cu[:-1]
     assert (gq[starts] == q[starts]).all() and (gk[starts] == k[starts]).all()   # p = 0 identity
 
@@ -64,7 +87,8 @@ def test_full_size_sampled_tokens(pvc, name):
     rng = np.random.default_rng(0)
     rows = np.unique(np.concatenate([cu[:-1], cu[1:] - 1, rng.integers(0, w.total_tokens, 3000)]))
     gq = host_bits(qd)
-    _check(gq[rows], R.rope_apply(q, cu, w.rope_base, rows=rows), "q sampled")
+    pos = P.positions_from_cu(cu)[rows]
+    _check(gq[rows], R.rope_apply(q, cu, w.rope_base, rows=rows), "q sampled", q[rows], pos, w.rope_base)
     assert (host_bits(kd) == gq).all()          # same input, same kernel: identical
     assert (gq[cu[:-1]] == q[cu[:-1]]).all()
 
@@ -109,7 +133,7 @@ def test_other_head_dims(pvc, d):
     qd = dev_bf16(q)
     pvc.rope_thd_apply(qd, None, dev_i32(cu), 500.0)
     torch.cuda.synchronize()
-    _check(host_bits(qd), R.rope_apply(q, cu, 500.0), f"d={d}")
+    _check(host_bits(qd), R.rope_apply(q, cu, 500.0), f"d={d}", q, P.positions_from_cu(cu), 500.0)
 
 
 def test_malformed_cu_sets_bits_and_copies(pvc):
