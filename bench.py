@@ -56,6 +56,30 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def counter_traffic(workload: str):
+    """HBM bytes per attention launch from the committed FETCH_SIZE/WRITE_SIZE
+    summary, if it was taken on this workload from the current kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_{workload}_hbm_counters.md")
+    src = os.path.join(ROOT, "packed_varlen_causal_amd", "csrc", "attn.hip")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(("|", "#", " ")):
+                key, _, val = line.partition(":")
+                fields[key.strip()] = val.strip()
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    if fields.get("attn_source_sha256_prefix") != sha:
+        return None
+    try:
+        return float(fields["attention_traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 class Inputs:
     def __init__(self, name, torch, pvc, scale="full", keep_host=False):
         from workloads import make_workload
@@ -237,6 +261,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip padded baseline and other workloads")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy 5 times (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -244,9 +270,18 @@ def main():
         sys.exit(2)
 
     import torch
-    import packed_varlen_causal_amd as pvc
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU")
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "reps": 5}), flush=True)
+        return
+    import packed_varlen_causal_amd as pvc
 
     x = Inputs(args.workload, torch, pvc, keep_host=not args.no_cpu_baseline)
     ms_step, stage_ms = time_steps(torch, pvc, x, args.steps, args.warmup)
@@ -299,7 +334,8 @@ def main():
             "peak": peak,
             "unit": unit,
             "frac": round(achieved / peak, 4),
-            "traffic": None,
+            "traffic": counter_traffic(x.w.name),
+            "traffic_unit": "bytes per launch (FETCH_SIZE x2.0 + WRITE_SIZE x1.0, copy-calibrated)",
             "algorithmic_per_launch": traffic_unit,
             "mfma_frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
             "hbm_roofline_tflops": round(min(hbm_roof, PEAK_BF16_TFLOPS), 1),
