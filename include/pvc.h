@@ -209,7 +209,7 @@ pvc_status pvc_attn_plan(const int32_t* cu_seqlens, int32_t nseg, int64_t total_
  *            before the final bf16 rounding); must not alias q, k or v
  * lse        NULL or [heads, total_tokens] fp32: natural-log sum of exponentials
  *            of the scaled scores of each row
- * head_dim   64 or 128
+ * head_dim   64 or 128; heads * head_dim at most 2^24 (PVC_ERR_INVALID_ARG)
  * total_tokens and causal must be those the plan was built with; otherwise
  * PVC_DEV_PLAN is set and nothing is written.
  * Arithmetic: bf16 MFMA products with fp32 accumulation; probabilities are
@@ -244,7 +244,7 @@ pvc_status pvc_varlen_attn_fwd(const void* q, const void* k, const void* v, void
  * L).  Only blocks wholly above the causal diagonal are skipped.  out has the
  * input's shape; its padded rows hold attention over the sample's valid keys.
  * seqlens [batch] int32 on the device, each in 1..max_len.  out_dtype as for
- * pvc_varlen_attn_fwd_planned.
+ * pvc_varlen_attn_fwd_planned; batch * heads * head_dim at most 2^24.
  */
 pvc_status pvc_padded_attn_fwd_sbhd(const void* q, const void* k, const void* v, void* out,
                                     const int32_t* seqlens, int32_t batch, int32_t max_len,

@@ -19,8 +19,9 @@
 //
 // Forward kernel: one 256-thread workgroup (four wave64s) per (head, tile).
 // Wave w owns query rows [128w' + 32w, +32).  Keys stream through LDS in
-// stages of 64 (double buffered: the next stage is fetched into registers
-// while the current one is consumed).  Per 32-key block a wave
+// stages of 64: K and V go from global memory straight into LDS (no register
+// round trip), double buffered, so stage st+1 is in flight while stage st is
+// computed.  Per 32-key block a wave
 //   S^T = K Q^T      8 (d=128) v_mfma_f32_32x32x16_bf16, K from LDS as the A
 //                    operand, Q^T held in registers as the B operand; each
 //                    lane then owns one query and 16 of the 32 keys
@@ -28,11 +29,14 @@
 //   online softmax   running max and sum per query in exp2 units; the row max
 //                    needs one lane-pair exchange (lane l <-> l^32)
 //   O^T += V^T P^T   the probabilities, rounded to bf16, are already in the B
-//                    operand layout; V^T is read from an LDS copy that was
-//                    transposed while staging
-// and skips any 32-key block that lies wholly outside its rows' segments or
-// above their diagonal, so cross-segment and above-diagonal blocks are never
-// computed.
+//                    operand layout; the V^T operand comes from row-major V in
+//                    LDS through the transposing LDS read (ds_read_b64_tr_b16)
+// A wave skips every 64-key stage that lies wholly outside its rows' segments
+// or above their diagonal, so cross-segment and above-diagonal blocks are never
+// computed.  The running max moves only when a row's new maximum exceeds it by
+// more than 2^8 (in probability), which leaves most stages without a rescale
+// of the accumulator.  LDS rows are unpadded; XOR swizzles on 16- and 32-byte
+// column chunks keep the operand reads free of bank conflicts.
 //
 // Grid to hardware: workgroups are dealt round-robin to the 8 XCDs, so the
 // block index is remapped to give each XCD a contiguous range of the
@@ -40,14 +44,17 @@
 // tiles that share a head's K/V run together on one L2.
 #include <math.h>
 
+#include <type_traits>
+
 #include "pvc_internal.h"
 
 namespace pvc {
 namespace {
 
-constexpr int kBM = 128;        // query rows per tile
+constexpr int kWaves = 4;       // waves per workgroup, 32 query rows each
+constexpr int kBM = 32 * kWaves; // query rows per tile
 constexpr int kBN = 64;         // keys per LDS stage
-constexpr int kThreads = 256;   // 4 waves x 32 rows
+constexpr int kThreads = 64 * kWaves;
 constexpr int kNumBuckets = 4096;
 constexpr int kSortThreads = 1024;
 constexpr int kNumXcd = 8;
@@ -208,21 +215,59 @@ __device__ inline f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& 
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Max over the lane pair (l, l^32): v_permlane32_swap hands each lane its
+// partner's value without a round trip through LDS.
 __device__ inline float lane_pair_max(float x) {
-    return fmaxf(x, __shfl_xor(x, 32, 64));
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+__device__ inline float lane_pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS tiles hold 64 keys x D bf16 with no padding, so each 1 KiB written by one
+// direct global->LDS load is contiguous.  Bank conflicts are removed by XOR
+// swizzles on the column chunks instead:
+//   K: 16-byte chunks, chunk ^ fk(row); the MFMA A-operand read (one row per
+//      lane, one 16-byte chunk) then covers distinct banks for any 8 or 16
+//      consecutive rows;
+//   V: 32-byte chunks, chunk ^ fv(row); the transposing read (four rows x one
+//      32-byte chunk per 16 lanes, and the next chunk for the next 16 lanes)
+//      covers distinct banks.
+template <int D> __device__ inline int k_swz(int row) {
+    if constexpr (D == 128) return row & 15;
+    else return (row & 7) ^ ((row >> 3) & 1);
+}
+template <int D> __device__ inline int v_swz(int row) {
+    if constexpr (D == 128) return ((row & 3) << 1) | ((row >> 1) & 1);
+    else return row & 3;
+}
+
+// Threshold (log2 units) by which a row's running max may lag before the
+// accumulator is rescaled: probabilities stay below 2^8.
+constexpr float kRescaleSlack = 8.0f;
+
 template <int D, bool CAUSAL, bool OUT_F32, bool SBHD>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(AttnParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_kernel(AttnParams p) {
     static_assert(D == 64 || D == 128, "head_dim");
-    constexpr int KPAD = D + 8;              // K row stride in LDS (bf16), 16 B pad
-    constexpr int VPAD = kBN + 4;            // V^T row stride in LDS (bf16), 8 B pad
     constexpr int NS = D / 16;               // MFMA k-steps for q.k
     constexpr int ND = D / 32;               // 32-wide d blocks of the output
-    constexpr int KCH = kBN * D / 8 / kThreads;      // 16-B K chunks per thread
-    constexpr int VKPT = D / 32;             // keys per thread in the V^T staging
-    __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBN * KPAD];
-    __shared__ __attribute__((aligned(16))) uint16_t sVt[2][D * VPAD];
+    constexpr int ROW_B = D * 2;             // bytes per key row in LDS
+    constexpr int TILE_B = kBN * ROW_B;      // bytes per K (or V) stage
+    constexpr int CHUNKS = TILE_B / 1024;    // 1 KiB direct loads per tile
+    constexpr int CPW = CHUNKS / kWaves;     // ... per wave
+    static_assert(CPW >= 1 && CPW * kWaves == CHUNKS, "staging split");
+    constexpr int ROWS_PER_CHUNK = 1024 / ROW_B;
+    constexpr int L16 = ROW_B / 16;          // 16-byte pieces per row
+    __shared__ __attribute__((aligned(1024))) uint16_t sK[2][kBN * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t sV[2][kBN * D];
 
     // ---- which (head, tile): XCD-contiguous remap of the block index
     const int nblk = gridDim.x;
@@ -262,7 +307,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     };
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int c = lane & 31;
     const int g = lane >> 5;
@@ -291,7 +336,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         max_start = last.x;
         min_end = first.y;
     }
-    // block key range
     int k_lo, k_hi;
     if constexpr (SBHD) {
         k_lo = 0;
@@ -310,49 +354,59 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         for (int s = 0; s < NS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
     }
 
-    // ---- staging registers
-    u32x4 kreg[KCH];
-    u32x4 vreg[VKPT];
-    const int v_dch = tid % (D / 8);                 // 8-wide d chunk of this thread's V rows
-    const int v_kg = tid / (D / 8);                  // key group: keys VKPT*v_kg ..
-    auto fetch = [&](int stage) {
+    // ---- direct global -> LDS staging.  Wave w writes the 1 KiB chunks
+    // w, w + kWaves, w + 2 kWaves, ... of each tile; lane l of a chunk lands
+    // at byte 16*l, so it fetches the 16-byte piece the swizzle puts there.
+    // Consecutive chunks of one wave are 16 (or 32) rows apart, which leaves
+    // the swizzle unchanged, so one per-lane offset serves all of them and a
+    // chunk only moves the uniform base pointer.
+    constexpr int CHUNK_ROWS = kWaves * ROWS_PER_CHUNK;     // rows between a wave's chunks
+    static_assert(CHUNK_ROWS % 16 == 0, "swizzle period");
+    const int64_t row_stride = SBHD ? (int64_t)p.B * H * D : (int64_t)H * D;   // elements per key row
+    const int64_t head_off = SBHD ? ((int64_t)b * H + head) * D : (int64_t)head * D;
+    const int fetch_rr = wave * ROWS_PER_CHUNK + lane / L16;   // row of chunk 0 in the stage
+    uint32_t k_loff, v_loff;
+    {
+        const int phys = lane % L16;
+        const int kpiece = phys ^ k_swz<D>(fetch_rr);
+        const int vpiece = (((phys >> 1) ^ v_swz<D>(fetch_rr)) << 1) | (phys & 1);
+        k_loff = (uint32_t)((fetch_rr * row_stride + kpiece * 8) * 2);
+        v_loff = (uint32_t)((fetch_rr * row_stride + vpiece * 8) * 2);
+    }
+    // one stage of K (or V) into LDS buffer `buf`
+    auto fetch = [&](const uint16_t* src, char* dst, uint32_t loff, int stage) {
         const int kt = k_lo + stage * kBN;
+        const char* base = reinterpret_cast<const char*>(src) + ((int64_t)kt * row_stride + head_off) * 2;
+        const bool ragged = kt + kBN - 1 > last_row;                       // uniform
 #pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int ci = tid + i * kThreads;
-            const int kr = ci / (D / 8), ch = ci % (D / 8);
-            const int krow = min(kt + kr, last_row);
-            kreg[i] = *reinterpret_cast<const u32x4*>(p.k + row_off(krow) + ch * 8);
-        }
-#pragma unroll
-        for (int i = 0; i < VKPT; ++i) {
-            const int vrow = min(kt + VKPT * v_kg + i, last_row);
-            vreg[i] = *reinterpret_cast<const u32x4*>(p.v + row_off(vrow) + v_dch * 8);
-        }
-    };
-    auto stash = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int ci = tid + i * kThreads;
-            const int kr = ci / (D / 8), ch = ci % (D / 8);
-            *reinterpret_cast<u32x4*>(&sK[buf][kr * KPAD + ch * 8]) = kreg[i];
-        }
-        // transpose: V[key][d] -> V^T[d][key]; VKPT consecutive keys per write
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int w = e >> 1, sh = (e & 1) * 16;
-            uint16_t* dst = &sVt[buf][(v_dch * 8 + e) * VPAD + VKPT * v_kg];
-            if constexpr (VKPT == 4) {
-                u32x2 pk;
-                pk.x = ((vreg[0][w] >> sh) & 0xFFFFu) | (((vreg[1][w] >> sh) & 0xFFFFu) << 16);
-                pk.y = ((vreg[2][w] >> sh) & 0xFFFFu) | (((vreg[3][w] >> sh) & 0xFFFFu) << 16);
-                *reinterpret_cast<u32x2*>(dst) = pk;
-            } else {
-                const uint32_t pk = ((vreg[0][w] >> sh) & 0xFFFFu) | (((vreg[1][w] >> sh) & 0xFFFFu) << 16);
-                *reinterpret_cast<uint32_t*>(dst) = pk;
+        for (int i = 0; i < CPW; ++i) {
+            int64_t shift = (int64_t)i * CHUNK_ROWS * row_stride * 2;   // bytes, uniform
+            if (ragged) {
+                // rows past the buffer re-read its last row (masked later)
+                const int over = max(kt + fetch_rr + i * CHUNK_ROWS - last_row, 0);
+                shift -= (int64_t)over * row_stride * 2;
             }
+            __builtin_amdgcn_global_load_lds(base + shift + loff,
+                                             (lds_void*)(dst + (wave + kWaves * i) * 1024), 16, 0, 0);
         }
     };
+
+    // ---- LDS read offsets.  Every swizzle term depends on the lane only, so
+    // each operand read is a per-lane base plus a compile-time offset.
+    //   K (A operand of S^T): row 32h + c, 16-byte piece (2s + g) ^ k_swz(c)
+    //   V (transposing read): row 32h + 16ks + 8hh + 4g + li/4, 32-byte chunk
+    //   (2j + chi) ^ v_swz(li/4), 8-byte piece li%4
+    uint32_t k_roff[NS], v_roff[ND];
+    {
+        const int li = lane & 15;
+        const int chi = (lane >> 4) & 1;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) k_roff[s] = c * ROW_B + (((2 * s + g) ^ k_swz<D>(c)) << 4);
+        const int vr = 4 * g + (li >> 2);
+#pragma unroll
+        for (int j = 0; j < ND; ++j)
+            v_roff[j] = vr * ROW_B + (((2 * j + chi) ^ v_swz<D>(vr)) << 5) + ((li & 3) << 3);
+    }
 
     // ---- running state (one query per lane; the lane pair (c, 0)/(c, 1)
     // shares the query and keeps identical m, disjoint halves of l and acc rows)
@@ -364,81 +418,145 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const float sl2 = p.scale_log2;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    if (nstages > 0) {
-        fetch(0);
-        stash(0);
-    }
-    __syncthreads();
-    for (int st = 0; st < nstages; ++st) {
-        const int buf = st & 1;
-        if (st + 1 < nstages) fetch(st + 1);
+    // ---- per-stage work.  A wave takes part in stage st only if some key of
+    // the stage is visible to one of its rows; it masks only stages that
+    // cross a segment edge or its diagonal.
+    auto stage_active = [&](int st) -> bool {
         const int kt = k_lo + st * kBN;
+        return wave_active && st >= 0 && st < nstages && kt < w_hi && kt + kBN > w_lo;
+    };
+    auto stage_full = [&](int st) -> bool {
+        const int kt = k_lo + st * kBN;
+        return kt >= max_start && kt + kBN <= min_end && (!CAUSAL || kt + kBN - 1 <= wr0);
+    };
+    char* const kbase = reinterpret_cast<char*>(&sK[0][0]);
+    char* const vbase = reinterpret_cast<char*>(&sV[0][0]);
+
+    // K operand: key 32h + c of the stage in buffer kb, k-step s
+    auto kop = [&](const char* kb, int h, int s) -> bf16x8 {
+        return *reinterpret_cast<const bf16x8*>(kb + k_roff[s] + 32 * h * ROW_B);
+    };
+    // V^T operand (d block j, 16-key step ks of half h) through the transposing read
+    auto vop = [&](const char* vb, int h, int ks, int j) -> bf16x8 {
+        const char* vp = vb + v_roff[j] + (32 * h + 16 * ks) * ROW_B;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * ROW_B));
+        return __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
+            lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+    };
+    // S^T of one stage: two 32-key halves, chains interleaved
+    auto qk = [&](const char* kb, f32x16& S0, f32x16& S1) {
+        S0 = f32x16(0.0f);
+        S1 = f32x16(0.0f);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const int kbase = kt + 32 * kb;
-            // wave-uniform skip: block outside every row's key range
-            if (!wave_active || kbase >= w_hi || kbase + 32 <= w_lo) continue;
-            f32x16 S = f32x16(0.0f);
-            const uint16_t* kp = &sK[buf][(32 * kb + c) * KPAD + 8 * g];
-#pragma unroll
-            for (int s = 0; s < NS; ++s)
-                S = mfma32(*reinterpret_cast<const bf16x8*>(kp + 16 * s), qreg[s], S);
-            // S[r] = score of key kbase + 8(r/4) + 4g + r%4 for this lane's query
-            const bool full = kbase >= max_start && kbase + 32 <= min_end &&
-                              (!CAUSAL || kbase + 31 <= wr0);
-            if (!full) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kbase + 8 * (r >> 2) + 4 * g + (r & 3);
-                    const bool ok = key >= start_l && key < end_l && (!CAUSAL || key <= row);
-                    S[r] = ok ? S[r] : -INFINITY;
-                }
-            }
-            float mx = S[0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-            mx = lane_pair_max(mx);
-            const float m_new = fmaxf(m_run, mx * sl2);
-            const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-            bf16x2 pk[8];
-            float rs = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(S[2 * i], sl2, -m_use));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(S[2 * i + 1], sl2, -m_use));
-                pk[i] = bf16x2{(__bf16)p0, (__bf16)p1};
-                rs = __builtin_amdgcn_fdot2_f32_bf16(pk[i], ones, rs, false);
-            }
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-                for (int j = 0; j < ND; ++j) acc[j] *= alpha;
-            }
-            l_run = l_run * alpha + rs;
-            m_run = m_new;
-            // O^T[d][q] += V^T[d][key] P^T[key][q], two 16-key steps
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 pb = {pk[4 * ks][0], pk[4 * ks][1], pk[4 * ks + 1][0], pk[4 * ks + 1][1],
-                                   pk[4 * ks + 2][0], pk[4 * ks + 2][1], pk[4 * ks + 3][0], pk[4 * ks + 3][1]};
-                const int col = 32 * kb + 16 * ks + 4 * g;
-#pragma unroll
-                for (int j = 0; j < ND; ++j) {
-                    const uint16_t* vp = &sVt[buf][(32 * j + c) * VPAD + col];
-                    const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
-                    const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 8);
-                    const u32x4 av = {lo.x, lo.y, hi.x, hi.y};
-                    acc[j] = mfma32(__builtin_bit_cast(bf16x8, av), pb, acc[j]);
-                }
-            }
+        for (int s = 0; s < NS; ++s) {
+            S0 = mfma32(kop(kb, 0, s), qreg[s], S0);
+            S1 = mfma32(kop(kb, 1, s), qreg[s], S1);
         }
-        if (st + 1 < nstages) stash(buf ^ 1);
-        __syncthreads();
+    };
+    // O^T += V^T P^T for one stage; P[h][ks] holds the bf16 probabilities of
+    // keys 32h + 16ks + 8(e/4) + 4g + e%4 of this lane's query
+    auto pv = [&](const char* vb, const bf16x8 (&P)[2][2]) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int j = 0; j < ND; ++j) acc[j] = mfma32(vop(vb, h, ks, j), P[h][ks], acc[j]);
+    };
+    // eight bf16 pairs of one 32-key half into the two B operands of P.V
+    auto pack = [&](const bf16x2 (&pk)[8], bf16x8 (&out)[2]) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            out[ks] = bf16x8{pk[4 * ks][0], pk[4 * ks][1], pk[4 * ks + 1][0], pk[4 * ks + 1][1],
+                             pk[4 * ks + 2][0], pk[4 * ks + 2][1], pk[4 * ks + 3][0], pk[4 * ks + 3][1]};
+    };
+    auto prob_pair = [&](const f32x16& S, int i, float m_use) -> bf16x2 {
+        return bf16x2{(__bf16)__builtin_amdgcn_exp2f(fmaf(S[2 * i], sl2, -m_use)),
+                      (__bf16)__builtin_amdgcn_exp2f(fmaf(S[2 * i + 1], sl2, -m_use))};
+    };
+    // stage max in exp2 units, shared by the lane pair
+    auto stage_max = [&](const f32x16& S0, const f32x16& S1) {
+        float mx = fmaxf(S0[0], S1[0]);
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(S0[r], S1[r]));
+        return lane_pair_max(mx) * sl2;
+    };
+    // -inf for keys outside the lane's segment or above its diagonal.  Score
+    // (h, r) belongs to key kt + 4g + C with C = 32h + 8(r/4) + r%4; the
+    // lane's visible keys [start_l, vis_end) become bounds on C per stage.
+    const int vis_end = CAUSAL ? min(end_l, row + 1) : end_l;
+    auto mask = [&](int st, f32x16& S0, f32x16& S1) {
+        const int x0 = k_lo + st * kBN + 4 * g;
+        const int lo = start_l - x0, hi = vis_end - x0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int C = 8 * (r >> 2) + (r & 3);
+            S0[r] = ((C >= lo) & (C < hi)) ? S0[r] : -INFINITY;
+            S1[r] = ((C + 32 >= lo) & (C + 32 < hi)) ? S1[r] : -INFINITY;
+        }
+    };
+    // ordered softmax of one stage: mask, running max (with rescale), probabilities
+    auto softmax_stage = [&](int st, f32x16& S0, f32x16& S1, bf16x8 (&P)[2][2]) {
+        if (!stage_full(st)) mask(st, S0, S1);
+        const float m_st = stage_max(S0, S1);
+        // move the running max only when it would lag by more than the slack;
+        // lanes that keep their max scale by exactly 1 (their m_run may still
+        // be -inf when all their keys so far were masked)
+        const bool grow = m_st > m_run + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_st) : 1.0f;
+#pragma unroll
+            for (int j = 0; j < ND; ++j) acc[j] *= alpha;
+            l_run *= alpha;
+            m_run = grow ? m_st : m_run;
+        }
+        const float m_use = m_run == -INFINITY ? 0.0f : m_run;
+        bf16x2 pk0[8], pk1[8];
+        float rs = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            pk0[i] = prob_pair(S0, i, m_use);
+            pk1[i] = prob_pair(S1, i, m_use);
+            rs = __builtin_amdgcn_fdot2_f32_bf16(pk0[i], ones, rs, false);
+            rs = __builtin_amdgcn_fdot2_f32_bf16(pk1[i], ones, rs, false);
+        }
+        l_run += rs;
+        pack(pk0, P[0]);
+        pack(pk1, P[1]);
+    };
+
+    // ---- stages in order.  K and V each have two LDS buffers: stage st is
+    // computed from buffer st % 2 while stage st+1 streams into the other.  The
+    // loop is unrolled by two so every buffer address is a compile-time offset.
+    {
+        auto seq = [&](int st, auto par) {
+            constexpr int PAR = decltype(par)::value;
+            __builtin_amdgcn_s_waitcnt(0x0F70);          // stage st has landed for this wave
+            __syncthreads();                              // ... and for all; st-1 is consumed
+            if (st + 1 < nstages) {
+                fetch(p.k, kbase + (PAR ^ 1) * TILE_B, k_loff, st + 1);
+                fetch(p.v, vbase + (PAR ^ 1) * TILE_B, v_loff, st + 1);
+            }
+            if (stage_active(st)) {
+                f32x16 S0, S1;
+                bf16x8 P[2][2];
+                qk(kbase + PAR * TILE_B, S0, S1);
+                softmax_stage(st, S0, S1, P);
+                pv(vbase + PAR * TILE_B, P);
+            }
+        };
+        fetch(p.k, kbase, k_loff, 0);
+        fetch(p.v, vbase, v_loff, 0);
+        for (int st = 0; st < nstages; st += 2) {
+            seq(st, std::integral_constant<int, 0>{});
+            if (st + 1 < nstages) seq(st + 1, std::integral_constant<int, 1>{});
+        }
     }
 
     // ---- epilogue: lane (c, g) holds O^T rows d = 32j + 8(r/4) + 4g + r%4
     if (!wave_active || wr0 + c >= r1) return;
-    const float l = l_run + __shfl_xor(l_run, 32, 64);
+    const float l = lane_pair_sum(l_run);
     const float inv = 1.0f / l;
     const int64_t ob = row_off(row);
 #pragma unroll
@@ -478,6 +596,9 @@ pvc_status launch_fwd(const AttnParams& prm, bool causal, bool out_f32, hipStrea
     }
     return launch_status();
 }
+
+// Per-lane staging offsets span one 64-key stage in 32 bits.
+constexpr int64_t kMaxRowElems = (int64_t)1 << 24;
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
@@ -538,6 +659,7 @@ extern "C" pvc_status pvc_varlen_attn_fwd_planned(const void* q, const void* k, 
         overlaps(out, out_bytes, v, in_bytes))
         return PVC_ERR_INVALID_ARG;
     if (L.ntiles * (int64_t)heads > 0x7ffffff0LL) return PVC_ERR_INVALID_ARG;
+    if ((int64_t)heads * head_dim > kMaxRowElems) return PVC_ERR_INVALID_ARG;
     const char* ws = static_cast<const char*>(workspace);
     AttnParams prm{};
     prm.q = static_cast<const uint16_t*>(q);
@@ -593,6 +715,7 @@ extern "C" pvc_status pvc_padded_attn_fwd_sbhd(const void* q, const void* k, con
     if (overlaps(out, out_bytes, q, bytes) || overlaps(out, out_bytes, k, bytes) ||
         overlaps(out, out_bytes, v, bytes))
         return PVC_ERR_INVALID_ARG;
+    if ((int64_t)batch * heads * head_dim > kMaxRowElems) return PVC_ERR_INVALID_ARG;
     const int64_t tiles = (max_len + kBM - 1) / kBM;
     const int64_t items = tiles * batch * heads;
     if (items > 0x7ffffff0LL) return PVC_ERR_INVALID_ARG;
