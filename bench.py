@@ -219,17 +219,26 @@ def cpu_baseline(x, seconds=12.0):
     real_rows = np.nonzero(seg_pad == 0)[0]
     q, k, v = x.host_qkv if x.host_qkv is not None else w.qkv()
     rng = np.random.default_rng(99)
-    # calibrate on a small sample, then size the timed sample to ~`seconds`
-    probe = rng.choice(real_rows, size=min(64, real_rows.size), replace=False)
+    # calibrate on a small sample, then run seeded batches of random rows
+    # until about `seconds` of oracle time has been spent
+    probe = rng.choice(real_rows, size=min(256, real_rows.size), replace=False)
     t0 = time.perf_counter()
     A.attention_rows(q, k, v, cu, probe, True, threads=threads)
-    dt = time.perf_counter() - t0
-    n = int(min(real_rows.size, max(64, 64 * seconds / max(dt, 1e-3))))
-    rows = rng.choice(real_rows, size=n, replace=False)
-    t0 = time.perf_counter()
-    A.attention_rows(q, k, v, cu, rows, True, threads=threads)
-    dt = time.perf_counter() - t0
-    flops = 4.0 * w.head_dim * w.heads * (pos[rows] + 1).sum()
+    rate = probe.size / max(time.perf_counter() - t0, 1e-3)          # rows per second
+    n_rows, flops, dt = 0, 0.0, 0.0
+    for _ in range(4):
+        left = seconds - dt
+        if left <= 0.1 * seconds:
+            break
+        n = int(min(real_rows.size, max(256, rate * left)))
+        rows = rng.choice(real_rows, size=n, replace=False)
+        t0 = time.perf_counter()
+        A.attention_rows(q, k, v, cu, rows, True, threads=threads)
+        t = time.perf_counter() - t0
+        dt += t
+        n_rows += n
+        flops += 4.0 * w.head_dim * w.heads * (pos[rows] + 1).sum()
+        rate = n / max(t, 1e-3)
     model = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -244,7 +253,7 @@ def cpu_baseline(x, seconds=12.0):
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{n} random real query rows x {w.heads} heads of the {w.name} workload, "
+        "sample": f"{n_rows} random real query rows x {w.heads} heads of the {w.name} workload, "
                   f"fp64 attention oracle (C loop, {threads} threads, {dt:.1f} s)",
         "seconds": round(dt, 2),
         "cpu": model,

@@ -9,9 +9,7 @@
 // Plan (two launches, device-side only, no host synchronization):
 //   plan_rows_kernel   every token i gets its segment's key range
 //                      [cu[r], cu[r+1]) by binary search (8 B per token);
-//   plan_sort_kernel   one block validates cu_seqlens, prices every 128-row
-//                      query tile by its key span and orders the tiles
-//                      longest first (counting sort), then seals the header.
+//   plan_check_kernel  one block validates cu_seqlens and seals the header.
 // Query tiles are aligned to the buffer, not to segments: tile w covers rows
 // [128w, 128w+128).  A tile may hold the tail of one segment and the head of
 // the next, or many short segments; every row carries its own key range, so
@@ -41,7 +39,11 @@
 // Grid to hardware: workgroups are dealt round-robin to the 8 XCDs, so the
 // block index is remapped to give each XCD a contiguous range of the
 // (head, tile) space; an XCD then works through a few heads, and the query
-// tiles that share a head's K/V run together on one L2.
+// tiles that share a head's K/V run together on one L2.  Within a head the
+// tiles go from the end of the buffer to its start, so the heaviest tiles of
+// each segment (its last rows see the most keys) are dispatched first.  A
+// global longest-first order was measured slower: it separates the tiles of
+// a segment and loses their K/V reuse in L2.
 #include <math.h>
 
 #include <type_traits>
@@ -53,10 +55,10 @@ namespace {
 
 constexpr int kWaves = 4;       // waves per workgroup, 32 query rows each
 constexpr int kBM = 32 * kWaves; // query rows per tile
-constexpr int kBN = 64;         // keys per LDS stage
+constexpr int kBN = 64;         // keys per LDS stage (32 or 64)
+constexpr int kRing = 2;        // LDS stages per K/V ring; kRing - 1 are in flight
 constexpr int kThreads = 64 * kWaves;
-constexpr int kNumBuckets = 4096;
-constexpr int kSortThreads = 1024;
+constexpr int kCheckThreads = 1024;
 constexpr int kNumXcd = 8;
 constexpr int32_t kPlanMagic = 0x31435650;   // "PVC1"
 
@@ -70,7 +72,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct PlanLayout {
-    size_t header, order, rows, total;
+    size_t header, rows, total;
     int64_t ntiles;
 };
 
@@ -80,8 +82,6 @@ PlanLayout plan_layout(int64_t T) {
     size_t off = 0;
     L.header = off;
     off += align_up(16 * sizeof(int32_t));
-    L.order = off;
-    off += align_up((size_t)L.ntiles * sizeof(int32_t));
     L.rows = off;
     off += align_up((size_t)T * sizeof(int2));
     L.total = off;
@@ -100,38 +100,16 @@ __global__ __launch_bounds__(256) void plan_rows_kernel(const int32_t* __restric
     rows[i] = ok ? make_int2((int)st, (int)en) : make_int2((int)i, (int)(i + 1));
 }
 
-__device__ int block_exclusive_scan_int(int x, int* sh, int& total) {
-    const int t = threadIdx.x;
-    sh[t] = x;
-    __syncthreads();
-    for (int off = 1; off < (int)blockDim.x; off <<= 1) {
-        int y = (t >= off) ? sh[t - off] : 0;
-        __syncthreads();
-        sh[t] += y;
-        __syncthreads();
-    }
-    total = sh[blockDim.x - 1];
-    const int excl = sh[t] - x;
-    __syncthreads();
-    return excl;
-}
-
-__global__ __launch_bounds__(kSortThreads) void plan_sort_kernel(
+__global__ __launch_bounds__(kCheckThreads) void plan_check_kernel(
         const int32_t* __restrict__ cu, int32_t nseg, int64_t T, int32_t max_seqlen, int32_t causal,
-        const int2* __restrict__ rows, int32_t* __restrict__ header, int32_t* __restrict__ order,
-        int32_t ntiles, uint32_t* dev_error) {
-    __shared__ int hist[kNumBuckets];
-    __shared__ int offs[kNumBuckets];
-    __shared__ int scan_sh[kSortThreads];
+        int32_t* __restrict__ header, int32_t ntiles, uint32_t* dev_error) {
     __shared__ unsigned s_err;
     const int t = threadIdx.x;
     if (t == 0) s_err = 0;
-    for (int b = t; b < kNumBuckets; b += kSortThreads) hist[b] = 0;
     __syncthreads();
-
-    // 1. the cu_seqlens contract
+    // the cu_seqlens contract
     uint32_t err = 0;
-    for (int64_t r = t; r < nseg; r += kSortThreads) {
+    for (int64_t r = t; r < nseg; r += kCheckThreads) {
         const int64_t a = cu[r], b = cu[r + 1];
         if (b <= a) err |= PVC_DEV_NOT_INCREASING;
         if (b - a > max_seqlen) err |= PVC_DEV_MAXSEQ;
@@ -141,43 +119,6 @@ __global__ __launch_bounds__(kSortThreads) void plan_sort_kernel(
         if ((int64_t)cu[nseg] != T) err |= PVC_DEV_TOTAL;
     }
     if (err) atomicOr(&s_err, err);
-
-    // 2. price every tile by its key span in 64-key stages
-    auto bucket_of = [&](int w) {
-        const int64_t f = (int64_t)w * kBM;
-        const int64_t l = min<int64_t>(f + kBM, T) - 1;
-        const int64_t lo = rows[f].x;
-        const int64_t hi = causal ? l + 1 : (int64_t)rows[l].y;
-        const int64_t stages = (hi - lo + kBN - 1) / kBN;
-        return (int)min<int64_t>(stages, kNumBuckets - 1);
-    };
-    for (int w = t; w < ntiles; w += kSortThreads) atomicAdd(&hist[bucket_of(w)], 1);
-    __syncthreads();
-
-    // 3. descending exclusive scan: offs[b] = number of tiles in buckets > b
-    constexpr int kPer = kNumBuckets / kSortThreads;
-    int local[kPer];
-    int sum = 0;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-        local[k] = hist[kNumBuckets - 1 - (t * kPer + k)];
-        sum += local[k];
-    }
-    int total = 0;
-    int run = block_exclusive_scan_int(sum, scan_sh, total);
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-        offs[kNumBuckets - 1 - (t * kPer + k)] = run;
-        run += local[k];
-    }
-    for (int b = t; b < kNumBuckets; b += kSortThreads) hist[b] = 0;   // reuse as cursors
-    __syncthreads();
-
-    // 4. scatter (order inside a bucket is arbitrary; results do not depend on it)
-    for (int w = t; w < ntiles; w += kSortThreads) {
-        const int b = bucket_of(w);
-        order[offs[b] + atomicAdd(&hist[b], 1)] = w;
-    }
     __syncthreads();
     if (t == 0) {
         header[HDR_MAGIC] = kPlanMagic;
@@ -199,7 +140,6 @@ struct AttnParams {
     void* out;
     float* lse;
     const int32_t* header;     // THD: plan header
-    const int32_t* order;      // THD: tile order
     const int2* rows;          // THD: per-row key range
     const int32_t* seqlens;    // SBHD: valid length per sample
     int64_t T;                 // THD: total tokens
@@ -210,6 +150,14 @@ struct AttnParams {
     float scale_log2;          // log2(e) / sqrt(d)
     uint32_t* dev_error;
 };
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>)
+template <int N, typename F> __device__ __attribute__((always_inline)) inline void static_for(F&& f) {
+    if constexpr (N > 0) {
+        static_for<N - 1>(f);
+        f(std::integral_constant<int, N - 1>{});
+    }
+}
 
 __device__ inline f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -266,8 +214,10 @@ void attn_fwd_kernel(AttnParams p) {
     static_assert(CPW >= 1 && CPW * kWaves == CHUNKS, "staging split");
     constexpr int ROWS_PER_CHUNK = 1024 / ROW_B;
     constexpr int L16 = ROW_B / 16;          // 16-byte pieces per row
-    __shared__ __attribute__((aligned(1024))) uint16_t sK[2][kBN * D];
-    __shared__ __attribute__((aligned(1024))) uint16_t sV[2][kBN * D];
+    constexpr int NH = kBN / 32;              // 32-key halves per stage
+    static_assert(NH == 1 || NH == 2, "stage size");
+    __shared__ __attribute__((aligned(1024))) uint16_t sK[kRing][kBN * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t sV[kRing][kBN * D];
 
     // ---- which (head, tile): XCD-contiguous remap of the block index
     const int nblk = gridDim.x;
@@ -285,14 +235,12 @@ void attn_fwd_kernel(AttnParams p) {
         r1 = min(r0 + kBM, p.L);
         last_row = p.L - 1;
     } else {
-        if (p.header[HDR_MAGIC] != kPlanMagic || p.header[HDR_T] != (int32_t)p.T ||
-            p.header[HDR_CAUSAL] != (CAUSAL ? 1 : 0) || p.header[HDR_NTILES] != p.ntiles) {
-            if (threadIdx.x == 0) raise_error(p.dev_error, PVC_DEV_PLAN);
-            return;
-        }
-        if (p.header[HDR_VALID] != 1) return;
+        // tiles of a head from the end of the buffer backwards: inside a
+        // segment the later tiles have the longer key ranges, so they start
+        // first, and the workgroups an XCD runs together are neighbours that
+        // share K/V in its L2
         head = logical / p.ntiles;
-        const int tile = min(max(p.order[logical - head * p.ntiles], 0), p.ntiles - 1);
+        const int tile = p.ntiles - 1 - (logical - head * p.ntiles);
         r0 = tile * kBM;
         r1 = (int)min<int64_t>((int64_t)r0 + kBM, p.T);
         last_row = (int)(p.T - 1);
@@ -344,7 +292,6 @@ void attn_fwd_kernel(AttnParams p) {
         k_lo = p.rows[r0].x;
         k_hi = CAUSAL ? r1 : p.rows[r1 - 1].y;
     }
-    const int nstages = (k_hi - k_lo + kBN - 1) / kBN;
 
     // ---- Q^T operand in registers: lane (c, g) holds Q[row][16s + 8g .. +8]
     bf16x8 qreg[NS];
@@ -353,6 +300,20 @@ void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
     }
+    // The plan header is read in one piece beside the row ranges and Q (all
+    // of those loads stay inside their buffers whatever the header holds).
+    // A stale or failed plan turns the tile into no stages and no output, so
+    // no address is ever formed from plan data that was not sealed.
+    bool plan_ok = true;
+    if constexpr (!SBHD) {
+        const int4 h0 = *reinterpret_cast<const int4*>(p.header);
+        const int2 h1 = *reinterpret_cast<const int2*>(p.header + 4);
+        const bool sealed = (h0.x == kPlanMagic) & (h0.y == (int32_t)p.T) & (h0.z == (CAUSAL ? 1 : 0)) &
+                            (h0.w == p.ntiles);
+        plan_ok = sealed & (h1.y == 1);
+        if (!sealed && threadIdx.x == 0) raise_error(p.dev_error, PVC_DEV_PLAN);
+    }
+    const int nstages = plan_ok ? (k_hi - k_lo + kBN - 1) / kBN : 0;
 
     // ---- direct global -> LDS staging.  Wave w writes the 1 KiB chunks
     // w, w + kWaves, w + 2 kWaves, ... of each tile; lane l of a chunk lands
@@ -444,21 +405,20 @@ void attn_fwd_kernel(AttnParams p) {
         return __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
             lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
     };
-    // S^T of one stage: two 32-key halves, chains interleaved
-    auto qk = [&](const char* kb, f32x16& S0, f32x16& S1) {
-        S0 = f32x16(0.0f);
-        S1 = f32x16(0.0f);
+    // S^T of one stage: one 32-key block per half, chains interleaved
+    auto qk = [&](const char* kb, f32x16 (&S)[NH]) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            S0 = mfma32(kop(kb, 0, s), qreg[s], S0);
-            S1 = mfma32(kop(kb, 1, s), qreg[s], S1);
-        }
+        for (int h = 0; h < NH; ++h) S[h] = f32x16(0.0f);
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int h = 0; h < NH; ++h) S[h] = mfma32(kop(kb, h, s), qreg[s], S[h]);
     };
     // O^T += V^T P^T for one stage; P[h][ks] holds the bf16 probabilities of
     // keys 32h + 16ks + 8(e/4) + 4g + e%4 of this lane's query
-    auto pv = [&](const char* vb, const bf16x8 (&P)[2][2]) {
+    auto pv = [&](const char* vb, const bf16x8 (&P)[NH][2]) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < NH; ++h)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -476,30 +436,33 @@ void attn_fwd_kernel(AttnParams p) {
                       (__bf16)__builtin_amdgcn_exp2f(fmaf(S[2 * i + 1], sl2, -m_use))};
     };
     // stage max in exp2 units, shared by the lane pair
-    auto stage_max = [&](const f32x16& S0, const f32x16& S1) {
-        float mx = fmaxf(S0[0], S1[0]);
+    auto stage_max = [&](const f32x16 (&S)[NH]) {
+        float mx = S[0][0];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(S0[r], S1[r]));
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int r = (h == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, S[h][r]);
         return lane_pair_max(mx) * sl2;
     };
     // -inf for keys outside the lane's segment or above its diagonal.  Score
     // (h, r) belongs to key kt + 4g + C with C = 32h + 8(r/4) + r%4; the
     // lane's visible keys [start_l, vis_end) become bounds on C per stage.
     const int vis_end = CAUSAL ? min(end_l, row + 1) : end_l;
-    auto mask = [&](int st, f32x16& S0, f32x16& S1) {
+    auto mask = [&](int st, f32x16 (&S)[NH]) {
         const int x0 = k_lo + st * kBN + 4 * g;
         const int lo = start_l - x0, hi = vis_end - x0;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int C = 8 * (r >> 2) + (r & 3);
-            S0[r] = ((C >= lo) & (C < hi)) ? S0[r] : -INFINITY;
-            S1[r] = ((C + 32 >= lo) & (C + 32 < hi)) ? S1[r] : -INFINITY;
-        }
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int C = 32 * h + 8 * (r >> 2) + (r & 3);
+                S[h][r] = ((C >= lo) & (C < hi)) ? S[h][r] : -INFINITY;
+            }
     };
-    // ordered softmax of one stage: mask, running max (with rescale), probabilities
-    auto softmax_stage = [&](int st, f32x16& S0, f32x16& S1, bf16x8 (&P)[2][2]) {
-        if (!stage_full(st)) mask(st, S0, S1);
-        const float m_st = stage_max(S0, S1);
+    // softmax of one stage: mask, running max (with rescale), probabilities
+    auto softmax_stage = [&](int st, f32x16 (&S)[NH], bf16x8 (&P)[NH][2]) {
+        if (!stage_full(st)) mask(st, S);
+        const float m_st = stage_max(S);
         // move the running max only when it would lag by more than the slack;
         // lanes that keep their max scale by exactly 1 (their m_run may still
         // be -inf when all their keys so far were masked)
@@ -512,50 +475,63 @@ void attn_fwd_kernel(AttnParams p) {
             m_run = grow ? m_st : m_run;
         }
         const float m_use = m_run == -INFINITY ? 0.0f : m_run;
-        bf16x2 pk0[8], pk1[8];
+        bf16x2 pk[NH][8];
         float rs = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            pk0[i] = prob_pair(S0, i, m_use);
-            pk1[i] = prob_pair(S1, i, m_use);
-            rs = __builtin_amdgcn_fdot2_f32_bf16(pk0[i], ones, rs, false);
-            rs = __builtin_amdgcn_fdot2_f32_bf16(pk1[i], ones, rs, false);
-        }
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int h = 0; h < NH; ++h) {
+                pk[h][i] = prob_pair(S[h], i, m_use);
+                rs = __builtin_amdgcn_fdot2_f32_bf16(pk[h][i], ones, rs, false);
+            }
         l_run += rs;
-        pack(pk0, P[0]);
-        pack(pk1, P[1]);
+#pragma unroll
+        for (int h = 0; h < NH; ++h) pack(pk[h], P[h]);
     };
 
-    // ---- stages in order.  K and V each have two LDS buffers: stage st is
-    // computed from buffer st % 2 while stage st+1 streams into the other.  The
-    // loop is unrolled by two so every buffer address is a compile-time offset.
-    {
-        auto seq = [&](int st, auto par) {
-            constexpr int PAR = decltype(par)::value;
-            __builtin_amdgcn_s_waitcnt(0x0F70);          // stage st has landed for this wave
-            __syncthreads();                              // ... and for all; st-1 is consumed
-            if (st + 1 < nstages) {
-                fetch(p.k, kbase + (PAR ^ 1) * TILE_B, k_loff, st + 1);
-                fetch(p.v, vbase + (PAR ^ 1) * TILE_B, v_loff, st + 1);
-            }
+    // ---- stages in order through a ring of kRing K and V buffers: stage st
+    // is computed from buffer st % kRing while stages st+1 .. st+kRing-1 are
+    // in flight.  The loop is unrolled by kRing so every buffer address is a
+    // compile-time offset.
+    constexpr int LPS = 2 * CPW;                  // direct loads per stage and wave
+    static_assert((kRing - 2) * LPS <= 63, "vmcnt range");
+    // s_waitcnt vmcnt(n) for the stages still allowed in flight (expcnt and
+    // lgkmcnt left open; vmcnt is split over bits 3:0 and 15:14)
+    auto wait_stages = [&](int ahead) {
+        static_for<kRing - 1>([&](auto n) {
+            constexpr int v = decltype(n)::value * LPS;
+            if (ahead == decltype(n)::value)
+                __builtin_amdgcn_s_waitcnt(0x0F70 | (v & 15) | ((v >> 4) << 14));
+        });
+    };
+    auto fetch_stage = [&](int stage, int slot) {
+        fetch(p.k, kbase + slot * TILE_B, k_loff, stage);
+        fetch(p.v, vbase + slot * TILE_B, v_loff, stage);
+    };
+    static_for<kRing - 1>([&](auto i) {
+        if (decltype(i)::value < nstages) fetch_stage(decltype(i)::value, decltype(i)::value);
+    });
+    for (int st0 = 0; st0 < nstages; st0 += kRing) {
+        static_for<kRing>([&](auto I) {
+            constexpr int SLOT = decltype(I)::value;
+            const int st = st0 + SLOT;
+            if (st >= nstages) return;
+            // stage st has landed for this wave, then for all; stage st-1 is consumed
+            wait_stages(min(kRing - 2, nstages - 1 - st));
+            __syncthreads();
+            if (st + kRing - 1 < nstages) fetch_stage(st + kRing - 1, (SLOT + kRing - 1) % kRing);
             if (stage_active(st)) {
-                f32x16 S0, S1;
-                bf16x8 P[2][2];
-                qk(kbase + PAR * TILE_B, S0, S1);
-                softmax_stage(st, S0, S1, P);
-                pv(vbase + PAR * TILE_B, P);
+                f32x16 S[NH];
+                bf16x8 P[NH][2];
+                qk(kbase + SLOT * TILE_B, S);
+                softmax_stage(st, S, P);
+                pv(vbase + SLOT * TILE_B, P);
             }
-        };
-        fetch(p.k, kbase, k_loff, 0);
-        fetch(p.v, vbase, v_loff, 0);
-        for (int st = 0; st < nstages; st += 2) {
-            seq(st, std::integral_constant<int, 0>{});
-            if (st + 1 < nstages) seq(st + 1, std::integral_constant<int, 1>{});
-        }
+        });
     }
 
     // ---- epilogue: lane (c, g) holds O^T rows d = 32j + 8(r/4) + 4g + r%4
-    if (!wave_active || wr0 + c >= r1) return;
+    if (!plan_ok || !wave_active || wr0 + c >= r1) return;
     const float l = lane_pair_sum(l_run);
     const float inv = 1.0f / l;
     const int64_t ob = row_off(row);
@@ -628,15 +604,13 @@ extern "C" pvc_status pvc_attn_plan(const int32_t* cu_seqlens, int32_t nseg, int
     if (workspace_bytes < L.total) return PVC_ERR_WORKSPACE;
     char* ws = static_cast<char*>(workspace);
     auto* header = reinterpret_cast<int32_t*>(ws + L.header);
-    auto* order = reinterpret_cast<int32_t*>(ws + L.order);
     auto* rows = reinterpret_cast<int2*>(ws + L.rows);
     hipStream_t s = as_stream(stream);
     const int64_t nblk = (total_tokens + 255) / 256;
     hipLaunchKernelGGL(plan_rows_kernel, dim3((unsigned)nblk), dim3(256), 0, s, cu_seqlens, nseg,
                        total_tokens, rows);
-    hipLaunchKernelGGL(plan_sort_kernel, dim3(1), dim3(kSortThreads), 0, s, cu_seqlens, nseg,
-                       total_tokens, max_seqlen, causal ? 1 : 0, rows, header, order,
-                       (int32_t)L.ntiles, dev_error);
+    hipLaunchKernelGGL(plan_check_kernel, dim3(1), dim3(kCheckThreads), 0, s, cu_seqlens, nseg,
+                       total_tokens, max_seqlen, causal ? 1 : 0, header, (int32_t)L.ntiles, dev_error);
     return launch_status();
 }
 
@@ -668,7 +642,6 @@ extern "C" pvc_status pvc_varlen_attn_fwd_planned(const void* q, const void* k, 
     prm.out = out;
     prm.lse = lse;
     prm.header = reinterpret_cast<const int32_t*>(ws + L.header);
-    prm.order = reinterpret_cast<const int32_t*>(ws + L.order);
     prm.rows = reinterpret_cast<const int2*>(ws + L.rows);
     prm.T = total_tokens;
     prm.H = heads;
