@@ -151,6 +151,23 @@ struct AttnParams {
     uint32_t* dev_error;
 };
 
+typedef __attribute__((address_space(3))) char lds_char;
+
+// One direct global -> LDS load of 16 bytes per lane: lane l's bytes at
+// base + off land at LDS address lds + 16 l.  Written as inline assembly so
+// that the compiler does not track it: with the builtin, it waits for every
+// such load to finish before the next LDS read, even when the read is from
+// another buffer, which serialises the prefetch with the compute.  The caller
+// waits for the loads itself (s_waitcnt vmcnt) before a barrier.  M0 holds
+// the LDS address; no compiled code in this file uses M0.  The LDS pointer
+// itself is an operand, so the compiler sees the buffer written.
+__device__ inline void lds_dma16(const void* base, uint32_t off, lds_char* lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(base), "s"(lds)
+                 : "memory");
+}
+
 // f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>)
 template <int N, typename F> __device__ __attribute__((always_inline)) inline void static_for(F&& f) {
     if constexpr (N > 0) {
@@ -335,20 +352,24 @@ void attn_fwd_kernel(AttnParams p) {
         v_loff = (uint32_t)((fetch_rr * row_stride + vpiece * 8) * 2);
     }
     // one stage of K (or V) into LDS buffer `buf`
-    auto fetch = [&](const uint16_t* src, char* dst, uint32_t loff, int stage) {
+    // Addresses are a uniform base (SGPR pair) plus a 32-bit per-lane offset.
+    // dst is the stage buffer's LDS byte address.
+    auto fetch = [&](const uint16_t* src, lds_char* dst, uint32_t loff, int stage) {
         const int kt = k_lo + stage * kBN;
         const char* base = reinterpret_cast<const char*>(src) + ((int64_t)kt * row_stride + head_off) * 2;
-        const bool ragged = kt + kBN - 1 > last_row;                       // uniform
+        const int64_t chunk_step = (int64_t)CHUNK_ROWS * row_stride * 2;
+        if (kt + kBN - 1 <= last_row) {                                     // uniform
 #pragma unroll
-        for (int i = 0; i < CPW; ++i) {
-            int64_t shift = (int64_t)i * CHUNK_ROWS * row_stride * 2;   // bytes, uniform
-            if (ragged) {
-                // rows past the buffer re-read its last row (masked later)
-                const int over = max(kt + fetch_rr + i * CHUNK_ROWS - last_row, 0);
-                shift -= (int64_t)over * row_stride * 2;
+            for (int i = 0; i < CPW; ++i) lds_dma16(base + i * chunk_step, loff, dst + (wave + kWaves * i) * 1024);
+        } else {
+            // the buffer's last stage: rows past its end re-read its last row
+            // (their scores are masked)
+            const uint32_t piece = loff - (uint32_t)(fetch_rr * row_stride * 2);
+#pragma unroll
+            for (int i = 0; i < CPW; ++i) {
+                const int rr = min(fetch_rr + i * CHUNK_ROWS, last_row - kt);
+                lds_dma16(base, (uint32_t)(rr * row_stride * 2) + piece, dst + (wave + kWaves * i) * 1024);
             }
-            __builtin_amdgcn_global_load_lds(base + shift + loff,
-                                             (lds_void*)(dst + (wave + kWaves * i) * 1024), 16, 0, 0);
         }
     };
 
@@ -504,9 +525,11 @@ void attn_fwd_kernel(AttnParams p) {
                 __builtin_amdgcn_s_waitcnt(0x0F70 | (v & 15) | ((v >> 4) << 14));
         });
     };
+    lds_char* const k_lds = (lds_char*)kbase;
+    lds_char* const v_lds = (lds_char*)vbase;
     auto fetch_stage = [&](int stage, int slot) {
-        fetch(p.k, kbase + slot * TILE_B, k_loff, stage);
-        fetch(p.v, vbase + slot * TILE_B, v_loff, stage);
+        fetch(p.k, k_lds + slot * TILE_B, k_loff, stage);
+        fetch(p.v, v_lds + slot * TILE_B, v_loff, stage);
     };
     static_for<kRing - 1>([&](auto i) {
         if (decltype(i)::value < nstages) fetch_stage(decltype(i)::value, decltype(i)::value);
