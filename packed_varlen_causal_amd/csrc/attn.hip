@@ -554,29 +554,56 @@ void attn_fwd_kernel(AttnParams p) {
     }
 
     // ---- epilogue: lane (c, g) holds O^T rows d = 32j + 8(r/4) + 4g + r%4
-    if (!plan_ok || !wave_active || wr0 + c >= r1) return;
+    if (!plan_ok) return;                                  // uniform: nothing was computed
     const float l = lane_pair_sum(l_run);
     const float inv = 1.0f / l;
-    const int64_t ob = row_off(row);
+    const bool row_ok = wave_active && wr0 + c < r1;
+    if constexpr (OUT_F32) {
+        if (row_ok) {
+            const int64_t ob = row_off(row);
 #pragma unroll
-    for (int j = 0; j < ND; ++j) {
+            for (int j = 0; j < ND; ++j)
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-            const int d0 = 32 * j + 8 * rq + 4 * g;
-            const float o0 = acc[j][4 * rq] * inv, o1 = acc[j][4 * rq + 1] * inv;
-            const float o2 = acc[j][4 * rq + 2] * inv, o3 = acc[j][4 * rq + 3] * inv;
-            if constexpr (OUT_F32) {
-                *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + ob + d0) = f32x4{o0, o1, o2, o3};
-            } else {
-                const bf16x2 a = {(__bf16)o0, (__bf16)o1};
-                const bf16x2 bb = {(__bf16)o2, (__bf16)o3};
-                const u32x2 w = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, bb)};
-                *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p.out) + ob + d0) = w;
+                for (int rq = 0; rq < 4; ++rq) {
+                    const int d0 = 32 * j + 8 * rq + 4 * g;
+                    *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + ob + d0) =
+                            f32x4{acc[j][4 * rq] * inv, acc[j][4 * rq + 1] * inv, acc[j][4 * rq + 2] * inv,
+                                  acc[j][4 * rq + 3] * inv};
+                }
+        }
+    } else {
+        // The bf16 tile goes through LDS so that every store instruction
+        // writes whole rows (16 consecutive lanes x 16 B = one 256-byte row
+        // at d=128) instead of 16-byte pieces of 32 rows.  Each wave uses its
+        // own 32-row slice of the K buffers, free once all waves are past the
+        // last stage; 16-byte chunks are XOR-swizzled by row.
+        constexpr int CPR = ROW_B / 16;                    // 16-byte chunks per row
+        __syncthreads();
+        char* const ob_lds = kbase + wave * 32 * ROW_B;
+#pragma unroll
+        for (int j = 0; j < ND; ++j)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const bf16x2 a = {(__bf16)(acc[j][4 * rq] * inv), (__bf16)(acc[j][4 * rq + 1] * inv)};
+                const bf16x2 bb = {(__bf16)(acc[j][4 * rq + 2] * inv), (__bf16)(acc[j][4 * rq + 3] * inv)};
+                const int chunk = (4 * j + rq) ^ (c & (CPR - 1));
+                *reinterpret_cast<u32x2*>(ob_lds + c * ROW_B + chunk * 16 + g * 8) =
+                        u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, bb)};
+            }
+        if (wave_active) {
+            constexpr int RPI = 64 / CPR;                  // rows per 64-lane store
+#pragma unroll
+            for (int i = 0; i < 32 / RPI; ++i) {
+                const int r = i * RPI + lane / CPR;
+                const int k = lane % CPR;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(ob_lds + r * ROW_B + ((k ^ (r & (CPR - 1))) << 4));
+                if (wr0 + r < r1)
+                    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.out) + row_off(wr0 + r) + k * 8) = v;
             }
         }
     }
     if constexpr (!SBHD) {
-        if (p.lse != nullptr && g == 0)
+        if (p.lse != nullptr && g == 0 && row_ok)
             p.lse[(int64_t)head * p.T + row] = (m_run + __log2f(l)) * 0.69314718055994530942f;
     }
 }
