@@ -310,15 +310,9 @@ void attn_fwd_kernel(AttnParams p) {
         k_hi = CAUSAL ? r1 : p.rows[r1 - 1].y;
     }
 
-    // ---- Q^T operand in registers: lane (c, g) holds Q[row][16s + 8g .. +8]
-    bf16x8 qreg[NS];
-    {
-        const uint16_t* qp = p.q + row_off(row) + 8 * g;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
-    }
-    // The plan header is read in one piece beside the row ranges and Q (all
-    // of those loads stay inside their buffers whatever the header holds).
+    bf16x8 qreg[NS];   // Q^T operand, loaded in the prologue below
+    // The plan header is read in one piece beside the row ranges (all of
+    // those loads stay inside their buffers whatever the header holds).
     // A stale or failed plan turns the tile into no stages and no output, so
     // no address is ever formed from plan data that was not sealed.
     bool plan_ok = true;
@@ -354,23 +348,29 @@ void attn_fwd_kernel(AttnParams p) {
     // one stage of K (or V) into LDS buffer `buf`
     // Addresses are a uniform base (SGPR pair) plus a 32-bit per-lane offset.
     // dst is the stage buffer's LDS byte address.
-    auto fetch = [&](const uint16_t* src, lds_char* dst, uint32_t loff, int stage) {
-        const int kt = k_lo + stage * kBN;
+    auto fetch_rows = [&](const uint16_t* src, lds_char* dst, uint32_t loff, int kt) {
         const char* base = reinterpret_cast<const char*>(src) + ((int64_t)kt * row_stride + head_off) * 2;
         const int64_t chunk_step = (int64_t)CHUNK_ROWS * row_stride * 2;
         if (kt + kBN - 1 <= last_row) {                                     // uniform
 #pragma unroll
             for (int i = 0; i < CPW; ++i) lds_dma16(base + i * chunk_step, loff, dst + (wave + kWaves * i) * 1024);
         } else {
-            // the buffer's last stage: rows past its end re-read its last row
-            // (their scores are masked)
+            // rows past the buffer's end re-read its last row (their scores are
+            // masked); kt itself may lie past the end (the upper half of a Q
+            // tile shorter than 64 rows), so offsets are taken from the first
+            // row that exists and stay non-negative
+            const int base_row = min(kt, last_row);
+            const char* b0 = reinterpret_cast<const char*>(src) + ((int64_t)base_row * row_stride + head_off) * 2;
             const uint32_t piece = loff - (uint32_t)(fetch_rr * row_stride * 2);
 #pragma unroll
             for (int i = 0; i < CPW; ++i) {
-                const int rr = min(fetch_rr + i * CHUNK_ROWS, last_row - kt);
-                lds_dma16(base, (uint32_t)(rr * row_stride * 2) + piece, dst + (wave + kWaves * i) * 1024);
+                const int rr = min(kt + fetch_rr + i * CHUNK_ROWS, last_row) - base_row;   // 0 .. kBN-1
+                lds_dma16(b0, (uint32_t)(rr * row_stride * 2) + piece, dst + (wave + kWaves * i) * 1024);
             }
         }
+    };
+    auto fetch = [&](const uint16_t* src, lds_char* dst, uint32_t loff, int stage) {
+        fetch_rows(src, dst, loff, k_lo + stage * kBN);
     };
 
     // ---- LDS read offsets.  Every swizzle term depends on the lane only, so
@@ -531,9 +531,28 @@ void attn_fwd_kernel(AttnParams p) {
         fetch(p.k, k_lds + slot * TILE_B, k_loff, stage);
         fetch(p.v, v_lds + slot * TILE_B, v_loff, stage);
     };
+    // ---- prologue: the Q tile and the first kRing-1 stages.  Q goes through
+    // the last ring slot (first overwritten by stage kRing-1 after the next
+    // barrier) with the K layout, rows 0..63 in its K buffer and 64..127 in
+    // its V buffer, so every load is a whole 1 KiB run of rows; each wave then
+    // reads its Q^T operand (lane (c, g): Q[row][16s + 8g .. +8]) like a K
+    // operand.
+    static_assert(kBM == 2 * kBN, "Q tile staging");
+    constexpr int QSLOT = kRing - 1;
+    if (nstages > 0) {
+        fetch_rows(p.q, k_lds + QSLOT * TILE_B, k_loff, r0);
+        fetch_rows(p.q, v_lds + QSLOT * TILE_B, k_loff, r0 + kBN);
+    }
     static_for<kRing - 1>([&](auto i) {
         if (decltype(i)::value < nstages) fetch_stage(decltype(i)::value, decltype(i)::value);
     });
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    {
+        const char* qb = (wave < 2 ? kbase : vbase) + QSLOT * TILE_B + (wave & 1) * 32 * ROW_B;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qb + k_roff[s]);
+    }
     for (int st0 = 0; st0 < nstages; st0 += kRing) {
         static_for<kRing>([&](auto I) {
             constexpr int SLOT = decltype(I)::value;
