@@ -55,7 +55,7 @@ namespace {
 
 constexpr int kWaves = 4;       // waves per workgroup, 32 query rows each
 constexpr int kBM = 32 * kWaves; // query rows per tile
-constexpr int kBN = 64;         // keys per LDS stage (32 or 64)
+constexpr int kBN = 32;         // keys per LDS stage (32 or 64)
 constexpr int kRing = 2;        // LDS stages per K/V ring; kRing - 1 are in flight
 constexpr int kThreads = 64 * kWaves;
 constexpr int kCheckThreads = 1024;
@@ -219,7 +219,7 @@ template <int D> __device__ inline int v_swz(int row) {
 constexpr float kRescaleSlack = 8.0f;
 
 template <int D, bool CAUSAL, bool OUT_F32, bool SBHD>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void attn_fwd_kernel(AttnParams p) {
     static_assert(D == 64 || D == 128, "head_dim");
     constexpr int NS = D / 16;               // MFMA k-steps for q.k
@@ -233,8 +233,9 @@ void attn_fwd_kernel(AttnParams p) {
     constexpr int L16 = ROW_B / 16;          // 16-byte pieces per row
     constexpr int NH = kBN / 32;              // 32-key halves per stage
     static_assert(NH == 1 || NH == 2, "stage size");
-    __shared__ __attribute__((aligned(1024))) uint16_t sK[kRing][kBN * D];
-    __shared__ __attribute__((aligned(1024))) uint16_t sV[kRing][kBN * D];
+    // one LDS block: kRing K stages, then kRing V stages (and, after the last
+    // stage, the output tile of every wave)
+    __shared__ __attribute__((aligned(1024))) uint16_t sKV[2 * kRing * kBN * D];
 
     // ---- which (head, tile): XCD-contiguous remap of the block index
     const int nblk = gridDim.x;
@@ -310,7 +311,13 @@ void attn_fwd_kernel(AttnParams p) {
         k_hi = CAUSAL ? r1 : p.rows[r1 - 1].y;
     }
 
-    bf16x8 qreg[NS];   // Q^T operand, loaded in the prologue below
+    // ---- Q^T operand in registers: lane (c, g) holds Q[row][16s + 8g .. +8]
+    bf16x8 qreg[NS];
+    {
+        const uint16_t* qp = p.q + row_off(row) + 8 * g;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+    }
     // The plan header is read in one piece beside the row ranges (all of
     // those loads stay inside their buffers whatever the header holds).
     // A stale or failed plan turns the tile into no stages and no output, so
@@ -411,8 +418,8 @@ void attn_fwd_kernel(AttnParams p) {
         const int kt = k_lo + st * kBN;
         return kt >= max_start && kt + kBN <= min_end && (!CAUSAL || kt + kBN - 1 <= wr0);
     };
-    char* const kbase = reinterpret_cast<char*>(&sK[0][0]);
-    char* const vbase = reinterpret_cast<char*>(&sV[0][0]);
+    char* const kbase = reinterpret_cast<char*>(&sKV[0]);
+    char* const vbase = kbase + kRing * TILE_B;
 
     // K operand: key 32h + c of the stage in buffer kb, k-step s
     auto kop = [&](const char* kb, int h, int s) -> bf16x8 {
@@ -531,28 +538,9 @@ void attn_fwd_kernel(AttnParams p) {
         fetch(p.k, k_lds + slot * TILE_B, k_loff, stage);
         fetch(p.v, v_lds + slot * TILE_B, v_loff, stage);
     };
-    // ---- prologue: the Q tile and the first kRing-1 stages.  Q goes through
-    // the last ring slot (first overwritten by stage kRing-1 after the next
-    // barrier) with the K layout, rows 0..63 in its K buffer and 64..127 in
-    // its V buffer, so every load is a whole 1 KiB run of rows; each wave then
-    // reads its Q^T operand (lane (c, g): Q[row][16s + 8g .. +8]) like a K
-    // operand.
-    static_assert(kBM == 2 * kBN, "Q tile staging");
-    constexpr int QSLOT = kRing - 1;
-    if (nstages > 0) {
-        fetch_rows(p.q, k_lds + QSLOT * TILE_B, k_loff, r0);
-        fetch_rows(p.q, v_lds + QSLOT * TILE_B, k_loff, r0 + kBN);
-    }
     static_for<kRing - 1>([&](auto i) {
         if (decltype(i)::value < nstages) fetch_stage(decltype(i)::value, decltype(i)::value);
     });
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    {
-        const char* qb = (wave < 2 ? kbase : vbase) + QSLOT * TILE_B + (wave & 1) * 32 * ROW_B;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qb + k_roff[s]);
-    }
     for (int st0 = 0; st0 < nstages; st0 += kRing) {
         static_for<kRing>([&](auto I) {
             constexpr int SLOT = decltype(I)::value;
@@ -594,9 +582,10 @@ void attn_fwd_kernel(AttnParams p) {
         // The bf16 tile goes through LDS so that every store instruction
         // writes whole rows (16 consecutive lanes x 16 B = one 256-byte row
         // at d=128) instead of 16-byte pieces of 32 rows.  Each wave uses its
-        // own 32-row slice of the K buffers, free once all waves are past the
-        // last stage; 16-byte chunks are XOR-swizzled by row.
+        // own 32-row slice of the stage buffers, free once all waves are past
+        // the last stage; 16-byte chunks are XOR-swizzled by row.
         constexpr int CPR = ROW_B / 16;                    // 16-byte chunks per row
+        static_assert(kBM * ROW_B <= 2 * kRing * TILE_B, "output tile fits the stage buffers");
         __syncthreads();
         char* const ob_lds = kbase + wave * 32 * ROW_B;
 #pragma unroll
