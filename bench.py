@@ -202,6 +202,96 @@ def padded_baseline(torch, pvc, x, reps=3, max_chunk_bytes=24 << 30):
     }
 
 
+def no_isolation_baseline(torch, pvc, x, window=4096, reps=5):
+    """The same buffer attended causally per whole window, ignoring document
+    boundaries ([opworld] "pitfall one": a 4k window of ten documents wastes
+    about 90% of its causal pairs on cross-document attention)."""
+    T = x.T
+    cu = torch.arange(0, T + 1, window, dtype=torch.int32, device="cuda")
+    if int(cu[-1]) != T:
+        return None
+    ws = torch.empty(pvc.attn_workspace_size(T, cu.numel() - 1), dtype=torch.uint8, device="cuda")
+    plan = pvc.AttnPlan(cu, T, window, True, workspace=ws)
+    out = torch.empty_like(x.q)
+    pvc.varlen_attn_fwd(x.q, x.k, x.v, plan=plan, out=out)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        pvc.varlen_attn_fwd(x.q, x.k, x.v, plan=plan, out=out)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    pairs = (T // window) * window * (window + 1) / 2
+    real = x.w.real_lengths.astype(np.float64)
+    return {"layout": f"THD, causal over whole {window}-token windows (documents not isolated)",
+            "ms": round(ms, 4), "computed_pairs_ratio": round(pairs / (real * (real + 1) / 2).sum(), 2)}
+
+
+def measured_peaks(torch):
+    """What this GPU sustains on plain library work: a device copy (read +
+    write bytes) and a large bf16 GEMM (hipBLASLt through torch)."""
+    n = 1 << 31
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(10):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * n * 10 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    m = 8192
+    x = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    y = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(x, y)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(10):
+        torch.matmul(x, y)
+    b.record()
+    torch.cuda.synchronize()
+    gemm = 2.0 * m ** 3 * 10 / (a.elapsed_time(b) * 1e-3) / 1e12
+    del x, y
+    torch.cuda.empty_cache()
+    return {"copy_gbps": round(copy_gbps, 1), "copy_bytes": 2 * n,
+            "gemm_bf16_tflops": round(gemm, 1), "gemm_shape": [m, m, m]}
+
+
+def pack_build_large(torch, pvc, T=1 << 28, reps=5):
+    """pack_build at 2^28 tokens with the short-segment length recipe
+    (uniform [8, 128]): large enough to be bound by HBM, not by launches."""
+    rng = np.random.default_rng([99, 0])
+    L = rng.integers(8, 129, size=int(T / 68 * 1.05) + 16).astype(np.int64)
+    c = np.cumsum(L)
+    n = int(np.searchsorted(c, T))
+    L = L[: n + 1].copy()
+    L[n] -= int(c[n] - T)
+    if L[n] == 0:
+        L = L[:n]
+    lengths = torch.from_numpy(L.astype(np.int32)).cuda()
+    tokens = torch.randint(3, 32000, (T,), dtype=torch.int32, device="cuda")
+    pvc.pack_build(lengths, tokens)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        pvc.pack_build(lengths, tokens)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    nseg = int(lengths.numel())
+    del lengths, tokens
+    torch.cuda.empty_cache()
+    return {"total_tokens": T, "segments": nseg, "ms": round(ms, 3),
+            "gbps": round(pack_bytes(T, nseg) / (ms * 1e-3) / 1e9, 1)}
+
+
 def cpu_baseline(x, seconds=12.0):
     """The fp64 oracle on a bounded, seeded sample of query rows of the same workload.
 
@@ -355,6 +445,10 @@ def main():
     if not args.no_extras:
         res["padded_sbhd"] = padded_baseline(torch, pvc, x)
         res["padded_sbhd"]["speedup_of_varlen"] = round(res["padded_sbhd"]["ms"] / attn_ms, 2)
+        res["measured_peaks"] = measured_peaks(torch)
+        res["roofline"]["frac_of_measured_copy"] = round(
+            a_bytes / (attn_ms * 1e-3) / 1e9 / res["measured_peaks"]["copy_gbps"], 4)
+        res["pack_build_2^28"] = pack_build_large(torch, pvc)
         others = {}
         for name in ("pretrain", "longctx", "short"):
             if name == x.w.name:
@@ -373,6 +467,14 @@ def main():
                 "rope_gbps": round(rope_bytes(y.T, y.H, y.D) / (float(st[1]) * 1e-3) / 1e9, 1),
                 "effective_tokens_per_s": round(int(y.w.real_lengths.sum()) / (ms_s * 1e-3), 1),
             }
+            pad = padded_baseline(torch, pvc, y)
+            pad["speedup_of_varlen"] = round(pad["ms"] / a_ms, 2)
+            others[name]["padded_sbhd"] = pad
+            if name == "pretrain":
+                ni = no_isolation_baseline(torch, pvc, y)
+                if ni is not None:
+                    ni["slowdown_vs_varlen"] = round(ni["ms"] / a_ms, 2)
+                    others[name]["no_isolation"] = ni
             del y
             torch.cuda.empty_cache()
         res["other_workloads"] = others
