@@ -40,10 +40,10 @@
 // block index is remapped to give each XCD a contiguous range of the
 // (head, tile) space; an XCD then works through a few heads, and the query
 // tiles that share a head's K/V run together on one L2.  Within a head the
-// tiles go from the end of the buffer to its start, so the heaviest tiles of
-// each segment (its last rows see the most keys) are dispatched first.  A
-// global longest-first order was measured slower: it separates the tiles of
-// a segment and loses their K/V reuse in L2.
+// segments go in buffer order and each segment's tiles from its end to its
+// start, so the heaviest tiles of a segment (its last rows see the most keys)
+// are dispatched first.  A global longest-first order was measured slower: it
+// separates the tiles of a segment and loses their K/V reuse in L2.
 #include <math.h>
 
 #include <type_traits>
@@ -253,12 +253,18 @@ void attn_fwd_kernel(AttnParams p) {
         r1 = min(r0 + kBM, p.L);
         last_row = p.L - 1;
     } else {
-        // tiles of a head from the end of the buffer backwards: inside a
-        // segment the later tiles have the longer key ranges, so they start
-        // first, and the workgroups an XCD runs together are neighbours that
-        // share K/V in its L2
+        // Segments in buffer order, and inside each segment its tiles from
+        // last to first: a segment's later tiles have the longer key ranges,
+        // so they start first, and the workgroups an XCD runs together are
+        // neighbours that share K/V in its L2.  The tiles whose first row lies
+        // in segment s are [ceil(start_s / BM), ceil(end_s / BM)); position
+        // pos of that run takes the tile mirrored in it.
         head = logical / p.ntiles;
-        const int tile = p.ntiles - 1 - (logical - head * p.ntiles);
+        const int pos = logical - head * p.ntiles;
+        const int2 sr = p.rows[(int64_t)pos * kBM];          // segment of the first row at pos
+        const int ta = (sr.x + kBM - 1) / kBM;
+        const int tb = min((sr.y + kBM - 1) / kBM, p.ntiles);
+        const int tile = (pos >= ta && pos < tb) ? ta + tb - 1 - pos : pos;
         r0 = tile * kBM;
         r1 = (int)min<int64_t>((int64_t)r0 + kBM, p.T);
         last_row = (int)(p.T - 1);
