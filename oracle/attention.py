@@ -18,6 +18,12 @@ Three forms are provided:
   attention_unpacked  each segment run alone as one ordinary sequence
                    ([m020] "08": packed vs per-sample execution;
                    [charlestar] "change A, not B").
+and the gradients of that definition:
+  attention_bwd    dQ, dK, dV for an upstream dO, per segment and head (the C
+                   loop oracle_attn_bwd_segment; the softmax-Jacobian formulas
+                   are written out in attn_oracle.c).  The pages print no
+                   backward formulas; this is the calculus of their forward
+                   definition, pinned by autograd and finite differences.
 """
 
 from __future__ import annotations
@@ -106,6 +112,11 @@ def attention(q, k, v, cu, causal: bool = True, threads: int = 1):
     return attention_rows(q, k, v, cu, np.arange(T, dtype=np.int64), causal, threads)
 
 
+def _as_f64(x):
+    x = np.asarray(x)
+    return bf16_bits_to_f64(x) if x.dtype == np.uint16 else np.ascontiguousarray(x, np.float64)
+
+
 def allow_matrix(cu, causal: bool = True) -> np.ndarray:
     """bool [T, T]: allow(i, j) from segment ids and positions, element by element."""
     cu = np.asarray(cu, np.int64)
@@ -119,8 +130,10 @@ def allow_matrix(cu, causal: bool = True) -> np.ndarray:
 
 
 def attention_brute(q, k, v, cu, causal: bool = True):
-    """Explicit additive mask: softmax(Q K^T / sqrt(d) + M) V per head, fp64 (tiny T)."""
-    Q, K, V = (bf16_bits_to_f64(x) for x in (q, k, v))
+    """Explicit additive mask: softmax(Q K^T / sqrt(d) + M) V per head, fp64 (tiny T).
+
+    Inputs are bf16 bit patterns (uint16) or floating arrays [T, H, d]."""
+    Q, K, V = (_as_f64(x) for x in (q, k, v))
     T, H, d = Q.shape
     M = np.where(allow_matrix(cu, causal), 0.0, -np.inf)
     out = np.empty((T, H, d))
@@ -144,3 +157,50 @@ def attention_unpacked(q, k, v, cu, causal: bool = True, threads: int = 1):
         outs.append(o)
         lses.append(ls)
     return np.concatenate(outs), np.concatenate(lses)
+
+
+def attention_bwd(q, k, v, dout, cu, causal: bool = True, threads: int = 1, heads=None, segments=None):
+    """fp64 gradients (dq, dk, dv), each [T, H, d], of the attention above for
+    upstream gradient ``dout`` (the C loop ``oracle_attn_bwd_segment`` per
+    segment and head; the formulas are in attn_oracle.c).
+
+    Inputs are bf16 bit patterns (uint16) or floating arrays [T, H, d].
+    ``heads`` / ``segments`` restrict the work to those heads / segment
+    indices (other entries of the outputs stay NaN).
+    """
+    lib = _load()
+    if not hasattr(lib, "_bwd_ready"):
+        p = ctypes.c_void_p
+        lib.oracle_attn_bwd_segment.argtypes = [p, p, p, p, ctypes.c_int64, ctypes.c_int32,
+                                                ctypes.c_int64, ctypes.c_int32, p, p, p, p]
+        lib.oracle_attn_bwd_segment.restype = None
+        lib._bwd_ready = True
+    Q, K, V, G = (_as_f64(x) for x in (q, k, v, dout))
+    T, H, d = Q.shape
+    cu = np.asarray(cu, np.int64)
+    heads = range(H) if heads is None else list(heads)
+    segments = range(cu.shape[0] - 1) if segments is None else list(segments)
+    dq, dk, dv = (np.full((T, H, d), np.nan) for _ in range(3))
+    ld = H * d
+    jobs = [(r, h) for r in segments for h in heads]
+
+    def run(job):
+        r, h = job
+        s, e = int(cu[r]), int(cu[r + 1])
+        n = e - s
+        if n <= 0:
+            return
+        scratch = np.empty(2 * n + d, np.float64)
+        off = (s * H + h) * d * 8            # byte offset of (row s, head h)
+        base = lambda a: ctypes.c_void_p(a.ctypes.data + off)  # noqa: E731
+        lib.oracle_attn_bwd_segment(base(Q), base(K), base(V), base(G), n, d, ld, int(bool(causal)),
+                                    base(dq), base(dk), base(dv), _ptr(scratch))
+
+    threads = max(1, min(int(threads), len(jobs)))
+    if threads == 1:
+        for j in jobs:
+            run(j)
+    else:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(run, jobs))
+    return dq, dk, dv

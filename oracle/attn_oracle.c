@@ -94,3 +94,75 @@ int oracle_attn_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v,
     }
     return 0;
 }
+
+/*
+ * Gradients of the attention above for one segment and one head, fp64.
+ *
+ * For a scalar loss with upstream gradient dO = dL/dO, the chain rule through
+ * o_i = sum_j p_ij v_j and the softmax p_ij = exp(s_ij) / sum_l exp(s_il) over
+ * the allowed keys gives, with s_ij = q_i . k_j / sqrt(d):
+ *   dV_j = sum_i p_ij dO_i
+ *   dP_ij = dO_i . v_j,   D_i = sum_j p_ij dP_ij = dO_i . o_i
+ *   dS_ij = p_ij (dP_ij - D_i)             (softmax Jacobian; masked p_ij = 0)
+ *   dQ_i = sum_j dS_ij k_j / sqrt(d),  dK_j = sum_i dS_ij q_i / sqrt(d).
+ * Masked pairs have p_ij = 0 and contribute nothing; keys of other segments
+ * never enter, so a segment's gradients equal those of the segment alone.
+ *
+ *   q, k, v, dout  the segment's first row of this head; row stride ld
+ *                  elements ([T, H, d] row major: ld = H * d); n rows
+ *   dq, dk, dv     outputs with the same layout, overwritten
+ *   scratch        at least 2 n + d doubles
+ * Every sum runs in index order in double.
+ */
+void oracle_attn_bwd_segment(const double* q, const double* k, const double* v, const double* dout,
+                             int64_t n, int32_t d, int64_t ld, int32_t causal, double* dq,
+                             double* dk, double* dv, double* scratch) {
+    const double inv_sqrt_d = 1.0 / sqrt((double)d);
+    double* p = scratch;          /* p_ij of one query row */
+    double* ds = scratch + n;     /* dS_ij of one query row */
+    double* o = scratch + 2 * n;  /* o_i */
+    for (int64_t j = 0; j < n; ++j)
+        for (int32_t c = 0; c < d; ++c) {
+            dk[j * ld + c] = 0.0;
+            dv[j * ld + c] = 0.0;
+        }
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t j_end = causal ? i + 1 : n;
+        const double* qi = q + i * ld;
+        const double* gi = dout + i * ld;
+        double m = -INFINITY;
+        for (int64_t j = 0; j < j_end; ++j) {
+            double dot = 0.0;
+            for (int32_t c = 0; c < d; ++c) dot += qi[c] * k[j * ld + c];
+            p[j] = dot * inv_sqrt_d;
+            if (p[j] > m) m = p[j];
+        }
+        double denom = 0.0;
+        for (int64_t j = 0; j < j_end; ++j) {
+            p[j] = exp(p[j] - m);
+            denom += p[j];
+        }
+        for (int64_t j = 0; j < j_end; ++j) p[j] /= denom;
+        for (int32_t c = 0; c < d; ++c) o[c] = 0.0;
+        for (int64_t j = 0; j < j_end; ++j)
+            for (int32_t c = 0; c < d; ++c) o[c] += p[j] * v[j * ld + c];
+        double D = 0.0;
+        for (int32_t c = 0; c < d; ++c) D += gi[c] * o[c];
+        for (int64_t j = 0; j < j_end; ++j) {
+            double dp = 0.0;
+            for (int32_t c = 0; c < d; ++c) dp += gi[c] * v[j * ld + c];
+            ds[j] = p[j] * (dp - D);
+        }
+        double* dqi = dq + i * ld;
+        for (int32_t c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < j_end; ++j) acc += ds[j] * k[j * ld + c];
+            dqi[c] = acc * inv_sqrt_d;
+        }
+        for (int64_t j = 0; j < j_end; ++j)
+            for (int32_t c = 0; c < d; ++c) {
+                dk[j * ld + c] += ds[j] * qi[c] * inv_sqrt_d;
+                dv[j * ld + c] += p[j] * gi[c];
+            }
+    }
+}
