@@ -235,6 +235,37 @@ pvc_status pvc_varlen_attn_fwd(const void* q, const void* k, const void* v, void
                                void* stream);
 
 /*
+ * Attention backward with an existing plan (the one the forward used): the
+ * gradients of the forward above for an upstream gradient dout,
+ *   dV = P^T dO,  dS = P o (dO V^T - D),  D_i = dO_i . O_i,
+ *   dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d),
+ * with P the masked softmax of the forward (the calculus of [charlestar]
+ * "EOS is content": the masked-softmax equation; masked pairs have P = 0, so
+ * no gradient crosses a segment boundary).  P is recomputed from q, k and lse.
+ *
+ * q, k, v, out, dout  [total_tokens, heads, head_dim] bf16; out is the forward's
+ *             bf16 output for these q, k, v
+ * lse         [heads, total_tokens] fp32, the forward's log-sum-exp (natural log)
+ * dq, dk, dv  [total_tokens, heads, head_dim], bf16 (grad_dtype PVC_OUT_BF16) or
+ *             fp32 (PVC_OUT_F32, the same schedule before the final rounding);
+ *             must not alias each other, the inputs or the scratch
+ * scratch     device buffer of pvc_attn_bwd_scratch_size bytes (overwritten)
+ * head_dim    64 or 128; 2 * heads * (total_tokens + 95) * 4 bytes must stay
+ *             below 4 GiB (PVC_ERR_INVALID_ARG otherwise)
+ * total_tokens and causal must be those the plan was built with; otherwise
+ * PVC_DEV_PLAN is set and nothing is written.  All pointers 16-byte aligned.
+ * Arithmetic: bf16 MFMA products with fp32 accumulation; P and dS are rounded
+ * to bf16 for their products.  Deterministic: no atomics.
+ */
+size_t pvc_attn_bwd_scratch_size(int64_t total_tokens, int32_t heads);
+pvc_status pvc_varlen_attn_bwd_planned(const void* q, const void* k, const void* v, const void* out,
+                                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                       int64_t total_tokens, int32_t heads, int32_t head_dim,
+                                       int32_t causal, int32_t grad_dtype, const void* workspace,
+                                       size_t workspace_bytes, void* scratch, size_t scratch_bytes,
+                                       uint32_t* dev_error, void* stream);
+
+/*
  * Padded comparison layout, for measurement: the same attention kernel on a
  * padded SBHD buffer [max_len, batch, heads, head_dim] (bf16) in which sample
  * b occupies rows s < seqlens[b].  Every sample is processed over all max_len

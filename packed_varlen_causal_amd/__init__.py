@@ -14,6 +14,7 @@ Entry points (same names as the C ABI without the ``pvc_`` prefix):
   rope_thd_apply        per-segment rotary embedding on q and k
   attn_plan             tile plan for one cu_seqlens (reusable across layers)
   varlen_attn_fwd       block-diagonal (causal) attention over THD q/k/v
+  varlen_attn_bwd       its gradients dq, dk, dv on the same plan
   padded_attn_fwd_sbhd  the same kernel on a padded SBHD buffer (measurement)
 """
 
@@ -26,8 +27,8 @@ import torch
 
 __all__ = [
     "PvcError", "DEV_ERROR_BITS", "lib_path", "pack_build", "validate_cu_seqlens",
-    "rope_thd_apply", "AttnPlan", "attn_plan", "varlen_attn_fwd", "padded_attn_fwd_sbhd",
-    "error_names", "attn_workspace_size",
+    "rope_thd_apply", "AttnPlan", "attn_plan", "varlen_attn_fwd", "varlen_attn_bwd",
+    "padded_attn_fwd_sbhd", "error_names", "attn_workspace_size", "attn_bwd_scratch_size",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -64,6 +65,9 @@ def _load() -> ctypes.CDLL:
         "pvc_varlen_attn_fwd_planned": ([P, P, P, P, P, I64, I32, I32, I32, I32, P, SZ, P, P], I32),
         "pvc_varlen_attn_fwd": ([P, P, P, P, P, P, I32, I64, I32, I32, I32, I32, I32, P, SZ, P, P], I32),
         "pvc_padded_attn_fwd_sbhd": ([P, P, P, P, P, I32, I32, I32, I32, I32, I32, P], I32),
+        "pvc_attn_bwd_scratch_size": ([I64, I32], SZ),
+        "pvc_varlen_attn_bwd_planned": ([P, P, P, P, P, P, P, P, P, I64, I32, I32, I32, I32, P, SZ, P, SZ,
+                                         P, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -278,6 +282,8 @@ def varlen_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         out = torch.empty((T, H, D), dtype=out_dtype, device=q.device)
     else:
         _require(out, "out", out_dtype, 3)
+        if tuple(out.shape) != (T, H, D):
+            raise ValueError("out must be [T, H, d] like q")
     lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if return_lse else None
     st = _lib.pvc_varlen_attn_fwd_planned(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), T, H, D, int(bool(causal)),
@@ -287,6 +293,59 @@ def varlen_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if check:
         _raise_dev(plan.dev_error, "varlen_attn_fwd")
     return (out, lse) if return_lse else out
+
+
+def attn_bwd_scratch_size(total_tokens: int, heads: int) -> int:
+    return int(_lib.pvc_attn_bwd_scratch_size(total_tokens, heads))
+
+
+def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                    dout: torch.Tensor, lse: torch.Tensor, plan: AttnPlan, causal: bool = True,
+                    grad_dtype: torch.dtype = torch.bfloat16, grads=None, scratch: torch.Tensor | None = None,
+                    check: bool = False, stream=None):
+    """Gradients (dq, dk, dv) of varlen_attn_fwd for an upstream gradient ``dout``.
+
+    q, k, v, out, dout bf16 [T, H, d]; lse fp32 [H, T] from the forward
+    (return_lse=True); ``plan`` the forward's plan.  Gradients are bf16, or
+    fp32 with grad_dtype=torch.float32; ``grads`` may pass three output tensors.
+    """
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _require(t, name, torch.bfloat16, 3)
+    if any(t.shape != q.shape for t in (k, v, out, dout)):
+        raise ValueError("q, k, v, out and dout must share the shape [T, H, d]")
+    T, H, D = q.shape
+    _require(lse, "lse", torch.float32, 2)
+    if tuple(lse.shape) != (H, T):
+        raise ValueError("lse must be [H, T]")
+    if grad_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("grad_dtype must be torch.bfloat16 or torch.float32")
+    if plan.total_tokens != T or plan.causal != bool(causal):
+        raise ValueError("plan was built for other total_tokens / causal")
+    if grads is None:
+        grads = tuple(torch.empty((T, H, D), dtype=grad_dtype, device=q.device) for _ in range(3))
+    else:
+        if len(grads) != 3:
+            raise ValueError("grads must be three tensors (dq, dk, dv)")
+        for name, t in zip(("dq", "dk", "dv"), grads):
+            _require(t, name, grad_dtype, 3)
+            if tuple(t.shape) != (T, H, D):
+                raise ValueError(f"{name} must be [T, H, d] like q")
+    nb = attn_bwd_scratch_size(T, H)
+    if scratch is None:
+        scratch = torch.empty(nb, dtype=torch.uint8, device=q.device)
+    else:
+        _require(scratch, "scratch", torch.uint8, 1)
+        if scratch.numel() < nb:
+            raise ValueError(f"scratch must hold {nb} bytes (attn_bwd_scratch_size)")
+    dq, dk, dv = grads
+    st = _lib.pvc_varlen_attn_bwd_planned(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), T, H, D,
+        int(bool(causal)), OUT_F32 if grad_dtype == torch.float32 else OUT_BF16, _ptr(plan.workspace),
+        plan.ws_bytes, _ptr(scratch), scratch.numel(), _ptr(plan.dev_error), _stream(stream))
+    _check(st, "varlen_attn_bwd")
+    if check:
+        _raise_dev(plan.dev_error, "varlen_attn_bwd")
+    return dq, dk, dv
 
 
 def padded_attn_fwd_sbhd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seqlens: torch.Tensor,
@@ -307,6 +366,8 @@ def padded_attn_fwd_sbhd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seql
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
     else:
         _require(out, "out", out_dtype, 4)
+        if out.shape != q.shape:
+            raise ValueError("out must be [L, B, H, d] like q")
     st = _lib.pvc_padded_attn_fwd_sbhd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(seqlens), B, L, H, D,
                                        int(bool(causal)),
                                        OUT_F32 if out_dtype == torch.float32 else OUT_BF16, _stream(stream))

@@ -17,9 +17,9 @@
 //
 // Forward kernel: one 256-thread workgroup (four wave64s) per (head, tile).
 // Wave w owns query rows [128w' + 32w, +32).  Keys stream through LDS in
-// stages of 64: K and V go from global memory straight into LDS (no register
+// stages of 32: K and V go from global memory straight into LDS (no register
 // round trip), double buffered, so stage st+1 is in flight while stage st is
-// computed.  Per 32-key block a wave
+// computed.  Per 32-key stage a wave
 //   S^T = K Q^T      8 (d=128) v_mfma_f32_32x32x16_bf16, K from LDS as the A
 //                    operand, Q^T held in registers as the B operand; each
 //                    lane then owns one query and 16 of the 32 keys
@@ -29,7 +29,7 @@
 //   O^T += V^T P^T   the probabilities, rounded to bf16, are already in the B
 //                    operand layout; the V^T operand comes from row-major V in
 //                    LDS through the transposing LDS read (ds_read_b64_tr_b16)
-// A wave skips every 64-key stage that lies wholly outside its rows' segments
+// A wave skips every 32-key stage that lies wholly outside its rows' segments
 // or above their diagonal, so cross-segment and above-diagonal blocks are never
 // computed.  The running max moves only when a row's new maximum exceeds it by
 // more than 2^8 (in probability), which leaves most stages without a rescale
@@ -48,45 +48,12 @@
 
 #include <type_traits>
 
-#include "pvc_internal.h"
+#include "attn_common.h"
 
 namespace pvc {
 namespace {
 
-constexpr int kWaves = 4;       // waves per workgroup, 32 query rows each
-constexpr int kBM = 32 * kWaves; // query rows per tile
-constexpr int kBN = 32;         // keys per LDS stage (32 or 64)
-constexpr int kRing = 2;        // LDS stages per K/V ring; kRing - 1 are in flight
-constexpr int kThreads = 64 * kWaves;
-constexpr int kCheckThreads = 1024;
-constexpr int kNumXcd = 8;
-constexpr int32_t kPlanMagic = 0x31435650;   // "PVC1"
-
-enum { HDR_MAGIC = 0, HDR_T = 1, HDR_CAUSAL = 2, HDR_NTILES = 3, HDR_ERR = 4, HDR_VALID = 5 };
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-struct PlanLayout {
-    size_t header, rows, total;
-    int64_t ntiles;
-};
-
-PlanLayout plan_layout(int64_t T) {
-    PlanLayout L;
-    L.ntiles = (T + kBM - 1) / kBM;
-    size_t off = 0;
-    L.header = off;
-    off += align_up(16 * sizeof(int32_t));
-    L.rows = off;
-    off += align_up((size_t)T * sizeof(int2));
-    L.total = off;
-    return L;
-}
+using namespace attn;
 
 // ------------------------------------------------------------------ plan
 
@@ -150,69 +117,6 @@ struct AttnParams {
     float scale_log2;          // log2(e) / sqrt(d)
     uint32_t* dev_error;
 };
-
-typedef __attribute__((address_space(3))) char lds_char;
-
-// One direct global -> LDS load of 16 bytes per lane: lane l's bytes at
-// base + off land at LDS address lds + 16 l.  Written as inline assembly so
-// that the compiler does not track it: with the builtin, it waits for every
-// such load to finish before the next LDS read, even when the read is from
-// another buffer, which serialises the prefetch with the compute.  The caller
-// waits for the loads itself (s_waitcnt vmcnt) before a barrier.  M0 holds
-// the LDS address; no compiled code in this file uses M0.  The LDS pointer
-// itself is an operand, so the compiler sees the buffer written.
-__device__ inline void lds_dma16(const void* base, uint32_t off, lds_char* lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :
-                 : "v"(off), "s"(base), "s"(lds)
-                 : "memory");
-}
-
-// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>)
-template <int N, typename F> __device__ __attribute__((always_inline)) inline void static_for(F&& f) {
-    if constexpr (N > 0) {
-        static_for<N - 1>(f);
-        f(std::integral_constant<int, N - 1>{});
-    }
-}
-
-__device__ inline f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// Max over the lane pair (l, l^32): v_permlane32_swap hands each lane its
-// partner's value without a round trip through LDS.
-__device__ inline float lane_pair_max(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ inline float lane_pair_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-// LDS tiles hold 64 keys x D bf16 with no padding, so each 1 KiB written by one
-// direct global->LDS load is contiguous.  Bank conflicts are removed by XOR
-// swizzles on the column chunks instead:
-//   K: 16-byte chunks, chunk ^ fk(row); the MFMA A-operand read (one row per
-//      lane, one 16-byte chunk) then covers distinct banks for any 8 or 16
-//      consecutive rows;
-//   V: 32-byte chunks, chunk ^ fv(row); the transposing read (four rows x one
-//      32-byte chunk per 16 lanes, and the next chunk for the next 16 lanes)
-//      covers distinct banks.
-template <int D> __device__ inline int k_swz(int row) {
-    if constexpr (D == 128) return row & 15;
-    else return (row & 7) ^ ((row >> 3) & 1);
-}
-template <int D> __device__ inline int v_swz(int row) {
-    if constexpr (D == 128) return ((row & 3) << 1) | ((row >> 1) & 1);
-    else return row & 3;
-}
 
 // Threshold (log2 units) by which a row's running max may lag before the
 // accumulator is rescaled: probabilities stay below 2^8.
@@ -369,9 +273,8 @@ void attn_fwd_kernel(AttnParams p) {
             for (int i = 0; i < CPW; ++i) lds_dma16(base + i * chunk_step, loff, dst + (wave + kWaves * i) * 1024);
         } else {
             // rows past the buffer's end re-read its last row (their scores are
-            // masked); kt itself may lie past the end (the upper half of a Q
-            // tile shorter than 64 rows), so offsets are taken from the first
-            // row that exists and stay non-negative
+            // masked); offsets are taken from the first row that exists, so
+            // they stay non-negative even for a stage that starts past the end
             const int base_row = min(kt, last_row);
             const char* b0 = reinterpret_cast<const char*>(src) + ((int64_t)base_row * row_stride + head_off) * 2;
             const uint32_t piece = loff - (uint32_t)(fetch_rr * row_stride * 2);
@@ -637,7 +540,7 @@ pvc_status launch_fwd(const AttnParams& prm, bool causal, bool out_f32, hipStrea
     return launch_status();
 }
 
-// Per-lane staging offsets span one 64-key stage in 32 bits.
+// Per-lane staging offsets span one 32-row stage in 32 bits (32 * 2^24 * 2 B).
 constexpr int64_t kMaxRowElems = (int64_t)1 << 24;
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }

@@ -1,0 +1,748 @@
+// Backward of block-diagonal causal attention over a packed THD buffer, for
+// gfx950.
+//
+// For an upstream gradient dO of O = softmax(Q K^T / sqrt(d) + M) V (the
+// forward of [charlestar] "EOS is content"), with P the masked softmax and
+// s = 1/sqrt(d):
+//   dV = P^T dO,  dP = dO V^T,  D_i = dO_i . O_i,  dS = P o (dP - D),
+//   dQ = s dS K,  dK = s dS^T Q.
+// P is recomputed from Q, K and the forward's log-sum-exp, so nothing of size
+// T x T is stored.  Three launches, all on the forward's plan (per-row key
+// ranges, 128-row tiles, the same XCD-contiguous mapping):
+//   bwd_prep_kernel   D_i = dO_i . O_i and lse_i * log2(e) per (head, row)
+//                     into a padded scratch buffer (HBM-bound);
+//   bwd_dq_kernel     query-major like the forward: a wave holds Q^T and dO^T
+//                     of its 32 rows in registers and streams 32-key stages of
+//                     K and V through LDS; per stage S^T = K Q^T and
+//                     dP^T = V dO^T (MFMA, K and V as A operands),
+//                     dS^T = P^T o (dP^T - D) in registers, and
+//                     dQ^T += K^T dS^T with K^T from the transposing LDS read;
+//   bwd_dkdv_kernel   key-major: a wave holds K^T and V^T of its 32 keys and
+//                     streams 32-query stages of Q, dO, lse and D; per stage
+//                     S = Q K^T and dP = dO V^T (lane = key), P and dS in
+//                     registers, dV^T += dO^T P and dK^T += Q^T dS with Q^T and
+//                     dO^T from the transposing LDS read.
+// Every product rounds its probability operand (P or dS) to bf16 and
+// accumulates in fp32.  No atomics: each output element is written once, so
+// results do not depend on scheduling.  Stages that lie wholly outside a
+// wave's segments or on the wrong side of its diagonal are skipped, exactly as
+// in the forward.
+#include "attn_common.h"
+
+namespace pvc {
+namespace {
+
+using namespace attn;
+
+struct BwdParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* out;
+    const uint16_t* dout;
+    const float* lse;          // [H, T], natural log (the forward's)
+    float* scratch;            // [2][H][Tp]: lse * log2(e), then D
+    void* dq;
+    void* dk;
+    void* dv;
+    const int32_t* header;
+    const int2* rows;
+    int64_t T;
+    int64_t Tp;                // padded row count of the scratch planes
+    int32_t H;
+    int32_t ntiles;
+    int32_t items;
+    float scale_log2;          // log2(e) / sqrt(d)
+    float scale;               // 1 / sqrt(d)
+    uint32_t* dev_error;
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Scratch rows per head: T rounded up to the stage size plus two stages, so
+// every 32-row block a stage reads lies inside the plane.
+inline int64_t scratch_rows(int64_t T) { return (T + kBN - 1) / kBN * kBN + 2 * kBN; }
+
+// ------------------------------------------------------------------- prep
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ out,
+                                                       const uint16_t* __restrict__ dout,
+                                                       const float* __restrict__ lse, float* __restrict__ scratch,
+                                                       int64_t T, int64_t Tp, int32_t H) {
+    constexpr int LPR = D / 8;                     // lanes per (row, head): 16 bytes each
+    constexpr int RPB = 256 / LPR;
+    const int64_t item = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;   // (t, h), h fastest
+    const int part = threadIdx.x % LPR;
+    const int64_t t = item / H;
+    const int h = (int)(item - t * H);
+    float acc = 0.0f;
+    if (t < T) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(out + item * D + part * 8);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(dout + item * D + part * 8);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            acc = fmaf(__uint_as_float(a[w] << 16), __uint_as_float(b[w] << 16), acc);
+            acc = fmaf(__uint_as_float(a[w] & 0xFFFF0000u), __uint_as_float(b[w] & 0xFFFF0000u), acc);
+        }
+    }
+#pragma unroll
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (part == 0 && t < Tp) {
+        scratch[(int64_t)h * Tp + t] = t < T ? lse[(int64_t)h * T + t] * kLog2e : 0.0f;
+        scratch[((int64_t)H + h) * Tp + t] = t < T ? acc : 0.0f;
+    }
+}
+
+// ------------------------------------------------------------- shared pieces
+
+// Block index -> logical (head, tile) item: the forward's XCD-contiguous mapping.
+__device__ inline int xcd_logical() {
+    const int per_xcd = gridDim.x / kNumXcd;
+    return (blockIdx.x % kNumXcd) * per_xcd + blockIdx.x / kNumXcd;
+}
+
+// Plan header check, read in one piece (see the forward).
+__device__ inline bool plan_sealed(const BwdParams& p, bool causal, bool& sealed) {
+    const int4 h0 = *reinterpret_cast<const int4*>(p.header);
+    const int2 h1 = *reinterpret_cast<const int2*>(p.header + 4);
+    sealed = (h0.x == kPlanMagic) & (h0.y == (int32_t)p.T) & (h0.z == (causal ? 1 : 0)) & (h0.w == p.ntiles);
+    return sealed & (h1.y == 1);
+}
+
+// ------------------------------------------------------------------ dQ
+
+template <int D, bool CAUSAL, bool OUT_F32>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_kernel(BwdParams p) {
+    static_assert(D == 64 || D == 128, "head_dim");
+    static_assert(kBN == 32, "one 32-key block per stage");
+    constexpr int NS = D / 16;
+    constexpr int ND = D / 32;
+    constexpr int ROW_B = D * 2;
+    constexpr int TILE_B = kBN * ROW_B;
+    constexpr int CHUNKS = TILE_B / 1024;
+    constexpr int CPW = CHUNKS / kWaves;
+    static_assert(CPW >= 1 && CPW * kWaves == CHUNKS, "staging split");
+    constexpr int ROWS_PER_CHUNK = 1024 / ROW_B;
+    constexpr int L16 = ROW_B / 16;
+    constexpr int CHUNK_ROWS = kWaves * ROWS_PER_CHUNK;
+    static_assert(CHUNK_ROWS % 16 == 0, "swizzle period");
+    __shared__ __attribute__((aligned(1024))) uint16_t sKV[2 * kRing * kBN * D];
+
+    const int logical = xcd_logical();
+    if (logical >= p.items) return;
+    // (head, tile) in the forward's order: segments in buffer order, each
+    // segment's tiles mirrored so its heaviest (last) tile starts first
+    const int head = logical / p.ntiles;
+    const int pos = logical - head * p.ntiles;
+    const int2 sr = p.rows[(int64_t)pos * kBM];
+    const int ta = (sr.x + kBM - 1) / kBM;
+    const int tb = min((sr.y + kBM - 1) / kBM, p.ntiles);
+    const int tile = (pos >= ta && pos < tb) ? ta + tb - 1 - pos : pos;
+    const int r0 = tile * kBM;
+    const int r1 = (int)min<int64_t>((int64_t)r0 + kBM, p.T);
+    const int last_row = (int)(p.T - 1);
+    const int H = p.H;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int c = lane & 31;
+    const int g = lane >> 5;
+    const int wr0 = r0 + 32 * wave;
+    const int wr1 = min(wr0 + 32, r1);
+    const bool wave_active = wr0 < r1;
+    const int row = min(wr0 + c, r1 - 1);
+
+    const int2 mine = p.rows[row];
+    const int start_l = mine.x, end_l = mine.y;
+    const int2 first = p.rows[min(wr0, r1 - 1)];
+    const int2 last = p.rows[max(wr1 - 1, 0)];
+    const int w_lo = first.x;
+    const int w_hi = CAUSAL ? wr1 : last.y;
+    const int max_start = last.x;
+    const int min_end = first.y;
+    const int k_lo = p.rows[r0].x;
+    const int k_hi = CAUSAL ? r1 : p.rows[r1 - 1].y;
+
+    auto row_off = [&](int r) -> int64_t { return ((int64_t)r * H + head) * D; };
+    // Q^T and dO^T B operands: lane (c, g) holds X[row][16s + 8g .. +8]
+    bf16x8 qreg[NS], doreg[NS];
+    {
+        const uint16_t* qp = p.q + row_off(row) + 8 * g;
+        const uint16_t* gp = p.dout + row_off(row) + 8 * g;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+            doreg[s] = *reinterpret_cast<const bf16x8*>(gp + 16 * s);
+        }
+    }
+    const float lse2 = p.scratch[(int64_t)head * p.Tp + row];
+    const float dlt = p.scratch[((int64_t)H + head) * p.Tp + row];
+    bool sealed;
+    const bool plan_ok = plan_sealed(p, CAUSAL, sealed);
+    if (!sealed && tid == 0) raise_error(p.dev_error, PVC_DEV_PLAN);
+    const int nstages = plan_ok ? (k_hi - k_lo + kBN - 1) / kBN : 0;
+
+    // ---- K and V stages, both with the K swizzle (both are read as A
+    // operands row by row; K is also read transposed)
+    const int64_t row_stride = (int64_t)H * D;
+    const int64_t head_off = (int64_t)head * D;
+    const int fetch_rr = wave * ROWS_PER_CHUNK + lane / L16;
+    const uint32_t loff =
+            (uint32_t)((fetch_rr * row_stride + ((lane % L16) ^ k_swz<D>(fetch_rr)) * 8) * 2);
+    char* const kbase = reinterpret_cast<char*>(&sKV[0]);
+    char* const vbase = kbase + kRing * TILE_B;
+    auto fetch_rows = [&](const uint16_t* src, lds_char* dst, int kt) {
+        const char* base = reinterpret_cast<const char*>(src) + ((int64_t)kt * row_stride + head_off) * 2;
+        const int64_t chunk_step = (int64_t)CHUNK_ROWS * row_stride * 2;
+        if (kt + kBN - 1 <= last_row) {
+#pragma unroll
+            for (int i = 0; i < CPW; ++i) lds_dma16(base + i * chunk_step, loff, dst + (wave + kWaves * i) * 1024);
+        } else {
+            // rows past the buffer's end re-read its last row (masked later)
+            const int base_row = min(kt, last_row);
+            const char* b0 = reinterpret_cast<const char*>(src) + ((int64_t)base_row * row_stride + head_off) * 2;
+            const uint32_t piece = loff - (uint32_t)(fetch_rr * row_stride * 2);
+#pragma unroll
+            for (int i = 0; i < CPW; ++i) {
+                const int rr = min(kt + fetch_rr + i * CHUNK_ROWS, last_row) - base_row;
+                lds_dma16(b0, (uint32_t)(rr * row_stride * 2) + piece, dst + (wave + kWaves * i) * 1024);
+            }
+        }
+    };
+    lds_char* const k_lds = (lds_char*)kbase;
+    lds_char* const v_lds = (lds_char*)vbase;
+    auto fetch_stage = [&](int st, int slot) {
+        fetch_rows(p.k, k_lds + slot * TILE_B, k_lo + st * kBN);
+        fetch_rows(p.v, v_lds + slot * TILE_B, k_lo + st * kBN);
+    };
+
+    // ---- LDS read offsets (K swizzle: 16-byte piece ^ k_swz(row))
+    //   row read (A operand): row c, piece 2s + g
+    //   transposing read: rows 16ks + 8hh + 4g + li/4, d = 32j + 16chi + 4(li%4)
+    uint32_t r_off[NS], t_off[ND][2];
+    {
+        const int li = lane & 15;
+        const int chi = (lane >> 4) & 1;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) r_off[s] = c * ROW_B + (((2 * s + g) ^ k_swz<D>(c)) << 4);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int rl = 4 * g + (li >> 2) + 8 * hh;
+#pragma unroll
+            for (int j = 0; j < ND; ++j)
+                t_off[j][hh] = rl * ROW_B + (((4 * j + 2 * chi + ((li & 3) >> 1)) ^ k_swz<D>(rl)) << 4) +
+                               ((li & 1) << 3);
+        }
+    }
+    auto rop = [&](const char* b, int s) { return *reinterpret_cast<const bf16x8*>(b + r_off[s]); };
+    auto top = [&](const char* b, int ks, int j) -> bf16x8 {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + t_off[j][0] + 16 * ks * ROW_B));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + t_off[j][1] + 16 * ks * ROW_B));
+        return __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
+            lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+    };
+
+    f32x16 acc[ND];
+#pragma unroll
+    for (int j = 0; j < ND; ++j) acc[j] = f32x16(0.0f);
+    const float sl2 = p.scale_log2;
+    const int vis_end = CAUSAL ? min(end_l, row + 1) : end_l;
+
+    auto stage_active = [&](int st) -> bool {
+        const int kt = k_lo + st * kBN;
+        return wave_active && kt < w_hi && kt + kBN > w_lo;
+    };
+    auto stage_full = [&](int st) -> bool {
+        const int kt = k_lo + st * kBN;
+        return kt >= max_start && kt + kBN <= min_end && (!CAUSAL || kt + kBN - 1 <= wr0);
+    };
+    auto stage = [&](int st, const char* kb, const char* vb) {
+        f32x16 S = f32x16(0.0f), dP = f32x16(0.0f);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            S = mfma32(rop(kb, s), qreg[s], S);          // S^T = K Q^T
+            dP = mfma32(rop(vb, s), doreg[s], dP);       // dP^T = V dO^T
+        }
+        if (!stage_full(st)) {
+            const int x0 = k_lo + st * kBN + 4 * g;
+            const int lo = start_l - x0, hi = vis_end - x0;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int C = 8 * (r >> 2) + (r & 3);
+                S[r] = ((C >= lo) & (C < hi)) ? S[r] : -INFINITY;
+            }
+        }
+        // dS^T = P^T o (dP^T - D); keys 16ks + 8(e/4) + 4g + e%4 of pack ks
+        bf16x2 pk[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(S[2 * i], sl2, -lse2));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(S[2 * i + 1], sl2, -lse2));
+            pk[i] = bf16x2{(__bf16)(p0 * (dP[2 * i] - dlt)), (__bf16)(p1 * (dP[2 * i + 1] - dlt))};
+        }
+        bf16x8 ds[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            ds[ks] = bf16x8{pk[4 * ks][0], pk[4 * ks][1], pk[4 * ks + 1][0], pk[4 * ks + 1][1],
+                            pk[4 * ks + 2][0], pk[4 * ks + 2][1], pk[4 * ks + 3][0], pk[4 * ks + 3][1]};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int j = 0; j < ND; ++j) acc[j] = mfma32(top(kb, ks, j), ds[ks], acc[j]);   // dQ^T += K^T dS^T
+    };
+
+    static_for<kRing - 1>([&](auto i) {
+        if (decltype(i)::value < nstages) fetch_stage(decltype(i)::value, decltype(i)::value);
+    });
+    for (int st0 = 0; st0 < nstages; st0 += kRing) {
+        static_for<kRing>([&](auto I) {
+            constexpr int SLOT = decltype(I)::value;
+            const int st = st0 + SLOT;
+            if (st >= nstages) return;
+            __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0): stage st has landed
+            __syncthreads();
+            if (st + kRing - 1 < nstages) fetch_stage(st + kRing - 1, (SLOT + kRing - 1) % kRing);
+            if (stage_active(st)) stage(st, kbase + SLOT * TILE_B, vbase + SLOT * TILE_B);
+        });
+    }
+
+    // ---- epilogue: dQ = s (dQ^T)^T; lane (c, g) holds rows d = 32j + 8(r/4) + 4g + r%4
+    if (!plan_ok) return;
+    const float sc = p.scale;
+    const bool row_ok = wave_active && wr0 + c < r1;
+    if constexpr (OUT_F32) {
+        if (row_ok) {
+            float* o = static_cast<float*>(p.dq) + row_off(row);
+#pragma unroll
+            for (int j = 0; j < ND; ++j)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq)
+                    *reinterpret_cast<f32x4*>(o + 32 * j + 8 * rq + 4 * g) =
+                            f32x4{acc[j][4 * rq] * sc, acc[j][4 * rq + 1] * sc, acc[j][4 * rq + 2] * sc,
+                                  acc[j][4 * rq + 3] * sc};
+        }
+    } else {
+        // through LDS for whole-row stores, as in the forward
+        constexpr int CPR = ROW_B / 16;
+        static_assert(kBM * ROW_B <= 2 * kRing * TILE_B, "output tile fits the stage buffers");
+        __syncthreads();
+        char* const ob = kbase + wave * 32 * ROW_B;
+#pragma unroll
+        for (int j = 0; j < ND; ++j)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const bf16x2 a = {(__bf16)(acc[j][4 * rq] * sc), (__bf16)(acc[j][4 * rq + 1] * sc)};
+                const bf16x2 b = {(__bf16)(acc[j][4 * rq + 2] * sc), (__bf16)(acc[j][4 * rq + 3] * sc)};
+                const int chunk = (4 * j + rq) ^ (c & (CPR - 1));
+                *reinterpret_cast<u32x2*>(ob + c * ROW_B + chunk * 16 + g * 8) =
+                        u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+            }
+        if (wave_active) {
+            constexpr int RPI = 64 / CPR;
+#pragma unroll
+            for (int i = 0; i < 32 / RPI; ++i) {
+                const int r = i * RPI + lane / CPR;
+                const int kk = lane % CPR;
+                const u32x4 val = *reinterpret_cast<const u32x4*>(ob + r * ROW_B + ((kk ^ (r & (CPR - 1))) << 4));
+                if (wr0 + r < r1)
+                    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.dq) + row_off(wr0 + r) + kk * 8) = val;
+            }
+        }
+    }
+}
+
+// --------------------------------------------------------------- dK, dV
+
+template <int D, bool CAUSAL, bool OUT_F32>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kernel(BwdParams p) {
+    static_assert(D == 64 || D == 128, "head_dim");
+    static_assert(kBN == 32, "one 32-query block per stage");
+    constexpr int NS = D / 16;
+    constexpr int ND = D / 32;
+    constexpr int ROW_B = D * 2;
+    constexpr int TILE_B = kBN * ROW_B;
+    constexpr int CHUNKS = TILE_B / 1024;
+    constexpr int CPW = CHUNKS / kWaves;
+    static_assert(CPW >= 1 && CPW * kWaves == CHUNKS, "staging split");
+    constexpr int ROWS_PER_CHUNK = 1024 / ROW_B;
+    constexpr int L16 = ROW_B / 16;
+    constexpr int CHUNK_ROWS = kWaves * ROWS_PER_CHUNK;
+    static_assert(CHUNK_ROWS % 16 == 0, "swizzle period");
+    // Q stages, then dO stages; then per stage 32 lse values and 32 D values
+    __shared__ __attribute__((aligned(1024))) uint16_t sQO[2 * kRing * kBN * D];
+    __shared__ __attribute__((aligned(16))) float sLD[kRing][2][kBN];
+
+    const int logical = xcd_logical();
+    if (logical >= p.items) return;
+    // key tiles in buffer order: a segment's first key tiles are seen by all
+    // its later queries, so they are its heaviest and start first
+    const int head = logical / p.ntiles;
+    const int tile = logical - head * p.ntiles;
+    const int r0 = tile * kBM;
+    const int r1 = (int)min<int64_t>((int64_t)r0 + kBM, p.T);
+    const int last_row = (int)(p.T - 1);
+    const int H = p.H;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int c = lane & 31;
+    const int g = lane >> 5;
+    const int kw0 = r0 + 32 * wave;                  // this wave's keys [kw0, kw1)
+    const int kw1 = min(kw0 + 32, r1);
+    const bool wave_active = kw0 < r1;
+    const int key = min(kw0 + c, r1 - 1);
+
+    // queries that may see key j: [lo_j, hi_j) = [causal ? j : start_j, end_j)
+    const int2 mine = p.rows[key];
+    const int lo_j = CAUSAL ? key : mine.x;
+    const int hi_j = mine.y;
+    const int2 first = p.rows[min(kw0, r1 - 1)];
+    const int2 last = p.rows[max(kw1 - 1, 0)];
+    const int w_qlo = CAUSAL ? kw0 : first.x;        // smallest lo_j of the wave
+    const int w_qhi = last.y;                         // largest hi_j
+    const int full_lo = CAUSAL ? kw1 - 1 : last.x;   // largest lo_j
+    const int full_hi = first.y;                      // smallest hi_j
+    // non-causal stages start on a multiple of 4 rows, so each 16-byte piece
+    // of the lse / D planes a stage loads is aligned
+    const int q_lo = CAUSAL ? r0 : (p.rows[r0].x & ~3);
+    const int q_hi = p.rows[r1 - 1].y;
+
+    auto row_off = [&](int r) -> int64_t { return ((int64_t)r * H + head) * D; };
+    // K^T and V^T B operands: lane (c, g) holds X[key][16s + 8g .. +8]
+    bf16x8 kreg[NS], vreg[NS];
+    {
+        const uint16_t* kp = p.k + row_off(key) + 8 * g;
+        const uint16_t* vp = p.v + row_off(key) + 8 * g;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            kreg[s] = *reinterpret_cast<const bf16x8*>(kp + 16 * s);
+            vreg[s] = *reinterpret_cast<const bf16x8*>(vp + 16 * s);
+        }
+    }
+    bool sealed;
+    const bool plan_ok = plan_sealed(p, CAUSAL, sealed);
+    if (!sealed && tid == 0) raise_error(p.dev_error, PVC_DEV_PLAN);
+    const int nstages = plan_ok ? (q_hi - q_lo + kBN - 1) / kBN : 0;
+
+    // ---- Q and dO stages (K swizzle), lse and D blocks (128 bytes each)
+    const int64_t row_stride = (int64_t)H * D;
+    const int64_t head_off = (int64_t)head * D;
+    const int fetch_rr = wave * ROWS_PER_CHUNK + lane / L16;
+    const uint32_t loff =
+            (uint32_t)((fetch_rr * row_stride + ((lane % L16) ^ k_swz<D>(fetch_rr)) * 8) * 2);
+    char* const qbase = reinterpret_cast<char*>(&sQO[0]);
+    char* const obase = qbase + kRing * TILE_B;
+    auto fetch_rows = [&](const uint16_t* src, lds_char* dst, int kt) {
+        const char* base = reinterpret_cast<const char*>(src) + ((int64_t)kt * row_stride + head_off) * 2;
+        const int64_t chunk_step = (int64_t)CHUNK_ROWS * row_stride * 2;
+        if (kt + kBN - 1 <= last_row) {
+#pragma unroll
+            for (int i = 0; i < CPW; ++i) lds_dma16(base + i * chunk_step, loff, dst + (wave + kWaves * i) * 1024);
+        } else {
+            const int base_row = min(kt, last_row);
+            const char* b0 = reinterpret_cast<const char*>(src) + ((int64_t)base_row * row_stride + head_off) * 2;
+            const uint32_t piece = loff - (uint32_t)(fetch_rr * row_stride * 2);
+#pragma unroll
+            for (int i = 0; i < CPW; ++i) {
+                const int rr = min(kt + fetch_rr + i * CHUNK_ROWS, last_row) - base_row;
+                lds_dma16(b0, (uint32_t)(rr * row_stride * 2) + piece, dst + (wave + kWaves * i) * 1024);
+            }
+        }
+    };
+    lds_char* const q_lds = (lds_char*)qbase;
+    lds_char* const o_lds = (lds_char*)obase;
+    lds_char* const ld_lds = (lds_char*)&sLD[0][0][0];
+    // lanes 0..7 of wave 0 load 32 lse values, lanes 8..15 the 32 D values of
+    // the stage: row qt + 4(l % 8) .. +3 of plane l / 8 (the planes are padded
+    // by two stages past T, so the block stays inside them)
+    const char* const sbase = reinterpret_cast<const char*>(p.scratch);
+    auto fetch_stage = [&](int st, int slot) {
+        const int qt = q_lo + st * kBN;
+        fetch_rows(p.q, q_lds + slot * TILE_B, qt);
+        fetch_rows(p.dout, o_lds + slot * TILE_B, qt);
+        if (wave == 0 && lane < 16) {
+            const int64_t plane = (lane < 8 ? (int64_t)head : (int64_t)H + head);
+            const uint32_t off = (uint32_t)((plane * p.Tp + qt + 4 * (lane & 7)) * 4);
+            lds_dma16(sbase, off, ld_lds + slot * (2 * kBN * 4));
+        }
+    };
+
+    uint32_t r_off[NS], t_off[ND][2];
+    {
+        const int li = lane & 15;
+        const int chi = (lane >> 4) & 1;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) r_off[s] = c * ROW_B + (((2 * s + g) ^ k_swz<D>(c)) << 4);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int rl = 4 * g + (li >> 2) + 8 * hh;
+#pragma unroll
+            for (int j = 0; j < ND; ++j)
+                t_off[j][hh] = rl * ROW_B + (((4 * j + 2 * chi + ((li & 3) >> 1)) ^ k_swz<D>(rl)) << 4) +
+                               ((li & 1) << 3);
+        }
+    }
+    auto rop = [&](const char* b, int s) { return *reinterpret_cast<const bf16x8*>(b + r_off[s]); };
+    auto top = [&](const char* b, int ks, int j) -> bf16x8 {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + t_off[j][0] + 16 * ks * ROW_B));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + t_off[j][1] + 16 * ks * ROW_B));
+        return __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
+            lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+    };
+
+    f32x16 accV[ND], accK[ND];
+#pragma unroll
+    for (int j = 0; j < ND; ++j) {
+        accV[j] = f32x16(0.0f);
+        accK[j] = f32x16(0.0f);
+    }
+    const float sl2 = p.scale_log2;
+
+    auto stage_active = [&](int st) -> bool {
+        const int qt = q_lo + st * kBN;
+        return wave_active && qt + kBN > w_qlo && qt < w_qhi;
+    };
+    auto stage_full = [&](int st) -> bool {
+        const int qt = q_lo + st * kBN;
+        return qt >= full_lo && qt + kBN <= full_hi;
+    };
+    auto pack = [&](const bf16x2 (&pk)[8], bf16x8 (&outp)[2]) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            outp[ks] = bf16x8{pk[4 * ks][0], pk[4 * ks][1], pk[4 * ks + 1][0], pk[4 * ks + 1][1],
+                              pk[4 * ks + 2][0], pk[4 * ks + 2][1], pk[4 * ks + 3][0], pk[4 * ks + 3][1]};
+    };
+    auto stage = [&](int st, const char* qb, const char* ob, const float* ld) {
+        // lane = key c; register r = query qt + 8(r/4) + 4g + r%4
+        f32x16 S = f32x16(0.0f), dP = f32x16(0.0f);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            S = mfma32(rop(qb, s), kreg[s], S);          // S = Q K^T
+            dP = mfma32(rop(ob, s), vreg[s], dP);        // dP = dO V^T
+        }
+        if (!stage_full(st)) {
+            const int x0 = q_lo + st * kBN + 4 * g;
+            const int lo = lo_j - x0, hi = hi_j - x0;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int C = 8 * (r >> 2) + (r & 3);
+                S[r] = ((C >= lo) & (C < hi)) ? S[r] : -INFINITY;
+            }
+        }
+        f32x4 l4[4], d4[4];
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq) {
+            l4[kq] = *reinterpret_cast<const f32x4*>(ld + 8 * kq + 4 * g);
+            d4[kq] = *reinterpret_cast<const f32x4*>(ld + kBN + 8 * kq + 4 * g);
+        }
+        bf16x2 pp[8], pd[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r0_ = 2 * i, r1_ = 2 * i + 1;
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(S[r0_], sl2, -l4[r0_ >> 2][r0_ & 3]));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(S[r1_], sl2, -l4[r1_ >> 2][r1_ & 3]));
+            pp[i] = bf16x2{(__bf16)p0, (__bf16)p1};
+            pd[i] = bf16x2{(__bf16)(p0 * (dP[r0_] - d4[r0_ >> 2][r0_ & 3])),
+                           (__bf16)(p1 * (dP[r1_] - d4[r1_ >> 2][r1_ & 3]))};
+        }
+        bf16x8 Pb[2], Db[2];
+        pack(pp, Pb);
+        pack(pd, Db);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int j = 0; j < ND; ++j) {
+                accV[j] = mfma32(top(ob, ks, j), Pb[ks], accV[j]);   // dV^T += dO^T P
+                accK[j] = mfma32(top(qb, ks, j), Db[ks], accK[j]);   // dK^T += Q^T dS
+            }
+    };
+
+    static_for<kRing - 1>([&](auto i) {
+        if (decltype(i)::value < nstages) fetch_stage(decltype(i)::value, decltype(i)::value);
+    });
+    for (int st0 = 0; st0 < nstages; st0 += kRing) {
+        static_for<kRing>([&](auto I) {
+            constexpr int SLOT = decltype(I)::value;
+            const int st = st0 + SLOT;
+            if (st >= nstages) return;
+            __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0): stage st has landed
+            __syncthreads();
+            if (st + kRing - 1 < nstages) fetch_stage(st + kRing - 1, (SLOT + kRing - 1) % kRing);
+            if (stage_active(st))
+                stage(st, qbase + SLOT * TILE_B, obase + SLOT * TILE_B, &sLD[SLOT][0][0]);
+        });
+    }
+
+    // ---- epilogue: lane (c, g) holds rows d = 32j + 8(r/4) + 4g + r%4 of
+    // dV^T and dK^T for key kw0 + c
+    if (!plan_ok) return;
+    const float sc = p.scale;
+    const bool key_ok = wave_active && kw0 + c < kw1;
+    if constexpr (OUT_F32) {
+        if (key_ok) {
+            float* ov = static_cast<float*>(p.dv) + row_off(key);
+            float* ok = static_cast<float*>(p.dk) + row_off(key);
+#pragma unroll
+            for (int j = 0; j < ND; ++j)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    const int d0 = 32 * j + 8 * rq + 4 * g;
+                    *reinterpret_cast<f32x4*>(ov + d0) =
+                            f32x4{accV[j][4 * rq], accV[j][4 * rq + 1], accV[j][4 * rq + 2], accV[j][4 * rq + 3]};
+                    *reinterpret_cast<f32x4*>(ok + d0) =
+                            f32x4{accK[j][4 * rq] * sc, accK[j][4 * rq + 1] * sc, accK[j][4 * rq + 2] * sc,
+                                  accK[j][4 * rq + 3] * sc};
+                }
+        }
+    } else {
+        constexpr int CPR = ROW_B / 16;
+        static_assert(kBM * ROW_B <= 2 * kRing * TILE_B, "output tile fits the stage buffers");
+        char* const ob = qbase + wave * 32 * ROW_B;
+        auto emit = [&](const f32x16 (&acc)[ND], float mul, uint16_t* dst) {
+            __syncthreads();                           // stage buffers (or the last tile) are free
+#pragma unroll
+            for (int j = 0; j < ND; ++j)
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    const bf16x2 a = {(__bf16)(acc[j][4 * rq] * mul), (__bf16)(acc[j][4 * rq + 1] * mul)};
+                    const bf16x2 b = {(__bf16)(acc[j][4 * rq + 2] * mul), (__bf16)(acc[j][4 * rq + 3] * mul)};
+                    const int chunk = (4 * j + rq) ^ (c & (CPR - 1));
+                    *reinterpret_cast<u32x2*>(ob + c * ROW_B + chunk * 16 + g * 8) =
+                            u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+                }
+            if (wave_active) {
+                constexpr int RPI = 64 / CPR;
+#pragma unroll
+                for (int i = 0; i < 32 / RPI; ++i) {
+                    const int r = i * RPI + lane / CPR;
+                    const int kk = lane % CPR;
+                    const u32x4 val =
+                            *reinterpret_cast<const u32x4*>(ob + r * ROW_B + ((kk ^ (r & (CPR - 1))) << 4));
+                    if (kw0 + r < kw1) *reinterpret_cast<u32x4*>(dst + row_off(kw0 + r) + kk * 8) = val;
+                }
+            }
+        };
+        emit(accV, 1.0f, static_cast<uint16_t*>(p.dv));
+        emit(accK, sc, static_cast<uint16_t*>(p.dk));
+    }
+}
+
+// ------------------------------------------------------------------- host
+
+template <int D>
+pvc_status launch_bwd(const BwdParams& prm, bool causal, bool out_f32, hipStream_t s) {
+    {
+        constexpr int RPB = 256 / (D / 8);
+        const int64_t items = prm.Tp * prm.H;
+        const int64_t nblk = (items + RPB - 1) / RPB;
+        hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)nblk), dim3(256), 0, s, prm.out, prm.dout, prm.lse,
+                           prm.scratch, prm.T, prm.Tp, prm.H);
+    }
+    const int64_t grid = ((int64_t)prm.items + kNumXcd - 1) / kNumXcd * kNumXcd;
+    if (grid > 0x7fffffffLL) return PVC_ERR_INVALID_ARG;
+    dim3 g((unsigned)grid), blk(kThreads);
+    if (causal) {
+        if (out_f32) {
+            hipLaunchKernelGGL((bwd_dq_kernel<D, true, true>), g, blk, 0, s, prm);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, true>), g, blk, 0, s, prm);
+        } else {
+            hipLaunchKernelGGL((bwd_dq_kernel<D, true, false>), g, blk, 0, s, prm);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false>), g, blk, 0, s, prm);
+        }
+    } else {
+        if (out_f32) {
+            hipLaunchKernelGGL((bwd_dq_kernel<D, false, true>), g, blk, 0, s, prm);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true>), g, blk, 0, s, prm);
+        } else {
+            hipLaunchKernelGGL((bwd_dq_kernel<D, false, false>), g, blk, 0, s, prm);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, false>), g, blk, 0, s, prm);
+        }
+    }
+    return launch_status();
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+constexpr int64_t kMaxRowElems = (int64_t)1 << 24;
+
+}  // namespace
+}  // namespace pvc
+
+using namespace pvc;
+using namespace pvc::attn;
+
+extern "C" size_t pvc_attn_bwd_scratch_size(int64_t total_tokens, int32_t heads) {
+    if (total_tokens < 1 || total_tokens > 0x7fffffffLL || heads < 1) return 0;
+    return align_up((size_t)2 * heads * scratch_rows(total_tokens) * sizeof(float));
+}
+
+extern "C" pvc_status pvc_varlen_attn_bwd_planned(const void* q, const void* k, const void* v, const void* out,
+                                                  const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                                  int64_t total_tokens, int32_t heads, int32_t head_dim,
+                                                  int32_t causal, int32_t grad_dtype, const void* workspace,
+                                                  size_t workspace_bytes, void* scratch, size_t scratch_bytes,
+                                                  uint32_t* dev_error, void* stream) {
+    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr || lse == nullptr ||
+        dq == nullptr || dk == nullptr || dv == nullptr || workspace == nullptr || scratch == nullptr)
+        return PVC_ERR_NULL;
+    if (total_tokens < 1 || total_tokens > 0x7fffffffLL || heads < 1) return PVC_ERR_INVALID_ARG;
+    if (grad_dtype != PVC_OUT_BF16 && grad_dtype != PVC_OUT_F32) return PVC_ERR_INVALID_ARG;
+    if (head_dim != 64 && head_dim != 128) return PVC_ERR_UNSUPPORTED;
+    const void* in16[] = {q, k, v, out, dout, dq, dk, dv, lse, scratch};
+    for (const void* ptr : in16)
+        if (!aligned16(ptr)) return PVC_ERR_INVALID_ARG;
+    const PlanLayout L = plan_layout(total_tokens);
+    if (workspace_bytes < L.total) return PVC_ERR_WORKSPACE;
+    if (scratch_bytes < pvc_attn_bwd_scratch_size(total_tokens, heads)) return PVC_ERR_WORKSPACE;
+    if ((int64_t)heads * head_dim > kMaxRowElems) return PVC_ERR_INVALID_ARG;
+    if (L.ntiles * (int64_t)heads > 0x7ffffff0LL) return PVC_ERR_INVALID_ARG;
+    // the lse / D blocks are addressed by 32-bit byte offsets into the scratch
+    if ((int64_t)2 * heads * scratch_rows(total_tokens) * 4 >= ((int64_t)1 << 32)) return PVC_ERR_INVALID_ARG;
+    const size_t in_bytes = (size_t)total_tokens * heads * head_dim * 2;
+    const size_t g_bytes = in_bytes * (grad_dtype == PVC_OUT_F32 ? 2 : 1);
+    const void* ins[] = {q, k, v, out, dout};
+    void* outs[] = {dq, dk, dv};
+    for (void* o : outs) {
+        for (const void* i : ins)
+            if (overlaps(o, g_bytes, i, in_bytes)) return PVC_ERR_INVALID_ARG;
+        if (overlaps(o, g_bytes, scratch, scratch_bytes)) return PVC_ERR_INVALID_ARG;
+    }
+    if (overlaps(dq, g_bytes, dk, g_bytes) || overlaps(dq, g_bytes, dv, g_bytes) || overlaps(dk, g_bytes, dv, g_bytes))
+        return PVC_ERR_INVALID_ARG;
+    const char* ws = static_cast<const char*>(workspace);
+    BwdParams prm{};
+    prm.q = static_cast<const uint16_t*>(q);
+    prm.k = static_cast<const uint16_t*>(k);
+    prm.v = static_cast<const uint16_t*>(v);
+    prm.out = static_cast<const uint16_t*>(out);
+    prm.dout = static_cast<const uint16_t*>(dout);
+    prm.lse = lse;
+    prm.scratch = static_cast<float*>(scratch);
+    prm.dq = dq;
+    prm.dk = dk;
+    prm.dv = dv;
+    prm.header = reinterpret_cast<const int32_t*>(ws + L.header);
+    prm.rows = reinterpret_cast<const int2*>(ws + L.rows);
+    prm.T = total_tokens;
+    prm.Tp = scratch_rows(total_tokens);
+    prm.H = heads;
+    prm.ntiles = (int32_t)L.ntiles;
+    prm.items = (int32_t)(L.ntiles * heads);
+    prm.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
+    prm.scale = (float)(1.0 / sqrt((double)head_dim));
+    prm.dev_error = dev_error;
+    hipStream_t s = as_stream(stream);
+    const bool f32 = grad_dtype == PVC_OUT_F32;
+    if (head_dim == 128) return launch_bwd<128>(prm, causal != 0, f32, s);
+    return launch_bwd<64>(prm, causal != 0, f32, s);
+}

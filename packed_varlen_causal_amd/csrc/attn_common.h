@@ -1,0 +1,114 @@
+// Shared pieces of the attention kernels (forward and backward) for gfx950:
+// tile geometry, the plan layout, MFMA and lane helpers, the untracked
+// global -> LDS load, and the LDS swizzles.
+#pragma once
+
+#include <math.h>
+
+#include <type_traits>
+
+#include "pvc_internal.h"
+
+namespace pvc {
+namespace attn {
+
+constexpr int kWaves = 4;       // waves per workgroup, 32 query rows each
+constexpr int kBM = 32 * kWaves; // query rows per tile
+constexpr int kBN = 32;         // keys per LDS stage (32 or 64)
+constexpr int kRing = 2;        // LDS stages per K/V ring; kRing - 1 are in flight
+constexpr int kThreads = 64 * kWaves;
+constexpr int kCheckThreads = 1024;
+constexpr int kNumXcd = 8;
+constexpr int32_t kPlanMagic = 0x31435650;   // "PVC1"
+
+enum { HDR_MAGIC = 0, HDR_T = 1, HDR_CAUSAL = 2, HDR_NTILES = 3, HDR_ERR = 4, HDR_VALID = 5 };
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct PlanLayout {
+    size_t header, rows, total;
+    int64_t ntiles;
+};
+
+inline PlanLayout plan_layout(int64_t T) {
+    PlanLayout L;
+    L.ntiles = (T + kBM - 1) / kBM;
+    size_t off = 0;
+    L.header = off;
+    off += align_up(16 * sizeof(int32_t));
+    L.rows = off;
+    off += align_up((size_t)T * sizeof(int2));
+    L.total = off;
+    return L;
+}
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+// One direct global -> LDS load of 16 bytes per lane: lane l's bytes at
+// base + off land at LDS address lds + 16 l.  Written as inline assembly so
+// that the compiler does not track it: with the builtin, it waits for every
+// such load to finish before the next LDS read, even when the read is from
+// another buffer, which serialises the prefetch with the compute.  The caller
+// waits for the loads itself (s_waitcnt vmcnt) before a barrier.  M0 holds
+// the LDS address; no compiled code in this file uses M0.  The LDS pointer
+// itself is an operand, so the compiler sees the buffer written.
+__device__ inline void lds_dma16(const void* base, uint32_t off, lds_char* lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(off), "s"(base), "s"(lds)
+                 : "memory");
+}
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>)
+template <int N, typename F> __device__ __attribute__((always_inline)) inline void static_for(F&& f) {
+    if constexpr (N > 0) {
+        static_for<N - 1>(f);
+        f(std::integral_constant<int, N - 1>{});
+    }
+}
+
+__device__ inline f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Max over the lane pair (l, l^32): v_permlane32_swap hands each lane its
+// partner's value without a round trip through LDS.
+__device__ inline float lane_pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ inline float lane_pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS tiles hold 64 keys x D bf16 with no padding, so each 1 KiB written by one
+// direct global->LDS load is contiguous.  Bank conflicts are removed by XOR
+// swizzles on the column chunks instead:
+//   K: 16-byte chunks, chunk ^ fk(row); the MFMA A-operand read (one row per
+//      lane, one 16-byte chunk) then covers distinct banks for any 8 or 16
+//      consecutive rows;
+//   V: 32-byte chunks, chunk ^ fv(row); the transposing read (four rows x one
+//      32-byte chunk per 16 lanes, and the next chunk for the next 16 lanes)
+//      covers distinct banks.
+template <int D> __device__ inline int k_swz(int row) {
+    if constexpr (D == 128) return row & 15;
+    else return (row & 7) ^ ((row >> 3) & 1);
+}
+template <int D> __device__ inline int v_swz(int row) {
+    if constexpr (D == 128) return ((row & 3) << 1) | ((row >> 1) & 1);
+    else return row & 3;
+}
+
+}  // namespace attn
+}  // namespace pvc

@@ -66,3 +66,92 @@ def three_part_check(out_f32: torch.Tensor, out_bf16: torch.Tensor, ref: np.ndar
     assert rep["max_abs_f32"] <= atol, rep
     assert mism == 0, rep
     return rep
+
+
+# ------------------------------------------------------------ gradients
+
+U_BF16 = 2.0 ** -8          # unit roundoff of bf16 (8 significand bits)
+U_F32 = 2.0 ** -24
+TAU = 2.0 ** -126           # smallest normal fp32: values below it are flushed
+
+
+def grad_error_bounds(q, k, v, dout, cu, causal=True, heads=None, segments=None):
+    """Elementwise first-order bounds on the backward kernels' fp32 gradient error.
+
+    The kernels take the forward's bf16 output O and its fp32 log-sum-exp,
+    recompute P in fp32, round P (for dV) and dS = P o (dP - D) (for dQ, dK)
+    to bf16, and accumulate in fp32.  With u the bf16 unit roundoff,
+    e = 2u + (n + d) 2^-24 per product term (one rounding of the operand, the
+    log-sum-exp's relative error from summing bf16 probabilities, fp32 sums),
+    W = P |V| (an upper bound of |O| and of the forward's PV error scale) and
+    dD_i = 3u sum_d |dO_id| W_id (bf16 O and the forward's own rounding):
+      |d dV_jd| <= e sum_i P_ij |dO_id|
+      |d dQ_id| <= s sum_j (e |dS_ij| + P_ij dD_i) |K_jd|
+      |d dK_jd| <= s sum_i (e |dS_ij| + P_ij dD_i) |Q_id|
+    P and dS here are fp64 values computed from the same bf16 inputs; second
+    order terms are dropped.  fp32 values below 2^-126 are flushed to zero by
+    the hardware (exp2, the bf16 conversions, MFMA), so every probability and
+    every dS term also carries an absolute error tau = 2^-126 (times
+    1 + |dP - D| for dS), and every sum n tau; with M the visibility mask:
+      |d dV_jd| += tau sum_i M_ij |dO_id| + n tau
+      |d dQ_id|, |d dK_jd| += s sum tau (1 + |dP_ij - D_i|) M_ij |K_jd| (|Q_id|) + n tau
+    Entries outside ``heads`` / ``segments`` are NaN.
+    """
+    Q, K, V, G = (bf16_bits_to_f64(x) for x in (q, k, v, dout))
+    T, H, d = Q.shape
+    s = 1.0 / np.sqrt(d)
+    cu = np.asarray(cu, np.int64)
+    heads = range(H) if heads is None else list(heads)
+    segments = range(cu.shape[0] - 1) if segments is None else list(segments)
+    bq, bk, bv = (np.full((T, H, d), np.nan) for _ in range(3))
+    for r in segments:
+        a, b = int(cu[r]), int(cu[r + 1])
+        n = b - a
+        e = 2 * U_BF16 + (n + d) * U_F32
+        for h in heads:
+            q_, k_, v_, g_ = Q[a:b, h], K[a:b, h], V[a:b, h], G[a:b, h]
+            S = s * (q_ @ k_.T)
+            M = np.tril(np.ones((n, n))) if causal else np.ones((n, n))
+            S[M == 0] = -np.inf
+            S -= S.max(axis=1, keepdims=True)
+            P = np.exp(S)
+            P /= P.sum(axis=1, keepdims=True)
+            O = P @ v_
+            W = P @ np.abs(v_)
+            dPD = g_ @ v_.T - (g_ * O).sum(axis=1)[:, None]
+            dS = P * dPD
+            dD = 3 * U_BF16 * (np.abs(g_) * W).sum(axis=1)
+            E = e * np.abs(dS) + P * dD[:, None] + TAU * (1 + np.abs(dPD)) * M
+            bv[a:b, h] = (e * P + TAU * M).T @ np.abs(g_) + n * TAU
+            bq[a:b, h] = s * (E @ np.abs(k_)) + n * TAU
+            bk[a:b, h] = s * (E.T @ np.abs(q_)) + n * TAU
+    return bq, bk, bv
+
+
+def grad_check(got_f32, got_bf16, refs, bounds, rows=None) -> dict:
+    """fp32 gradients within their elementwise bounds of the fp64 oracle (where
+    the oracle was evaluated), and bf16 gradients equal to the RNE rounding of
+    the fp32 ones bit for bit."""
+    rep = {}
+    idx = None if rows is None else torch.as_tensor(np.asarray(rows, np.int64), device=got_f32[0].device)
+    for name, f, b16, ref, bnd in zip(("dq", "dk", "dv"), got_f32, got_bf16, refs, bounds):
+        if idx is not None:       # select on the device: full-size gradients stay there
+            f, b16, ref, bnd = f[idx], b16[idx], ref[rows], bnd[rows]
+        f = f.detach().cpu().numpy().astype(np.float64)
+        bits = host_bits(b16)
+        assert np.isfinite(f).all(), f"non-finite {name}"
+        sel = np.isfinite(ref)
+        err = np.abs(f - ref)[sel]
+        lim = bnd[sel]
+        rne = host_bits(torch.from_numpy(f.astype(np.float32)).to(torch.bfloat16))
+        rep[name] = {
+            "max_abs_err": float(err.max()),
+            "max_err_over_bound": float((err / np.maximum(lim, 1e-300)).max()),
+            "max_abs_ref": float(np.abs(ref[sel]).max()),
+            "bf16_vs_rne_mismatches": int((rne != bits).sum()),
+        }
+    say("    grad parity", rep)
+    for name, r in rep.items():
+        assert r["max_err_over_bound"] <= 1.0, (name, r)
+        assert r["bf16_vs_rne_mismatches"] == 0, (name, r)
+    return rep

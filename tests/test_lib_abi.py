@@ -24,8 +24,14 @@ def declared_functions():
 def lib():
     path = os.path.join(ROOT, "packed_varlen_causal_amd", "libpvc.so")
     if not os.path.exists(path):
-        from packed_varlen_causal_amd.build import build
-        build()
+        # build.py by path: importing the package would try to load the library
+        import importlib.util
+
+        spec = importlib.util.spec_from_file_location(
+            "pvc_build", os.path.join(ROOT, "packed_varlen_causal_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
     return ctypes.CDLL(path)
 
 
@@ -33,7 +39,8 @@ def test_header_declares_the_hot_path():
     names = declared_functions()
     for must in ("pvc_pack_build", "pvc_validate_cu_seqlens", "pvc_rope_thd_apply", "pvc_attn_plan",
                  "pvc_varlen_attn_fwd", "pvc_varlen_attn_fwd_planned", "pvc_padded_attn_fwd_sbhd",
-                 "pvc_attn_workspace_size", "pvc_pack_build_workspace_size", "pvc_status_string"):
+                 "pvc_attn_workspace_size", "pvc_pack_build_workspace_size", "pvc_status_string",
+                 "pvc_varlen_attn_bwd_planned", "pvc_attn_bwd_scratch_size"):
         assert must in names
 
 
@@ -140,6 +147,31 @@ def test_null_and_range_checks_return_before_gpu_work(lib):
     assert lib.pvc_padded_attn_fwd_sbhd(a, b, c, o, fake, 0, 4, 2, 64, 1, 0, None) == 2
     assert lib.pvc_padded_attn_fwd_sbhd(a, b, c, o, fake, 2, 4, 2, 64, 1, 5, None) == 2
     assert lib.pvc_padded_attn_fwd_sbhd(a, b, c, o, fake, 2, 4, 2, 80, 1, 0, None) == 3
+
+    lib.pvc_attn_bwd_scratch_size.restype = SZ
+    lib.pvc_attn_bwd_scratch_size.argtypes = [I64, I32]
+    assert lib.pvc_attn_bwd_scratch_size(0, 2) == 0
+    # two fp32 rows per head, padded to 32 tokens plus one block of 64
+    assert lib.pvc_attn_bwd_scratch_size(9, 2) >= 2 * 2 * (32 + 64) * 4
+    lib.pvc_varlen_attn_bwd_planned.restype = I32
+    lib.pvc_varlen_attn_bwd_planned.argtypes = [P] * 9 + [I64, I32, I32, I32, I32, P, SZ, P, SZ, P, P]
+    g = [_vp(0x100000 * (i + 1)) for i in range(10)]   # q k v out dout lse dq dk dv scratch
+    big = 1 << 20
+
+    def bwd(*, ptrs=None, T=9, H=2, D=64, causal=1, gd=0, ws=big, sc=big):
+        p = list(g if ptrs is None else ptrs)
+        return lib.pvc_varlen_attn_bwd_planned(*p[:9], T, H, D, causal, gd, fake, ws, p[9], sc, None, None)
+
+    assert bwd(ptrs=[None] + g[1:]) == 1
+    assert bwd(ptrs=g[:9] + [None]) == 1
+    assert bwd(D=96) == 3
+    assert bwd(gd=5) == 2
+    assert bwd(T=0) == 2
+    assert bwd(ws=8) == 4
+    assert bwd(sc=8) == 4
+    assert bwd(ptrs=g[:6] + [_vp(0x100008)] + g[7:]) == 2      # misaligned dq
+    assert bwd(ptrs=g[:7] + [g[6]] + g[8:]) == 2               # dk aliasing dq
+    assert bwd(ptrs=g[:8] + [g[0]] + g[9:]) == 2               # dv aliasing q
 
 
 def test_python_binding_imports_without_gpu():

@@ -8,7 +8,8 @@ Page tags used in citations (the pages are the specification):
   [charlestar] charlestar.github.io  "sequence packing and variable-length attention"
 
 Every random draw comes from ``numpy.random.default_rng([cfg_id, stream, seed])``
-(PCG64).  Streams: 0 = sample lengths, 1 = token ids, 2/3/4 = q/k/v.  q/k/v are
+(PCG64).  Streams: 0 = sample lengths, 1 = token ids, 2/3/4 = q/k/v, 5 = an upstream
+gradient of the attention output.  q/k/v are
 standard normal float32 values rounded to bf16 (round to nearest even) and are
 carried as uint16 bit patterns, shape ``[T, H, d]`` (THD, no batch dim).
 
@@ -277,8 +278,9 @@ def token_ids(w: Workload) -> np.ndarray:
 
 
 def qkv_bits(w: Workload, which: str, chunk: int = 1 << 24) -> np.ndarray:
-    """uint16 [T, H, d] bf16 bit patterns of N(0,1) draws for ``which`` in 'q','k','v'."""
-    stream = {"q": 2, "k": 3, "v": 4}[which]
+    """uint16 [T, H, d] bf16 bit patterns of N(0,1) draws for ``which`` in
+    'q', 'k', 'v' or 'g' (an upstream gradient for the attention output)."""
+    stream = {"q": 2, "k": 3, "v": 4, "g": 5}[which]
     rng = _rng(w.cfg_id, stream, w.seed)
     n = w.total_tokens * w.heads * w.head_dim
     out = np.empty(n, np.uint16)
