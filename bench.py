@@ -10,8 +10,10 @@ Printed: ONE JSON line.  value = useful attention TFLOP/s over the whole step
 (useful FLOPs = 4 d H per same-segment causal pair of the real samples; pad
 segments are computed but not counted).  Per-kernel durations come from HIP
 events recorded on the stream the kernels run on.  Beside it, in the same
-process: the same kernel on the padded SBHD layout, the other workloads'
-attention rates, and the fp64 CPU oracle timed on a bounded sample of rows.
+process: the backward (varlen_attn_bwd, not part of the step: useful FLOPs
+2.5x the forward's), the same kernel on the padded SBHD layout, the other
+workloads' attention rates, and the fp64 CPU oracle timed on a bounded sample
+of rows.
 """
 
 from __future__ import annotations
@@ -31,6 +33,10 @@ sys.path.insert(0, ROOT)
 METRIC = "varlen causal attn fwd useful TFLOP/s (% bf16 MFMA peak) + effective tokens/s"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+# useful backward FLOPs per useful forward FLOP: five products of the forward's
+# size (S = QK^T again, dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q)
+# against the forward's two
+BWD_FLOP_RATIO = 2.5
 
 
 def useful_flops(lengths, is_pad, heads, head_dim, causal=True) -> float:
@@ -154,6 +160,39 @@ def time_attn_only(torch, pvc, x, steps, warmup):
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / steps
+
+
+def time_backward(torch, pvc, x, steps, warmup):
+    """varlen_attn_bwd (prep + dQ + dK/dV launches) on the step's rotated q, k,
+    the forward's output and log-sum-exp, and a seeded N(0, 1) upstream
+    gradient; bf16 gradients.  Returns ms per backward call."""
+    meta = pvc.pack_build(x.lengths, x.tokens, x.is_pad, dev_error=x.err)
+    pvc.rope_thd_apply(x.q, x.k, meta["cu_seqlens"], x.w.rope_base, q_out=x.q_rot, k_out=x.k_rot)
+    plan = pvc.AttnPlan(meta["cu_seqlens"], x.T, x.max_seqlen, x.w.causal, dev_error=x.err, workspace=x.ws)
+    out, lse = pvc.varlen_attn_fwd(x.q_rot, x.k_rot, x.v, plan=plan, return_lse=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    dout = torch.randn(x.q.shape, generator=gen, device="cuda", dtype=torch.bfloat16)
+    grads = tuple(torch.empty_like(x.q) for _ in range(3))
+    scratch = torch.empty(pvc.attn_bwd_scratch_size(x.T, x.H), dtype=torch.uint8, device="cuda")
+    call = lambda: pvc.varlen_attn_bwd(x.q_rot, x.k_rot, x.v, out, dout, lse, plan,  # noqa: E731
+                                       grads=grads, scratch=scratch)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    if int(x.err.item()) != 0:
+        raise RuntimeError(f"device error bits {pvc.error_names(int(x.err.item()))}")
+    ms = a.elapsed_time(b) / steps
+    del out, lse, dout, grads, scratch
+    bflops = BWD_FLOP_RATIO * x.flops
+    return {"ms": round(ms, 4), "useful_tflops": round(bflops / (ms * 1e-3) / 1e12, 2),
+            "pct_bf16_peak": round(100 * bflops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
 
 
 def padded_baseline(torch, pvc, x, reps=3, max_chunk_bytes=24 << 30):
@@ -441,6 +480,7 @@ def main():
         },
     }
     torch.cuda.synchronize()
+    res["kernels"]["varlen_attn_bwd"] = time_backward(torch, pvc, x, max(3, args.steps // 2), 2)
 
     if not args.no_extras:
         res["padded_sbhd"] = padded_baseline(torch, pvc, x)
@@ -467,6 +507,7 @@ def main():
                 "rope_gbps": round(rope_bytes(y.T, y.H, y.D) / (float(st[1]) * 1e-3) / 1e9, 1),
                 "effective_tokens_per_s": round(int(y.w.real_lengths.sum()) / (ms_s * 1e-3), 1),
             }
+            others[name]["backward"] = time_backward(torch, pvc, y, max(3, args.steps // 2), 2)
             pad = padded_baseline(torch, pvc, y)
             pad["speedup_of_varlen"] = round(pad["ms"] / a_ms, 2)
             others[name]["padded_sbhd"] = pad

@@ -18,15 +18,22 @@
 //                     dS^T = P^T o (dP^T - D) in registers, and
 //                     dQ^T += K^T dS^T with K^T from the transposing LDS read;
 //   bwd_dkdv_kernel   key-major: a wave holds K^T and V^T of its 32 keys and
-//                     streams 32-query stages of Q, dO, lse and D; per stage
+//                     streams 64-query stages (two 32-query halves) of Q, dO,
+//                     lse and D through a ring of three buffers; per half
 //                     S = Q K^T and dP = dO V^T (lane = key), P and dS in
 //                     registers, dV^T += dO^T P and dK^T += Q^T dS with Q^T and
-//                     dO^T from the transposing LDS read.
+//                     dO^T from the transposing LDS read.  Both halves' S and
+//                     dP are issued first, so one half's MFMA chains overlap
+//                     the other half's exponentials.  One wave per SIMD
+//                     (about 370 registers: the two fp32 accumulators alone
+//                     take 128).
 // Every product rounds its probability operand (P or dS) to bf16 and
 // accumulates in fp32.  No atomics: each output element is written once, so
 // results do not depend on scheduling.  Stages that lie wholly outside a
-// wave's segments or on the wrong side of its diagonal are skipped, exactly as
-// in the forward.
+// wave's segments or on the wrong side of its diagonal are skipped, as in the
+// forward.  The dQ kernel recomputes S and dP, which the dK/dV kernel also
+// computes: seven products per score instead of five, the price of writing
+// every gradient once without atomics.
 #include "attn_common.h"
 
 namespace pvc {
@@ -62,6 +69,27 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Scratch rows per head: T rounded up to the stage size plus two stages, so
 // every 32-row block a stage reads lies inside the plane.
 inline int64_t scratch_rows(int64_t T) { return (T + kBN - 1) / kBN * kBN + 2 * kBN; }
+
+#ifndef PVC_DQ_RING
+#define PVC_DQ_RING 2
+#endif
+#ifndef PVC_DKDV_RING
+#define PVC_DKDV_RING 3
+#endif
+constexpr int kDqRing = PVC_DQ_RING;        // stage buffers of the dQ kernel
+constexpr int kDkdvRing = PVC_DKDV_RING;    // stage buffers of the dK/dV kernel
+
+// s_waitcnt vmcnt(LPS * ahead) for ahead < RING - 1 (expcnt and lgkmcnt left
+// open; vmcnt is split over bits 3:0 and 15:14): every stage but the newest
+// `ahead` ones has landed for this wave
+template <int RING, int LPS>
+__device__ __attribute__((always_inline)) inline void wait_stages(int ahead) {
+    static_assert((RING - 2) * LPS <= 63, "vmcnt range");
+    static_for<RING - 1>([&](auto n) {
+        constexpr int v = decltype(n)::value * LPS;
+        if (ahead == decltype(n)::value) __builtin_amdgcn_s_waitcnt(0x0F70 | (v & 15) | ((v >> 4) << 14));
+    });
+}
 
 // ------------------------------------------------------------------- prep
 
@@ -128,7 +156,7 @@ void bwd_dq_kernel(BwdParams p) {
     constexpr int L16 = ROW_B / 16;
     constexpr int CHUNK_ROWS = kWaves * ROWS_PER_CHUNK;
     static_assert(CHUNK_ROWS % 16 == 0, "swizzle period");
-    __shared__ __attribute__((aligned(1024))) uint16_t sKV[2 * kRing * kBN * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t sKV[2 * kDqRing * kBN * D];
 
     const int logical = xcd_logical();
     if (logical >= p.items) return;
@@ -193,7 +221,7 @@ void bwd_dq_kernel(BwdParams p) {
     const uint32_t loff =
             (uint32_t)((fetch_rr * row_stride + ((lane % L16) ^ k_swz<D>(fetch_rr)) * 8) * 2);
     char* const kbase = reinterpret_cast<char*>(&sKV[0]);
-    char* const vbase = kbase + kRing * TILE_B;
+    char* const vbase = kbase + kDqRing * TILE_B;
     auto fetch_rows = [&](const uint16_t* src, lds_char* dst, int kt) {
         const char* base = reinterpret_cast<const char*>(src) + ((int64_t)kt * row_stride + head_off) * 2;
         const int64_t chunk_step = (int64_t)CHUNK_ROWS * row_stride * 2;
@@ -259,7 +287,7 @@ void bwd_dq_kernel(BwdParams p) {
         const int kt = k_lo + st * kBN;
         return kt >= max_start && kt + kBN <= min_end && (!CAUSAL || kt + kBN - 1 <= wr0);
     };
-    auto stage = [&](int st, const char* kb, const char* vb) {
+    auto stage = [&](int st, const char* kb, const char* vb) __attribute__((always_inline)) {
         f32x16 S = f32x16(0.0f), dP = f32x16(0.0f);
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -294,17 +322,20 @@ void bwd_dq_kernel(BwdParams p) {
             for (int j = 0; j < ND; ++j) acc[j] = mfma32(top(kb, ks, j), ds[ks], acc[j]);   // dQ^T += K^T dS^T
     };
 
-    static_for<kRing - 1>([&](auto i) {
+    // stages through a ring of kDqRing K and V buffers: stage st is computed
+    // while stages st+1 .. st+kDqRing-1 are in flight
+    constexpr int RING = kDqRing;
+    static_for<RING - 1>([&](auto i) {
         if (decltype(i)::value < nstages) fetch_stage(decltype(i)::value, decltype(i)::value);
     });
-    for (int st0 = 0; st0 < nstages; st0 += kRing) {
-        static_for<kRing>([&](auto I) {
+    for (int st0 = 0; st0 < nstages; st0 += RING) {
+        static_for<RING>([&](auto I) {
             constexpr int SLOT = decltype(I)::value;
             const int st = st0 + SLOT;
             if (st >= nstages) return;
-            __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0): stage st has landed
+            wait_stages<RING, 2 * CPW>(min(RING - 2, nstages - 1 - st));   // stage st has landed
             __syncthreads();
-            if (st + kRing - 1 < nstages) fetch_stage(st + kRing - 1, (SLOT + kRing - 1) % kRing);
+            if (st + RING - 1 < nstages) fetch_stage(st + RING - 1, (SLOT + RING - 1) % RING);
             if (stage_active(st)) stage(st, kbase + SLOT * TILE_B, vbase + SLOT * TILE_B);
         });
     }
@@ -327,7 +358,7 @@ void bwd_dq_kernel(BwdParams p) {
     } else {
         // through LDS for whole-row stores, as in the forward
         constexpr int CPR = ROW_B / 16;
-        static_assert(kBM * ROW_B <= 2 * kRing * TILE_B, "output tile fits the stage buffers");
+        static_assert(kBM * ROW_B <= 2 * kDqRing * TILE_B, "output tile fits the stage buffers");
         __syncthreads();
         char* const ob = kbase + wave * 32 * ROW_B;
 #pragma unroll
@@ -356,11 +387,13 @@ void bwd_dq_kernel(BwdParams p) {
 
 // --------------------------------------------------------------- dK, dV
 
-template <int D, bool CAUSAL, bool OUT_F32>
+template <int D, bool CAUSAL, bool OUT_F32, int NH>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdParams p) {
     static_assert(D == 64 || D == 128, "head_dim");
-    static_assert(kBN == 32, "one 32-query block per stage");
+    static_assert(kBN == 32, "32-query halves");
+    constexpr int SROWS = NH * kBN;               // query rows per stage
+    static_assert(SROWS <= 64, "the lse / D planes are padded by 64 rows");
     constexpr int NS = D / 16;
     constexpr int ND = D / 32;
     constexpr int ROW_B = D * 2;
@@ -372,9 +405,10 @@ void bwd_dkdv_kernel(BwdParams p) {
     constexpr int L16 = ROW_B / 16;
     constexpr int CHUNK_ROWS = kWaves * ROWS_PER_CHUNK;
     static_assert(CHUNK_ROWS % 16 == 0, "swizzle period");
-    // Q stages, then dO stages; then per stage 32 lse values and 32 D values
-    __shared__ __attribute__((aligned(1024))) uint16_t sQO[2 * kRing * kBN * D];
-    __shared__ __attribute__((aligned(16))) float sLD[kRing][2][kBN];
+    // Q stages, then dO stages (NH 32-row halves each); per stage and half
+    // 32 lse values and 32 D values
+    __shared__ __attribute__((aligned(1024))) uint16_t sQO[2 * kDkdvRing * SROWS * D];
+    __shared__ __attribute__((aligned(16))) float sLD[kDkdvRing][NH][2][kBN];
 
     const int logical = xcd_logical();
     if (logical >= p.items) return;
@@ -427,7 +461,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     bool sealed;
     const bool plan_ok = plan_sealed(p, CAUSAL, sealed);
     if (!sealed && tid == 0) raise_error(p.dev_error, PVC_DEV_PLAN);
-    const int nstages = plan_ok ? (q_hi - q_lo + kBN - 1) / kBN : 0;
+    const int nstages = plan_ok ? (q_hi - q_lo + SROWS - 1) / SROWS : 0;
 
     // ---- Q and dO stages (K swizzle), lse and D blocks (128 bytes each)
     const int64_t row_stride = (int64_t)H * D;
@@ -436,7 +470,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     const uint32_t loff =
             (uint32_t)((fetch_rr * row_stride + ((lane % L16) ^ k_swz<D>(fetch_rr)) * 8) * 2);
     char* const qbase = reinterpret_cast<char*>(&sQO[0]);
-    char* const obase = qbase + kRing * TILE_B;
+    char* const obase = qbase + kDkdvRing * NH * TILE_B;
     auto fetch_rows = [&](const uint16_t* src, lds_char* dst, int kt) {
         const char* base = reinterpret_cast<const char*>(src) + ((int64_t)kt * row_stride + head_off) * 2;
         const int64_t chunk_step = (int64_t)CHUNK_ROWS * row_stride * 2;
@@ -457,19 +491,27 @@ void bwd_dkdv_kernel(BwdParams p) {
     lds_char* const q_lds = (lds_char*)qbase;
     lds_char* const o_lds = (lds_char*)obase;
     lds_char* const ld_lds = (lds_char*)&sLD[0][0][0];
-    // lanes 0..7 of wave 0 load 32 lse values, lanes 8..15 the 32 D values of
-    // the stage: row qt + 4(l % 8) .. +3 of plane l / 8 (the planes are padded
-    // by two stages past T, so the block stays inside them)
+    // the lse and D values of a stage are 16 NH pieces of 16 bytes, laid out
+    // [half][plane][8 pieces]; every wave loads 4 NH of them (lanes 0 ..
+    // 4 NH - 1), so all waves issue the same number of loads per stage.
+    // Piece P = 4 NH wave + lane holds rows qt + 32 (P / 16) + 4 (P % 8) .. +3
+    // of plane (P / 8) % 2 (the planes are padded by 64 rows past T, so every
+    // piece lies inside them).
     const char* const sbase = reinterpret_cast<const char*>(p.scratch);
+    constexpr int PPW = 4 * NH;                      // pieces per wave
+    const int piece = PPW * wave + (lane & (PPW - 1));
+    const int64_t piece_row =
+            ((piece >> 3) & 1 ? (int64_t)H + head : (int64_t)head) * p.Tp + (piece >> 4) * kBN + 4 * (piece & 7);
     auto fetch_stage = [&](int st, int slot) {
-        const int qt = q_lo + st * kBN;
-        fetch_rows(p.q, q_lds + slot * TILE_B, qt);
-        fetch_rows(p.dout, o_lds + slot * TILE_B, qt);
-        if (wave == 0 && lane < 16) {
-            const int64_t plane = (lane < 8 ? (int64_t)head : (int64_t)H + head);
-            const uint32_t off = (uint32_t)((plane * p.Tp + qt + 4 * (lane & 7)) * 4);
-            lds_dma16(sbase, off, ld_lds + slot * (2 * kBN * 4));
+        const int qt = q_lo + st * SROWS;
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            fetch_rows(p.q, q_lds + (slot * NH + h) * TILE_B, qt + h * kBN);
+            fetch_rows(p.dout, o_lds + (slot * NH + h) * TILE_B, qt + h * kBN);
         }
+        // the LDS destination is wave-uniform; readfirstlane keeps it scalar
+        const int ld_dst = __builtin_amdgcn_readfirstlane((slot * NH * 2 * kBN + PPW * 4 * wave) * 4);
+        if (lane < PPW) lds_dma16(sbase, (uint32_t)((piece_row + qt) * 4), ld_lds + ld_dst);
     };
 
     uint32_t r_off[NS], t_off[ND][2];
@@ -504,77 +546,91 @@ void bwd_dkdv_kernel(BwdParams p) {
     const float sl2 = p.scale_log2;
 
     auto stage_active = [&](int st) -> bool {
-        const int qt = q_lo + st * kBN;
-        return wave_active && qt + kBN > w_qlo && qt < w_qhi;
+        const int qt = q_lo + st * SROWS;
+        return wave_active && qt + SROWS > w_qlo && qt < w_qhi;
     };
-    auto stage_full = [&](int st) -> bool {
-        const int qt = q_lo + st * kBN;
-        return qt >= full_lo && qt + kBN <= full_hi;
-    };
+    auto half_full = [&](int qt) -> bool { return qt >= full_lo && qt + kBN <= full_hi; };
     auto pack = [&](const bf16x2 (&pk)[8], bf16x8 (&outp)[2]) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
             outp[ks] = bf16x8{pk[4 * ks][0], pk[4 * ks][1], pk[4 * ks + 1][0], pk[4 * ks + 1][1],
                               pk[4 * ks + 2][0], pk[4 * ks + 2][1], pk[4 * ks + 3][0], pk[4 * ks + 3][1]};
     };
-    auto stage = [&](int st, const char* qb, const char* ob, const float* ld) {
-        // lane = key c; register r = query qt + 8(r/4) + 4g + r%4
-        f32x16 S = f32x16(0.0f), dP = f32x16(0.0f);
+    // one stage: S = Q K^T and dP = dO V^T for every half first, so the
+    // MFMA chains of one half overlap the exp / pack work of the other
+    auto stage = [&](int st, int slot) __attribute__((always_inline)) {
+        const int qt = q_lo + st * SROWS;
+        f32x16 S[NH], dP[NH];
+        static_for<NH>([&](auto H_) {
+            constexpr int h = decltype(H_)::value;
+            const char* qb = qbase + (slot * NH + h) * TILE_B;
+            const char* ob = obase + (slot * NH + h) * TILE_B;
+            S[h] = f32x16(0.0f);
+            dP[h] = f32x16(0.0f);
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            S = mfma32(rop(qb, s), kreg[s], S);          // S = Q K^T
-            dP = mfma32(rop(ob, s), vreg[s], dP);        // dP = dO V^T
-        }
-        if (!stage_full(st)) {
-            const int x0 = q_lo + st * kBN + 4 * g;
-            const int lo = lo_j - x0, hi = hi_j - x0;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int C = 8 * (r >> 2) + (r & 3);
-                S[r] = ((C >= lo) & (C < hi)) ? S[r] : -INFINITY;
+            for (int s = 0; s < NS; ++s) {
+                S[h] = mfma32(rop(qb, s), kreg[s], S[h]);      // S = Q K^T
+                dP[h] = mfma32(rop(ob, s), vreg[s], dP[h]);    // dP = dO V^T
             }
-        }
-        f32x4 l4[4], d4[4];
+        });
+        static_for<NH>([&](auto H_) {
+            constexpr int h = decltype(H_)::value;
+            // lane = key c; register r = query qt + 32h + 8(r/4) + 4g + r%4
+            const int qh = qt + h * kBN;
+            if (!half_full(qh)) {
+                const int x0 = qh + 4 * g;
+                const int lo = lo_j - x0, hi = hi_j - x0;
 #pragma unroll
-        for (int kq = 0; kq < 4; ++kq) {
-            l4[kq] = *reinterpret_cast<const f32x4*>(ld + 8 * kq + 4 * g);
-            d4[kq] = *reinterpret_cast<const f32x4*>(ld + kBN + 8 * kq + 4 * g);
-        }
-        bf16x2 pp[8], pd[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r0_ = 2 * i, r1_ = 2 * i + 1;
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(S[r0_], sl2, -l4[r0_ >> 2][r0_ & 3]));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(S[r1_], sl2, -l4[r1_ >> 2][r1_ & 3]));
-            pp[i] = bf16x2{(__bf16)p0, (__bf16)p1};
-            pd[i] = bf16x2{(__bf16)(p0 * (dP[r0_] - d4[r0_ >> 2][r0_ & 3])),
-                           (__bf16)(p1 * (dP[r1_] - d4[r1_ >> 2][r1_ & 3]))};
-        }
-        bf16x8 Pb[2], Db[2];
-        pack(pp, Pb);
-        pack(pd, Db);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int j = 0; j < ND; ++j) {
-                accV[j] = mfma32(top(ob, ks, j), Pb[ks], accV[j]);   // dV^T += dO^T P
-                accK[j] = mfma32(top(qb, ks, j), Db[ks], accK[j]);   // dK^T += Q^T dS
+                for (int r = 0; r < 16; ++r) {
+                    const int C = 8 * (r >> 2) + (r & 3);
+                    S[h][r] = ((C >= lo) & (C < hi)) ? S[h][r] : -INFINITY;
+                }
             }
+            const float* ld = &sLD[slot][h][0][0];
+            f32x4 l4[4], d4[4];
+#pragma unroll
+            for (int kq = 0; kq < 4; ++kq) {
+                l4[kq] = *reinterpret_cast<const f32x4*>(ld + 8 * kq + 4 * g);
+                d4[kq] = *reinterpret_cast<const f32x4*>(ld + kBN + 8 * kq + 4 * g);
+            }
+            bf16x2 pp[8], pd[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int r0_ = 2 * i, r1_ = 2 * i + 1;
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(S[h][r0_], sl2, -l4[r0_ >> 2][r0_ & 3]));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(S[h][r1_], sl2, -l4[r1_ >> 2][r1_ & 3]));
+                pp[i] = bf16x2{(__bf16)p0, (__bf16)p1};
+                pd[i] = bf16x2{(__bf16)(p0 * (dP[h][r0_] - d4[r0_ >> 2][r0_ & 3])),
+                               (__bf16)(p1 * (dP[h][r1_] - d4[r1_ >> 2][r1_ & 3]))};
+            }
+            bf16x8 Pb[2], Db[2];
+            pack(pp, Pb);
+            pack(pd, Db);
+            const char* qb = qbase + (slot * NH + h) * TILE_B;
+            const char* ob = obase + (slot * NH + h) * TILE_B;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int j = 0; j < ND; ++j) {
+                    accV[j] = mfma32(top(ob, ks, j), Pb[ks], accV[j]);   // dV^T += dO^T P
+                    accK[j] = mfma32(top(qb, ks, j), Db[ks], accK[j]);   // dK^T += Q^T dS
+                }
+        });
     };
 
-    static_for<kRing - 1>([&](auto i) {
+    constexpr int RING = kDkdvRing;
+    static_for<RING - 1>([&](auto i) {
         if (decltype(i)::value < nstages) fetch_stage(decltype(i)::value, decltype(i)::value);
     });
-    for (int st0 = 0; st0 < nstages; st0 += kRing) {
-        static_for<kRing>([&](auto I) {
+    for (int st0 = 0; st0 < nstages; st0 += RING) {
+        static_for<RING>([&](auto I) {
             constexpr int SLOT = decltype(I)::value;
             const int st = st0 + SLOT;
             if (st >= nstages) return;
-            __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0): stage st has landed
+            wait_stages<RING, 2 * NH * CPW + 1>(min(RING - 2, nstages - 1 - st));   // stage st has landed
             __syncthreads();
-            if (st + kRing - 1 < nstages) fetch_stage(st + kRing - 1, (SLOT + kRing - 1) % kRing);
-            if (stage_active(st))
-                stage(st, qbase + SLOT * TILE_B, obase + SLOT * TILE_B, &sLD[SLOT][0][0]);
+            if (st + RING - 1 < nstages) fetch_stage(st + RING - 1, (SLOT + RING - 1) % RING);
+            if (stage_active(st)) stage(st, SLOT);
         });
     }
 
@@ -601,7 +657,7 @@ void bwd_dkdv_kernel(BwdParams p) {
         }
     } else {
         constexpr int CPR = ROW_B / 16;
-        static_assert(kBM * ROW_B <= 2 * kRing * TILE_B, "output tile fits the stage buffers");
+        static_assert(kBM * ROW_B <= 2 * kDkdvRing * NH * TILE_B, "output tile fits the stage buffers");
         char* const ob = qbase + wave * 32 * ROW_B;
         auto emit = [&](const f32x16 (&acc)[ND], float mul, uint16_t* dst) {
             __syncthreads();                           // stage buffers (or the last tile) are free
@@ -634,6 +690,11 @@ void bwd_dkdv_kernel(BwdParams p) {
 
 // ------------------------------------------------------------------- host
 
+#ifndef PVC_DKDV_HALVES
+#define PVC_DKDV_HALVES 2
+#endif
+constexpr int kDkdvHalves = PVC_DKDV_HALVES;
+
 template <int D>
 pvc_status launch_bwd(const BwdParams& prm, bool causal, bool out_f32, hipStream_t s) {
     {
@@ -649,18 +710,18 @@ pvc_status launch_bwd(const BwdParams& prm, bool causal, bool out_f32, hipStream
     if (causal) {
         if (out_f32) {
             hipLaunchKernelGGL((bwd_dq_kernel<D, true, true>), g, blk, 0, s, prm);
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, true>), g, blk, 0, s, prm);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, true, kDkdvHalves>), g, blk, 0, s, prm);
         } else {
             hipLaunchKernelGGL((bwd_dq_kernel<D, true, false>), g, blk, 0, s, prm);
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false>), g, blk, 0, s, prm);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false, kDkdvHalves>), g, blk, 0, s, prm);
         }
     } else {
         if (out_f32) {
             hipLaunchKernelGGL((bwd_dq_kernel<D, false, true>), g, blk, 0, s, prm);
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true>), g, blk, 0, s, prm);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true, kDkdvHalves>), g, blk, 0, s, prm);
         } else {
             hipLaunchKernelGGL((bwd_dq_kernel<D, false, false>), g, blk, 0, s, prm);
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, false>), g, blk, 0, s, prm);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, false, kDkdvHalves>), g, blk, 0, s, prm);
         }
     }
     return launch_status();
