@@ -13,10 +13,12 @@ Contents (each function cites the passage it follows):
   attention   fp64 block-diagonal causal attention (C loop, explicit mask,
               and per-segment unpacked forms)
   accounting  slot, waste and pair counts used for useful-FLOP figures
+  loss        packed cross-entropy: loss sum, target count, per-segment sums,
+              token / sample averages, gradient of the loss sum
 
 Every function here is pinned by tests that do not restate its own formula
 (worked examples printed on the pages, closed forms, invariants, library
 routines on special cases, brute force on tiny inputs).
 """
 
-from . import accounting, attention, pack, rope  # noqa: F401
+from . import accounting, attention, loss, pack, rope  # noqa: F401
