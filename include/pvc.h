@@ -77,7 +77,9 @@ enum {
                                      ([charlestar]: [0,4,5,9] looks like a prefix sum
                                      of [3,2,4] but moves b0 into A) */
     PVC_DEV_RANGE = 64u,          /* the sum of lengths does not fit in int32 */
-    PVC_DEV_PLAN = 128u           /* attention run with a plan built for other arguments */
+    PVC_DEV_PLAN = 128u,          /* attention run with a plan built for other arguments */
+    PVC_DEV_LABEL = 256u          /* packed CE: a label outside [0, vocab) that is not
+                                     the ignore index (the row is not a target) */
 };
 
 /* Static text for a status code (never NULL). */
@@ -281,6 +283,62 @@ pvc_status pvc_padded_attn_fwd_sbhd(const void* q, const void* k, const void* v,
                                     const int32_t* seqlens, int32_t batch, int32_t max_len,
                                     int32_t heads, int32_t head_dim, int32_t causal,
                                     int32_t out_dtype, void* stream);
+
+/* ------------------------------------------------------ packed cross-entropy */
+
+/* Workspace bytes of pvc_packed_ce_loss for total_tokens rows (0 if out of
+ * range). */
+size_t pvc_ce_workspace_size(int64_t total_tokens);
+
+/* Cross-entropy over the rows of a packed buffer: the loss summed over the
+ * valid targets and the int64 count of valid targets, kept apart rather than
+ * averaged ([charlestar] "cross-boundary prediction pairs": reduction "sum"
+ * with the ignore index, then the count of labels that are not ignored; no
+ * class weights, no label smoothing).  Optionally per-row losses, per-segment
+ * sums and counts (the S_r and n_r of [charlestar] "packing should not choose
+ * the weight of long samples", for a token or a sample average) and the
+ * gradient of the loss sum.
+ *
+ * logits       [total_tokens rows, vocab] on the device, row stride ld
+ *              elements (ld >= vocab); bf16 (logits_dtype PVC_OUT_BF16) or
+ *              fp32 (PVC_OUT_F32).  Rows whose starts are 16-byte aligned are
+ *              read as 16-byte vectors, others one value at a time.
+ * labels       [total_tokens] int32: the pre-shifted labels of pvc_pack_build
+ *              (label[i] is the target of row i; ignore_index where row i
+ *              predicts nothing).  A label outside [0, vocab) other than
+ *              ignore_index makes the row a non-target and sets
+ *              PVC_DEV_LABEL.
+ * cu_seqlens   [nseg + 1] int32 (nullable unless seg_loss / seg_count are
+ *              given); a malformed cu sets PVC_DEV_CU0 / NOT_INCREASING /
+ *              TOTAL and its entries are clamped into [0, total_tokens].
+ * loss_sum     [1] fp64 out: the sum of the valid rows' losses.  Each row's
+ *              loss is computed in fp32 (log-sum-exp with the row max
+ *              subtracted); the sums run in fp64 in a fixed order, so the
+ *              result does not depend on scheduling.
+ * target_count [1] int64 out: the number of rows with a label in [0, vocab).
+ * row_loss     [total_tokens] fp32 out, nullable: each row's loss, 0 for a
+ *              row that is not a target.
+ * seg_loss, seg_count  [nseg] fp64 / int64 out, nullable: the sums over
+ *              [cu_r, cu_{r+1}).
+ * grad         nullable: [total_tokens, vocab], row stride grad_ld, bf16 or
+ *              fp32 (grad_dtype): grad_scale * (softmax(z_i) - onehot(y_i)) on
+ *              target rows, 0 on the others.  May be the logits buffer itself
+ *              (same dtype and stride: computed in place); otherwise it must
+ *              not overlap the logits.  grad_scale finite (for example 1/N or
+ *              W/N of [charlestar] "the distributed denominator").
+ * workspace    >= pvc_ce_workspace_size(total_tokens) bytes, 16-byte aligned.
+ * Device outputs are written on `stream`; nothing is synchronized.
+ * Errors: NULL required pointer -> PVC_ERR_NULL; total_tokens outside
+ * [1, 2^31), vocab < 1, ld < vocab, an unknown dtype, a non-finite scale,
+ * nseg outside [1, total_tokens], overlapping outputs -> PVC_ERR_INVALID_ARG;
+ * a small workspace -> PVC_ERR_WORKSPACE.
+ */
+pvc_status pvc_packed_ce_loss(const void* logits, int32_t logits_dtype, int64_t ld, const int32_t* labels,
+                              int64_t total_tokens, int32_t vocab, int32_t ignore_index,
+                              const int32_t* cu_seqlens, int32_t nseg, double* loss_sum,
+                              int64_t* target_count, float* row_loss, double* seg_loss, int64_t* seg_count,
+                              void* grad, int32_t grad_dtype, int64_t grad_ld, float grad_scale,
+                              void* workspace, size_t workspace_bytes, uint32_t* dev_error, void* stream);
 
 #ifdef __cplusplus
 }

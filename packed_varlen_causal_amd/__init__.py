@@ -16,6 +16,9 @@ Entry points (same names as the C ABI without the ``pvc_`` prefix):
   varlen_attn_fwd       block-diagonal (causal) attention over THD q/k/v
   varlen_attn_bwd       its gradients dq, dk, dv on the same plan
   padded_attn_fwd_sbhd  the same kernel on a padded SBHD buffer (measurement)
+  packed_ce_loss        cross-entropy over the packed rows: loss sum, int64
+                        target count, optional per-row / per-segment values and
+                        the fused gradient
 """
 
 from __future__ import annotations
@@ -29,6 +32,7 @@ __all__ = [
     "PvcError", "DEV_ERROR_BITS", "lib_path", "pack_build", "validate_cu_seqlens",
     "rope_thd_apply", "AttnPlan", "attn_plan", "varlen_attn_fwd", "varlen_attn_bwd",
     "padded_attn_fwd_sbhd", "error_names", "attn_workspace_size", "attn_bwd_scratch_size",
+    "packed_ce_loss", "ce_workspace_size",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -38,7 +42,7 @@ OK, ERR_NULL, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(6
 OUT_BF16, OUT_F32 = 0, 1
 DEV_ERROR_BITS = {
     1: "CU0", 2: "NOT_INCREASING", 4: "TOTAL", 8: "MAXSEQ", 16: "LENGTH",
-    32: "MISMATCH", 64: "RANGE", 128: "PLAN",
+    32: "MISMATCH", 64: "RANGE", 128: "PLAN", 256: "LABEL",
 }
 
 
@@ -68,6 +72,9 @@ def _load() -> ctypes.CDLL:
         "pvc_attn_bwd_scratch_size": ([I64, I32], SZ),
         "pvc_varlen_attn_bwd_planned": ([P, P, P, P, P, P, P, P, P, I64, I32, I32, I32, I32, P, SZ, P, SZ,
                                          P, P], I32),
+        "pvc_ce_workspace_size": ([I64], SZ),
+        "pvc_packed_ce_loss": ([P, I32, I64, P, I64, I32, I32, P, I32, P, P, P, P, P, P, I32, I64, F32, P, SZ,
+                                P, P], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -372,4 +379,85 @@ def padded_attn_fwd_sbhd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seql
                                        int(bool(causal)),
                                        OUT_F32 if out_dtype == torch.float32 else OUT_BF16, _stream(stream))
     _check(st, "padded_attn_fwd_sbhd")
+    return out
+
+
+def ce_workspace_size(total_tokens: int) -> int:
+    return int(_lib.pvc_ce_workspace_size(total_tokens))
+
+
+def packed_ce_loss(logits: torch.Tensor, labels: torch.Tensor, cu_seqlens: torch.Tensor | None = None,
+                   ignore_index: int = -100, row_loss: bool = False, segments: bool = False,
+                   grad: torch.Tensor | str | None = None, grad_dtype: torch.dtype | None = None,
+                   grad_scale: float = 1.0, workspace: torch.Tensor | None = None,
+                   dev_error: torch.Tensor | None = None, check: bool = False, stream=None) -> dict:
+    """Cross-entropy over packed rows (see pvc_packed_ce_loss in include/pvc.h).
+
+    logits [T, V] bf16 or fp32 (rows may be strided: stride(1) must be 1);
+    labels [T] int32, the pre-shifted labels of pack_build.  Returns a dict of
+    device tensors: loss_sum (fp64 [1]), target_count (int64 [1]), and on
+    request row_loss (fp32 [T]), seg_loss / seg_count ([nseg], needs
+    cu_seqlens) and grad.  ``grad`` is "new" (a fresh tensor of grad_dtype,
+    default the logits' dtype), "inplace" (written over the logits) or a
+    caller tensor of the logits' shape.
+    """
+    if logits.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("logits must be bf16 or fp32")
+    if logits.device.type != "cuda" or logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be a 2-D GPU tensor with unit stride along the vocabulary")
+    T, V = logits.shape
+    _require(labels, "labels", torch.int32, 1)
+    if labels.numel() != T:
+        raise ValueError("one label per row")
+    dev = logits.device
+    dt = OUT_F32 if logits.dtype == torch.float32 else OUT_BF16
+    nseg = 0
+    if cu_seqlens is not None:
+        _require(cu_seqlens, "cu_seqlens", torch.int32, 1)
+        nseg = cu_seqlens.numel() - 1
+    elif segments:
+        raise ValueError("segments=True needs cu_seqlens")
+    out = {"loss_sum": torch.empty(1, dtype=torch.float64, device=dev),
+           "target_count": torch.empty(1, dtype=torch.int64, device=dev)}
+    if row_loss:
+        out["row_loss"] = torch.empty(T, dtype=torch.float32, device=dev)
+    if segments:
+        out["seg_loss"] = torch.empty(nseg, dtype=torch.float64, device=dev)
+        out["seg_count"] = torch.empty(nseg, dtype=torch.int64, device=dev)
+    g = None
+    if isinstance(grad, str):
+        if grad == "inplace":
+            if grad_dtype not in (None, logits.dtype):
+                raise ValueError("an in-place gradient has the logits' dtype")
+            g = logits
+        elif grad == "new":
+            g = torch.empty((T, V), dtype=grad_dtype or logits.dtype, device=dev)
+        else:
+            raise ValueError('grad must be None, "new", "inplace" or a tensor')
+    elif grad is not None:
+        g = grad
+        if g.dtype not in (torch.bfloat16, torch.float32) or g.dim() != 2 or tuple(g.shape) != (T, V) \
+                or g.stride(1) != 1 or g.device != dev:
+            raise ValueError("grad must be a [T, V] bf16 / fp32 GPU tensor with unit vocabulary stride")
+    if g is not None:
+        out["grad"] = g
+    nb = ce_workspace_size(T)
+    if workspace is None:
+        workspace = torch.empty(nb, dtype=torch.uint8, device=dev)
+    else:
+        _require(workspace, "workspace", torch.uint8, 1)
+        if workspace.numel() < nb:
+            raise ValueError(f"workspace must hold {nb} bytes (ce_workspace_size)")
+    if dev_error is None:
+        dev_error = torch.zeros(1, dtype=torch.int32, device=dev)
+    gdt = 0 if g is None else (OUT_F32 if g.dtype == torch.float32 else OUT_BF16)
+    st = _lib.pvc_packed_ce_loss(
+        _ptr(logits), dt, logits.stride(0), _ptr(labels), T, V, ignore_index, _ptr(cu_seqlens), nseg,
+        _ptr(out["loss_sum"]), _ptr(out["target_count"]), _ptr(out.get("row_loss")), _ptr(out.get("seg_loss")),
+        _ptr(out.get("seg_count")), _ptr(g), gdt, 0 if g is None else g.stride(0), float(grad_scale),
+        _ptr(workspace), workspace.numel(), _ptr(dev_error), _stream(stream))
+    _check(st, "packed_ce_loss")
+    out["dev_error"] = dev_error
+    if check:
+        _raise_dev(dev_error, "packed_ce_loss")
     return out

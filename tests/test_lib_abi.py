@@ -40,7 +40,8 @@ def test_header_declares_the_hot_path():
     for must in ("pvc_pack_build", "pvc_validate_cu_seqlens", "pvc_rope_thd_apply", "pvc_attn_plan",
                  "pvc_varlen_attn_fwd", "pvc_varlen_attn_fwd_planned", "pvc_padded_attn_fwd_sbhd",
                  "pvc_attn_workspace_size", "pvc_pack_build_workspace_size", "pvc_status_string",
-                 "pvc_varlen_attn_bwd_planned", "pvc_attn_bwd_scratch_size"):
+                 "pvc_varlen_attn_bwd_planned", "pvc_attn_bwd_scratch_size", "pvc_packed_ce_loss",
+                 "pvc_ce_workspace_size"):
         assert must in names
 
 
@@ -172,6 +173,31 @@ def test_null_and_range_checks_return_before_gpu_work(lib):
     assert bwd(ptrs=g[:6] + [_vp(0x100008)] + g[7:]) == 2      # misaligned dq
     assert bwd(ptrs=g[:7] + [g[6]] + g[8:]) == 2               # dk aliasing dq
     assert bwd(ptrs=g[:8] + [g[0]] + g[9:]) == 2               # dv aliasing q
+
+    lib.pvc_ce_workspace_size.restype = SZ
+    lib.pvc_ce_workspace_size.argtypes = [I64]
+    assert lib.pvc_ce_workspace_size(0) == 0
+    assert lib.pvc_ce_workspace_size(100) >= 100 * 4       # one fp32 loss per row
+    lib.pvc_packed_ce_loss.restype = I32
+    lib.pvc_packed_ce_loss.argtypes = [P, I32, I64, P, I64, I32, I32, P, I32, P, P, P, P, P, P, I32, I64, F32,
+                                       P, SZ, P, P]
+    z, lab, ls, tc = (_vp(0x1000000 * (i + 1)) for i in range(4))
+
+    def ce(*, logits=z, dt=0, ld=64, T=9, V=64, cu=None, nseg=0, seg=None, grad=None, gdt=0, gld=64, scale=1.0,
+           ws=big, labels=lab):
+        return lib.pvc_packed_ce_loss(logits, dt, ld, labels, T, V, -100, cu, nseg, ls, tc, None, seg, None, grad,
+                                      gdt, gld, scale, fake, ws, None, None)
+
+    assert ce(logits=None) == 1
+    assert ce(labels=None) == 1
+    assert ce(seg=_vp(0x9000000)) == 1                     # segment sums without cu_seqlens
+    assert ce(T=0) == 2
+    assert ce(ld=63) == 2                                  # row stride below the vocabulary
+    assert ce(dt=7) == 2
+    assert ce(ws=8) == 4
+    assert ce(cu=fake, nseg=10) == 2                       # more segments than rows
+    assert ce(grad=_vp(0x1000000 + 64)) == 2               # gradient overlapping the logits
+    assert ce(grad=_vp(0x9000000), scale=float("inf")) == 2
 
 
 def test_python_binding_imports_without_gpu():

@@ -13,6 +13,7 @@ from .generators import (  # noqa: F401
     Workload,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
+    logits_bits,
     make_workload,
     qkv_bits,
     token_ids,

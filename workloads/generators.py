@@ -9,7 +9,7 @@ Page tags used in citations (the pages are the specification):
 
 Every random draw comes from ``numpy.random.default_rng([cfg_id, stream, seed])``
 (PCG64).  Streams: 0 = sample lengths, 1 = token ids, 2/3/4 = q/k/v, 5 = an upstream
-gradient of the attention output.  q/k/v are
+gradient of the attention output, 6 = logits for the packed cross-entropy.  q/k/v are
 standard normal float32 values rounded to bf16 (round to nearest even) and are
 carried as uint16 bit patterns, shape ``[T, H, d]`` (THD, no batch dim).
 
@@ -288,3 +288,16 @@ def qkv_bits(w: Workload, which: str, chunk: int = 1 << 24) -> np.ndarray:
         e = min(n, s + chunk)
         out[s:e] = f32_to_bf16_bits(rng.standard_normal(e - s, dtype=np.float32))
     return out.reshape(w.total_tokens, w.heads, w.head_dim)
+
+
+def logits_bits(w: Workload, vocab: int, sigma: float = 2.0, rows: int | None = None,
+                chunk: int = 1 << 24) -> np.ndarray:
+    """uint16 [rows or T, vocab] bf16 bit patterns of N(0, sigma^2) logits."""
+    rng = _rng(w.cfg_id, 6, w.seed)
+    T = w.total_tokens if rows is None else rows
+    n = T * vocab
+    out = np.empty(n, np.uint16)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        out[s:e] = f32_to_bf16_bits(rng.standard_normal(e - s, dtype=np.float32) * np.float32(sigma))
+    return out.reshape(T, vocab)
