@@ -11,7 +11,8 @@ Printed: ONE JSON line.  value = useful attention TFLOP/s over the whole step
 segments are computed but not counted).  Per-kernel durations come from HIP
 events recorded on the stream the kernels run on.  Beside it, in the same
 process: the backward (varlen_attn_bwd, not part of the step: useful FLOPs
-2.5x the forward's), the same kernel on the padded SBHD layout, the other
+2.5x the forward's), the packed cross-entropy over the step's labels with
+[T, 32000] logits (packed_ce_loss, not part of the step), the same kernel on the padded SBHD layout, the other
 workloads' attention rates, and the fp64 CPU oracle timed on a bounded sample
 of rows.
 """
@@ -193,6 +194,46 @@ def time_backward(torch, pvc, x, steps, warmup):
     bflops = BWD_FLOP_RATIO * x.flops
     return {"ms": round(ms, 4), "useful_tflops": round(bflops / (ms * 1e-3) / 1e12, 2),
             "pct_bf16_peak": round(100 * bflops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+
+
+CE_VOCAB = 32000          # the token recipe's id range [3, 32000)
+
+
+def time_ce(torch, pvc, x, steps, warmup, vocab=CE_VOCAB):
+    """packed_ce_loss over the step's pre-shifted labels and [T, vocab] bf16
+    logits drawn on the device from a seeded generator: loss sum + target
+    count (+ per-segment sums), then the same with the fused gradient written
+    in place.  Algorithmic bytes: the logits read once (2 T V), labels and
+    row losses (8 T), plus 2 T V written with the gradient."""
+    meta = pvc.pack_build(x.lengths, x.tokens, x.is_pad, dev_error=x.err)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(6)
+    logits = torch.randn((x.T, vocab), generator=gen, device="cuda", dtype=torch.bfloat16) * 2
+    ws = torch.empty(pvc.ce_workspace_size(x.T), dtype=torch.uint8, device="cuda")
+    res = {"vocab": vocab, "logits": f"[{x.T}, {vocab}] bf16, N(0, 4), seeded on the device"}
+    for name, grad in (("loss", None), ("loss_and_grad_inplace", "inplace")):
+        call = lambda: pvc.packed_ce_loss(logits, meta["shifted_labels"], meta["cu_seqlens"],  # noqa: E731
+                                          segments=True, grad=grad, grad_scale=1.0, workspace=ws,
+                                          dev_error=x.err)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        nbytes = 2.0 * x.T * vocab * (2 if grad else 1) + 8.0 * x.T
+        res[name] = {"ms": round(ms, 4), "gbps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                     "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                     "algorithmic_bytes": nbytes}
+    if int(x.err.item()) != 0:
+        raise RuntimeError(f"device error bits {pvc.error_names(int(x.err.item()))}")
+    del logits, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def padded_baseline(torch, pvc, x, reps=3, max_chunk_bytes=24 << 30):
@@ -481,6 +522,7 @@ def main():
     }
     torch.cuda.synchronize()
     res["kernels"]["varlen_attn_bwd"] = time_backward(torch, pvc, x, max(3, args.steps // 2), 2)
+    res["kernels"]["packed_ce_loss"] = time_ce(torch, pvc, x, max(3, args.steps // 2), 2)
 
     if not args.no_extras:
         res["padded_sbhd"] = padded_baseline(torch, pvc, x)

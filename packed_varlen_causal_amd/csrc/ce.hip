@@ -41,6 +41,7 @@ namespace {
 constexpr int kCeThreads = 256;
 constexpr int kCeRowsPerBlock = 4096;        // rows per ce_reduce_kernel workgroup
 constexpr int kCeChunk = 4;                  // 16-byte vectors per thread per chunk
+constexpr int kCeResident = 16;              // vectors per thread of a register-resident row
 constexpr float kL2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 
@@ -136,7 +137,11 @@ struct CeParams {
 
 // One row per workgroup.  VEC: the row start is 16-byte aligned, so the first
 // floor(V / N) * N values are read as vectors and the rest one by one.
-template <bool IN_F32, int GRAD /* 0 none, 1 bf16, 2 fp32 */>
+// RES: the vectors of the row fit in registers (at most kCeResident per
+// thread): they are loaded once, the thread's max is taken over all of them
+// before any exponential, and the gradient pass reads them from registers
+// instead of from memory again.
+template <bool IN_F32, int GRAD /* 0 none, 1 bf16, 2 fp32 */, bool RES>
 __global__ __launch_bounds__(kCeThreads) void ce_row_kernel(CeParams p, bool vec) {
     using VT = Vec<IN_F32>;
     constexpr int N = VT::N;
@@ -153,7 +158,38 @@ __global__ __launch_bounds__(kCeThreads) void ce_row_kernel(CeParams p, bool vec
     MaxSum acc;
     const int nvec = vec ? V / N : 0;
     const u32x4* vp = reinterpret_cast<const u32x4*>(rowp);
-    for (int c0 = 0; c0 < nvec; c0 += kCeChunk * kCeThreads) {
+    u32x4 res[RES ? kCeResident : 1];
+    if constexpr (RES) {
+#pragma unroll
+        for (int i = 0; i < kCeResident; ++i) {
+            const int vi = i * kCeThreads + tid;
+            res[i] = vi < nvec ? vp[vi] : u32x4{0u, 0u, 0u, 0u};
+        }
+        float cm = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < kCeResident; ++i) {
+            if (i * kCeThreads + tid < nvec) {
+                float x[N];
+                VT::unpack(res[i], x);
+#pragma unroll
+                for (int e = 0; e < N; ++e) cm = fmaxf(cm, x[e]);
+            }
+        }
+        const float nb = -safe_base(cm) * kL2e;
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kCeResident; ++i) {
+            if (i * kCeThreads + tid < nvec) {
+                float x[N];
+                VT::unpack(res[i], x);
+#pragma unroll
+                for (int e = 0; e < N; ++e) s += __builtin_amdgcn_exp2f(fmaf(x[e], kL2e, nb));
+            }
+        }
+        acc.m = cm;
+        acc.s = s;
+    }
+    for (int c0 = 0; !RES && c0 < nvec; c0 += kCeChunk * kCeThreads) {
         float x[kCeChunk][N];
         float cm = -INFINITY;
 #pragma unroll
@@ -201,9 +237,9 @@ __global__ __launch_bounds__(kCeThreads) void ce_row_kernel(CeParams p, bool vec
             const float pr = __builtin_amdgcn_exp2f(fmaf(x - base, kL2e, -l2s));
             return sc * (pr - (idx == y ? 1.0f : 0.0f));
         };
-        for (int vi = tid; vi < nvec; vi += kCeThreads) {
+        auto emit = [&](int vi, const u32x4& wv) {
             float x[N];
-            VT::unpack(vp[vi], x);
+            VT::unpack(wv, x);
             if constexpr (GRAD == 2) {
 #pragma unroll
                 for (int q = 0; q < N / 4; ++q)
@@ -223,6 +259,13 @@ __global__ __launch_bounds__(kCeThreads) void ce_row_kernel(CeParams p, bool vec
                     reinterpret_cast<uint32_t*>(growp)[2 * vi + 1] = w[1];
                 }
             }
+        };
+        if constexpr (RES) {
+#pragma unroll
+            for (int i = 0; i < kCeResident; ++i)
+                if (i * kCeThreads + tid < nvec) emit(i * kCeThreads + tid, res[i]);
+        } else {
+            for (int vi = tid; vi < nvec; vi += kCeThreads) emit(vi, vp[vi]);
         }
         for (int i = nvec * N + tid; i < V; i += kCeThreads) {
             const float g = gval(VT::scalar(rowp, i), i);
@@ -358,12 +401,19 @@ bool ce_overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
+template <bool IN_F32, bool RES>
+void launch_rows2(const CeParams& prm, bool vec, int grad, hipStream_t s) {
+    const dim3 g((unsigned)prm.T), b(kCeThreads);
+    if (grad == 0) hipLaunchKernelGGL((ce_row_kernel<IN_F32, 0, RES>), g, b, 0, s, prm, vec);
+    else if (grad == 1) hipLaunchKernelGGL((ce_row_kernel<IN_F32, 1, RES>), g, b, 0, s, prm, vec);
+    else hipLaunchKernelGGL((ce_row_kernel<IN_F32, 2, RES>), g, b, 0, s, prm, vec);
+}
+
 template <bool IN_F32>
 void launch_rows(const CeParams& prm, bool vec, int grad, hipStream_t s) {
-    const dim3 g((unsigned)prm.T), b(kCeThreads);
-    if (grad == 0) hipLaunchKernelGGL((ce_row_kernel<IN_F32, 0>), g, b, 0, s, prm, vec);
-    else if (grad == 1) hipLaunchKernelGGL((ce_row_kernel<IN_F32, 1>), g, b, 0, s, prm, vec);
-    else hipLaunchKernelGGL((ce_row_kernel<IN_F32, 2>), g, b, 0, s, prm, vec);
+    constexpr int N = IN_F32 ? 4 : 8;
+    if (vec && prm.V / N <= kCeResident * kCeThreads) launch_rows2<IN_F32, true>(prm, vec, grad, s);
+    else launch_rows2<IN_F32, false>(prm, vec, grad, s);
 }
 
 }  // namespace
