@@ -19,6 +19,11 @@ Precision contract shared with the device library:
           same angle bit for bit;
   cos, sin and the rotation in double, then one rounding to bf16 (nearest,
           ties to even).
+Interleaved pairing (the RoFormer construction [charlestar] "positions and
+RoPE" cites; a flag on the device side): pair j is (x_{2j}, x_{2j+1}), with the
+same angle theta_j and the same precision contract:
+    y_{2j}   = x_{2j} cos theta - x_{2j+1} sin theta
+    y_{2j+1} = x_{2j+1} cos theta + x_{2j} sin theta
 The pages' shift-invariance identity ([charlestar] "positions and RoPE"):
 (R(m+c)q)^T (R(n+c)k) = q^T R(n-m) k, so a common per-segment offset cancels.
 """
@@ -74,11 +79,23 @@ def rotate_f64(x: np.ndarray, theta: np.ndarray) -> np.ndarray:
     return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
 
 
-def rope_apply(x_bits: np.ndarray, cu, base: float = 10000.0, rows=None) -> np.ndarray:
+def rotate_interleaved_f64(x: np.ndarray, theta: np.ndarray) -> np.ndarray:
+    """Interleaved rotation in double: pair j is (x_{2j}, x_{2j+1})."""
+    c = np.cos(theta.astype(np.float64))[:, None, :]
+    s = np.sin(theta.astype(np.float64))[:, None, :]
+    x1, x2 = x[..., 0::2], x[..., 1::2]
+    y = np.empty_like(x)
+    y[..., 0::2] = x1 * c - x2 * s
+    y[..., 1::2] = x2 * c + x1 * s
+    return y
+
+
+def rope_apply(x_bits: np.ndarray, cu, base: float = 10000.0, rows=None, interleaved: bool = False) -> np.ndarray:
     """bf16 bits [T, H, d] -> rotated bf16 bits; ``rows`` restricts to those tokens."""
     pos = positions_from_cu(cu)
     if rows is not None:
         rows = np.asarray(rows, np.int64)
         pos, x_bits = pos[rows], x_bits[rows]
     theta = rope_angles(pos, x_bits.shape[-1], base)
-    return f64_to_bf16_bits(rotate_f64(bf16_bits_to_f64(x_bits), theta))
+    rot = rotate_interleaved_f64 if interleaved else rotate_f64
+    return f64_to_bf16_bits(rot(bf16_bits_to_f64(x_bits), theta))

@@ -128,3 +128,14 @@ def test_c_oracle_mutants_are_caught(tmp_path, old, new):
     assert err > 1e-6
     good = _build_c_mutant(tmp_path, "/* scores of the allowed keys", "/* scores of the allowed keys", "unmutated")
     assert np.abs(_run_c(good, q, k, v, cu) - ref).max() < 1e-12
+
+
+def test_interleaved_pair_swap_is_caught():
+    bad = _mutate(R, "rotate_interleaved_f64", "x1, x2 = x[..., 0::2], x[..., 1::2]",
+                  "x1, x2 = x[..., 1::2], x[..., 0::2]")
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((3, 2, 16))
+    theta = rng.uniform(-5, 5, (3, 8)).astype(np.float32)
+    z = (x[..., 0::2] + 1j * x[..., 1::2]) * np.exp(1j * theta.astype(np.float64))[:, None, :]
+    assert np.abs(bad(x, theta)[..., 0::2] - z.real).max() > 1e-3
+    assert np.abs(R.rotate_interleaved_f64(x, theta)[..., 0::2] - z.real).max() < 1e-13

@@ -120,3 +120,44 @@ def test_shift_invariance(c):
         a = R.rotate_f64(q, ((m + c) * f)[None]).ravel() @ R.rotate_f64(k, ((n + c) * f)[None]).ravel()
         b = q.ravel() @ R.rotate_f64(k, ((n - m) * f)[None]).ravel()
         assert abs(a - b) <= 1e-9 * max(1.0, abs(b))
+
+
+def test_interleaved_matches_complex_multiplication():
+    """Interleaved pair (x_{2j}, x_{2j+1}) as x_{2j} + i x_{2j+1}, turned by
+    e^{i theta_j} (the RoFormer complex form)."""
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((5, 3, 16))
+    theta = rng.uniform(-50, 50, (5, 8)).astype(np.float32)
+    y = R.rotate_interleaved_f64(x, theta)
+    z = (x[..., 0::2] + 1j * x[..., 1::2]) * np.exp(1j * theta.astype(np.float64))[:, None, :]
+    np.testing.assert_allclose(y[..., 0::2], z.real, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(y[..., 1::2], z.imag, rtol=0, atol=1e-13)
+
+
+def test_interleaved_is_rotate_half_under_a_permutation():
+    """Moving element 2j to j and 2j+1 to j + d/2 turns the interleaved pairing
+    into the rotate-half one: interleaved(x) = P^-1 rotate_half(P x)."""
+    w = make_workload("sft", scale="small")
+    x = qkv_bits(w, "k")
+    d = x.shape[-1]
+    perm = np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)])     # new index -> old index
+    cu = P.pack_build(w.lengths)["cu_seqlens"]
+    a = R.rope_apply(x, cu, interleaved=True)
+    b = R.rope_apply(np.ascontiguousarray(x[..., perm]), cu)
+    inv = np.argsort(perm)
+    assert (a == b[..., inv]).all()
+    assert (a != R.rope_apply(x, cu)).any()
+    starts = cu[:-1]
+    assert (a[starts] == x[starts]).all()          # p = 0 stays the identity
+
+
+def test_interleaved_shift_invariance():
+    rng = np.random.default_rng(5)
+    d = 32
+    f = R.rope_freqs(d).astype(np.float64)
+    q, k = rng.standard_normal((1, 1, d)), rng.standard_normal((1, 1, d))
+    for m, n, c in [(0, 0, 9), (3, 1, 100), (17, 40, 5)]:
+        rot = R.rotate_interleaved_f64
+        a = rot(q, ((m + c) * f)[None]).ravel() @ rot(k, ((n + c) * f)[None]).ravel()
+        b = q.ravel() @ rot(k, ((n - m) * f)[None]).ravel()
+        assert abs(a - b) <= 1e-9 * max(1.0, abs(b))
