@@ -172,6 +172,16 @@ pvc_status pvc_rope_thd_apply(const void* q_in, void* q_out, const void* k_in, v
                               const int32_t* cu_seqlens, int32_t nseg, float base,
                               uint32_t* dev_error, void* stream);
 
+/* pvc_rope_thd_apply with the interleaved pairing (x_{2j}, x_{2j+1}) of the
+ * RoFormer construction that [charlestar] "positions and RoPE" cites, in place
+ * of rotate-half: y_{2j} = x_{2j} cos - x_{2j+1} sin, y_{2j+1} = x_{2j+1} cos +
+ * x_{2j} sin, theta_j = fp32(p) * f_j as above.  Same arguments, precision,
+ * alignment rules and errors. */
+pvc_status pvc_rope_thd_apply_interleaved(const void* q_in, void* q_out, const void* k_in, void* k_out,
+                                          int64_t total_tokens, int32_t heads, int32_t head_dim,
+                                          const int32_t* cu_seqlens, int32_t nseg, float base,
+                                          uint32_t* dev_error, void* stream);
+
 /* ------------------------------------------------------- attention */
 
 /* Output element types of the attention entry points. */

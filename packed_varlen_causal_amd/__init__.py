@@ -64,6 +64,7 @@ def _load() -> ctypes.CDLL:
         "pvc_pack_build": ([P, P, P, I32, I64, I32, P, P, P, P, P, P, P, P, P, SZ, P], I32),
         "pvc_validate_cu_seqlens": ([P, I32, I64, I32, P, P, P], I32),
         "pvc_rope_thd_apply": ([P, P, P, P, I64, I32, I32, P, I32, F32, P, P], I32),
+        "pvc_rope_thd_apply_interleaved": ([P, P, P, P, I64, I32, I32, P, I32, F32, P, P], I32),
         "pvc_attn_workspace_size": ([I64, I32], SZ),
         "pvc_attn_plan": ([P, I32, I64, I32, I32, P, SZ, P, P], I32),
         "pvc_varlen_attn_fwd_planned": ([P, P, P, P, P, I64, I32, I32, I32, I32, P, SZ, P, P], I32),
@@ -204,8 +205,9 @@ def validate_cu_seqlens(cu_seqlens: torch.Tensor, total_tokens: int, max_seqlen:
 def rope_thd_apply(q: torch.Tensor, k: torch.Tensor | None, cu_seqlens: torch.Tensor,
                    base: float = 10000.0, q_out: torch.Tensor | None = None,
                    k_out: torch.Tensor | None = None, dev_error: torch.Tensor | None = None,
-                   stream=None):
-    """Per-segment RoPE on bf16 [T, H, d] q (and k).  In place unless outputs are given."""
+                   stream=None, interleaved: bool = False):
+    """Per-segment RoPE on bf16 [T, H, d] q (and k).  In place unless outputs are given.
+    Rotate-half pairing, or (x_2j, x_2j+1) pairs with ``interleaved=True``."""
     _require(q, "q", torch.bfloat16, 3)
     _require(cu_seqlens, "cu_seqlens", torch.int32, 1)
     T, H, D = q.shape
@@ -219,8 +221,11 @@ def rope_thd_apply(q: torch.Tensor, k: torch.Tensor | None, cu_seqlens: torch.Te
             raise ValueError("k must have q's shape")
         k_out = k if k_out is None else k_out
         _require(k_out, "k_out", torch.bfloat16, 3)
+        if k_out.shape != q.shape:
+            raise ValueError("k_out must match k")
     err = dev_error
-    st = _lib.pvc_rope_thd_apply(_ptr(q), _ptr(q_out), _ptr(k), _ptr(k_out if k is not None else None),
+    fn = _lib.pvc_rope_thd_apply_interleaved if interleaved else _lib.pvc_rope_thd_apply
+    st = fn(_ptr(q), _ptr(q_out), _ptr(k), _ptr(k_out if k is not None else None),
                                  T, H, D, _ptr(cu_seqlens), cu_seqlens.numel() - 1, float(base),
                                  _ptr(err), _stream(stream))
     _check(st, "rope_thd_apply")

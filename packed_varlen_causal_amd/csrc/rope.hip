@@ -3,7 +3,8 @@
 // [charlestar] "nine tokens, three identities": p_i = i - cu_r; [opworld]
 // "pitfall two": reset positions per document).
 //
-// Rotate-half pairing (j, j + d/2), angle theta_j = fp32(p) * f_j with the fp32
+// Rotate-half pairing (j, j + d/2), or with the interleaved flag the pairing
+// (2j, 2j + 1) of the RoFormer construction; angle theta_j = fp32(p) * f_j with the fp32
 // frequency table f_j = base^(-2j/d) computed on the host in double.  The angle
 // stays that one fp32 product; sin, cos and the rotation are evaluated in
 // double and the result is rounded once to bf16.  fp32 rotation would lose
@@ -17,7 +18,8 @@
 // bits the pair equals one direct round-to-nearest-even of the double.
 //
 // Work layout: one thread owns one token, eight consecutive pairs (16 bytes of
-// each half-row) and kHeadsPerThread heads of q and of k.  It evaluates its
+// each half-row; interleaved: four pairs, one 16-byte piece) and
+// kHeadsPerThread heads of q and of k.  It evaluates its
 // eight sin/cos pairs once and streams the heads; the d/16 threads of a token
 // together read and write whole 2*d-byte head rows, so every access is a
 // coalesced 16-byte vector.  The kernel moves 2 B in + 2 B out per element and
@@ -73,12 +75,27 @@ __device__ inline void rotate8(const u32x4& a, const u32x4& b, const double* c, 
     }
 }
 
+// Interleaved pairs: a holds x_{2j} .. x_{2j+7} (pairs j .. j+3, one per dword).
+__device__ inline u32x4 rotate4_interleaved(const u32x4& a, const double* c, const double* s) {
+    u32x4 y;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const double x1 = (double)bf16_to_f32(uint16_t(a[w]));
+        const double x2 = (double)bf16_to_f32(uint16_t(a[w] >> 16));
+        y[w] = f64_to_bf16_bits(x1 * c[w] - x2 * s[w]) | (f64_to_bf16_bits(x2 * c[w] + x1 * s[w]) << 16);
+    }
+    return y;
+}
+
 // head_dim a multiple of 16: vectorized path.
+template <bool INTERLEAVED>
 __global__ __launch_bounds__(kRopeThreads) void rope_vec_kernel(
         const uint16_t* q_in, uint16_t* q_out, const uint16_t* k_in, uint16_t* k_out, int64_t T,
         int32_t H, int32_t D, const int32_t* __restrict__ cu, int32_t nseg, RopeFreqs freqs,
         uint32_t* dev_error) {
-    const int chunks = D >> 4;                        // 8-pair chunks per head row
+    // 16-byte pieces a thread owns per head row: two 8-pair halves (rotate-half)
+    // or one 4-pair piece (interleaved)
+    const int chunks = INTERLEAVED ? D >> 3 : D >> 4;
     const int hgroups = (H + kHeadsPerThread - 1) / kHeadsPerThread;
     const int64_t gid = (int64_t)blockIdx.x * kRopeThreads + threadIdx.x;
     const int64_t per_token = (int64_t)chunks * hgroups;
@@ -94,10 +111,11 @@ __global__ __launch_bounds__(kRopeThreads) void rope_vec_kernel(
     if (!ok && ch == 0 && hg == 0) raise_error(dev_error, i >= en ? PVC_DEV_TOTAL : PVC_DEV_NOT_INCREASING);
     const float p = ok ? (float)(i - st) : 0.0f;     // malformed cu: identity (copy through)
 
-    double c[8], s[8];
-    const int j0 = ch * 8;
+    constexpr int NP = INTERLEAVED ? 4 : 8;           // pairs per thread
+    double c[NP], s[NP];
+    const int j0 = ch * NP;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < NP; ++e) {
         const float theta = p * freqs.f[j0 + e];      // one fp32 product
         sincos((double)theta, &s[e], &c[e]);
     }
@@ -111,17 +129,23 @@ __global__ __launch_bounds__(kRopeThreads) void rope_vec_kernel(
         if (src == nullptr) break;
         for (int h = h_lo; h < h_hi; ++h) {
             const int64_t row = (i * H + h) * (int64_t)D;
-            const u32x4 a = *reinterpret_cast<const u32x4*>(src + row + j0);
-            const u32x4 b = *reinterpret_cast<const u32x4*>(src + row + half + j0);
-            u32x4 ya, yb;
-            rotate8(a, b, c, s, ya, yb);
-            *reinterpret_cast<u32x4*>(dst + row + j0) = ya;
-            *reinterpret_cast<u32x4*>(dst + row + half + j0) = yb;
+            if constexpr (INTERLEAVED) {
+                const u32x4 a = *reinterpret_cast<const u32x4*>(src + row + 2 * j0);
+                *reinterpret_cast<u32x4*>(dst + row + 2 * j0) = rotate4_interleaved(a, c, s);
+            } else {
+                const u32x4 a = *reinterpret_cast<const u32x4*>(src + row + j0);
+                const u32x4 b = *reinterpret_cast<const u32x4*>(src + row + half + j0);
+                u32x4 ya, yb;
+                rotate8(a, b, c, s, ya, yb);
+                *reinterpret_cast<u32x4*>(dst + row + j0) = ya;
+                *reinterpret_cast<u32x4*>(dst + row + half + j0) = yb;
+            }
         }
     }
 }
 
 // Any even head_dim: one thread per (token, pair), heads looped.
+template <bool INTERLEAVED>
 __global__ __launch_bounds__(kRopeThreads) void rope_scalar_kernel(
         const uint16_t* q_in, uint16_t* q_out, const uint16_t* k_in, uint16_t* k_out, int64_t T,
         int32_t H, int32_t D, const int32_t* __restrict__ cu, int32_t nseg, RopeFreqs freqs,
@@ -145,10 +169,12 @@ __global__ __launch_bounds__(kRopeThreads) void rope_scalar_kernel(
         if (src == nullptr) break;
         for (int h = 0; h < H; ++h) {
             const int64_t row = (i * H + h) * (int64_t)D;
-            const double x1 = (double)bf16_to_f32(src[row + j]);
-            const double x2 = (double)bf16_to_f32(src[row + half + j]);
-            dst[row + j] = (uint16_t)f64_to_bf16_bits(x1 * cs - x2 * sn);
-            dst[row + half + j] = (uint16_t)f64_to_bf16_bits(x2 * cs + x1 * sn);
+            const int64_t e1 = INTERLEAVED ? row + 2 * j : row + j;
+            const int64_t e2 = INTERLEAVED ? row + 2 * j + 1 : row + half + j;
+            const double x1 = (double)bf16_to_f32(src[e1]);
+            const double x2 = (double)bf16_to_f32(src[e2]);
+            dst[e1] = (uint16_t)f64_to_bf16_bits(x1 * cs - x2 * sn);
+            dst[e2] = (uint16_t)f64_to_bf16_bits(x2 * cs + x1 * sn);
         }
     }
 }
@@ -158,10 +184,11 @@ __global__ __launch_bounds__(kRopeThreads) void rope_scalar_kernel(
 
 using namespace pvc;
 
-extern "C" pvc_status pvc_rope_thd_apply(const void* q_in, void* q_out, const void* k_in, void* k_out,
-                                         int64_t total_tokens, int32_t heads, int32_t head_dim,
-                                         const int32_t* cu_seqlens, int32_t nseg, float base,
-                                         uint32_t* dev_error, void* stream) {
+namespace {
+
+pvc_status rope_apply(const void* q_in, void* q_out, const void* k_in, void* k_out, int64_t total_tokens,
+                      int32_t heads, int32_t head_dim, const int32_t* cu_seqlens, int32_t nseg, float base,
+                      bool interleaved, uint32_t* dev_error, void* stream) {
     if (q_in == nullptr || q_out == nullptr || cu_seqlens == nullptr) return PVC_ERR_NULL;
     if ((k_in == nullptr) != (k_out == nullptr)) return PVC_ERR_NULL;
     if (total_tokens < 1 || total_tokens > 0x7fffffffLL || heads < 1 || nseg < 1)
@@ -181,15 +208,41 @@ extern "C" pvc_status pvc_rope_thd_apply(const void* q_in, void* q_out, const vo
                            reinterpret_cast<uintptr_t>(k_in) | reinterpret_cast<uintptr_t>(k_out)) & 15u) == 0;
     if (head_dim % 16 == 0 && aligned) {
         const int64_t hgroups = (heads + kHeadsPerThread - 1) / kHeadsPerThread;
-        const int64_t threads = total_tokens * (head_dim / 16) * hgroups;
+        const int64_t threads = total_tokens * (head_dim / (interleaved ? 8 : 16)) * hgroups;
         const int64_t nblk = (threads + kRopeThreads - 1) / kRopeThreads;
-        hipLaunchKernelGGL(rope_vec_kernel, dim3((unsigned)nblk), dim3(kRopeThreads), 0, s, qi, qo, ki,
-                           ko, total_tokens, heads, head_dim, cu_seqlens, nseg, freqs, dev_error);
+        if (interleaved)
+            hipLaunchKernelGGL(rope_vec_kernel<true>, dim3((unsigned)nblk), dim3(kRopeThreads), 0, s, qi, qo, ki,
+                               ko, total_tokens, heads, head_dim, cu_seqlens, nseg, freqs, dev_error);
+        else
+            hipLaunchKernelGGL(rope_vec_kernel<false>, dim3((unsigned)nblk), dim3(kRopeThreads), 0, s, qi, qo,
+                               ki, ko, total_tokens, heads, head_dim, cu_seqlens, nseg, freqs, dev_error);
     } else {
         const int64_t threads = total_tokens * (head_dim / 2);
         const int64_t nblk = (threads + kRopeThreads - 1) / kRopeThreads;
-        hipLaunchKernelGGL(rope_scalar_kernel, dim3((unsigned)nblk), dim3(kRopeThreads), 0, s, qi, qo,
-                           ki, ko, total_tokens, heads, head_dim, cu_seqlens, nseg, freqs, dev_error);
+        if (interleaved)
+            hipLaunchKernelGGL(rope_scalar_kernel<true>, dim3((unsigned)nblk), dim3(kRopeThreads), 0, s, qi, qo,
+                               ki, ko, total_tokens, heads, head_dim, cu_seqlens, nseg, freqs, dev_error);
+        else
+            hipLaunchKernelGGL(rope_scalar_kernel<false>, dim3((unsigned)nblk), dim3(kRopeThreads), 0, s, qi,
+                               qo, ki, ko, total_tokens, heads, head_dim, cu_seqlens, nseg, freqs, dev_error);
     }
     return launch_status();
+}
+
+}  // namespace
+
+extern "C" pvc_status pvc_rope_thd_apply(const void* q_in, void* q_out, const void* k_in, void* k_out,
+                                         int64_t total_tokens, int32_t heads, int32_t head_dim,
+                                         const int32_t* cu_seqlens, int32_t nseg, float base,
+                                         uint32_t* dev_error, void* stream) {
+    return rope_apply(q_in, q_out, k_in, k_out, total_tokens, heads, head_dim, cu_seqlens, nseg, base, false,
+                      dev_error, stream);
+}
+
+extern "C" pvc_status pvc_rope_thd_apply_interleaved(const void* q_in, void* q_out, const void* k_in,
+                                                     void* k_out, int64_t total_tokens, int32_t heads,
+                                                     int32_t head_dim, const int32_t* cu_seqlens, int32_t nseg,
+                                                     float base, uint32_t* dev_error, void* stream) {
+    return rope_apply(q_in, q_out, k_in, k_out, total_tokens, heads, head_dim, cu_seqlens, nseg, base, true,
+                      dev_error, stream);
 }

@@ -29,16 +29,20 @@ def _ulp_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return np.abs(key(a) - key(b))
 
 
-def _near_tie(x_bits: np.ndarray, positions, base: float) -> np.ndarray:
+def _near_tie(x_bits: np.ndarray, positions, base: float, interleaved: bool = False) -> np.ndarray:
     """Elements whose exact rotated value lies so close to a bf16 rounding
     midpoint that two correct double evaluations may round to different
     neighbours: distance to the midpoint below the double evaluation's error
     bound, 8 * 2^-53 * (|x_j| + |x_{j+d/2}|), measured in bf16 ulps."""
     d = x_bits.shape[-1]
     x = R.bf16_bits_to_f64(x_bits)
-    y = R.rotate_f64(x, R.rope_angles(positions, d, base))
-    mag = np.abs(x[..., : d // 2]) + np.abs(x[..., d // 2:])
-    mag = np.concatenate([mag, mag], axis=-1)
+    if interleaved:
+        y = R.rotate_interleaved_f64(x, R.rope_angles(positions, d, base))
+        mag = np.repeat(np.abs(x[..., 0::2]) + np.abs(x[..., 1::2]), 2, axis=-1)
+    else:
+        y = R.rotate_f64(x, R.rope_angles(positions, d, base))
+        mag = np.abs(x[..., : d // 2]) + np.abs(x[..., d // 2:])
+        mag = np.concatenate([mag, mag], axis=-1)
     ay = np.abs(y)
     e = np.floor(np.log2(np.where(ay > 0, ay, 1.0)))
     ulp = np.exp2(e - 7)
@@ -47,10 +51,11 @@ def _near_tie(x_bits: np.ndarray, positions, base: float) -> np.ndarray:
     return np.abs(frac - 0.5) <= tol
 
 
-def _check(got_bits, ref_bits, what, x_bits=None, positions=None, base=10000.0):
+def _check(got_bits, ref_bits, what, x_bits=None, positions=None, base=10000.0, interleaved=False):
     """Bit-exact except near-tie elements (at most one ulp there)."""
     d = _ulp_diff(got_bits, ref_bits)
-    near = _near_tie(x_bits, positions, base) if x_bits is not None else np.zeros(d.shape, bool)
+    near = (_near_tie(x_bits, positions, base, interleaved) if x_bits is not None
+            else np.zeros(d.shape, bool))
     say(f"    {what}: {int((d > 0).sum())} of {d.size} elements differ (max {int(d.max())} ulp); "
         f"near-tie elements {int(near.sum())}")
     assert d.max() <= 1, what
@@ -144,3 +149,46 @@ def test_malformed_cu_sets_bits_and_copies(pvc):
     torch.cuda.synchronize()
     assert int(err.item()) & P.ERR_TOTAL
     assert (host_bits(qd)[7:] == q[7:]).all()
+
+
+@pytest.mark.parametrize("name", CONFIG_NAMES)
+def test_interleaved_small_workloads_all_tokens(pvc, name):
+    w = make_workload(name, scale="small")
+    say(f"  rope interleaved small {name}: T={w.total_tokens} H={w.heads} d={w.head_dim}")
+    q, k = qkv_bits(w, "q"), qkv_bits(w, "k")
+    cu = P.pack_build(w.lengths)["cu_seqlens"]
+    qd, kd = dev_bf16(q), dev_bf16(k)
+    pvc.rope_thd_apply(qd, kd, dev_i32(cu), w.rope_base, interleaved=True)
+    torch.cuda.synchronize()
+    pos = P.positions_from_cu(cu)
+    for got, x, what in ((host_bits(qd), q, "q"), (host_bits(kd), k, "k")):
+        _check(got, R.rope_apply(x, cu, w.rope_base, interleaved=True), what, x, pos, w.rope_base, True)
+        assert (got[cu[:-1]] == x[cu[:-1]]).all()
+
+
+@pytest.mark.parametrize("d", [8, 48, 96, 128])
+def test_interleaved_head_dims(pvc, d):
+    """d = 8: one pair per thread; d % 16 == 0: the vectorized four-pair path."""
+    lengths = [5, 17, 300, 1]
+    T = sum(lengths)
+    from workloads import f32_to_bf16_bits
+    q = f32_to_bf16_bits(np.random.default_rng(d + 1).standard_normal((T, 3, d), dtype=np.float32))
+    cu = P.pack_build(lengths)["cu_seqlens"]
+    qd = dev_bf16(q)
+    pvc.rope_thd_apply(qd, None, dev_i32(cu), 500.0, interleaved=True)
+    torch.cuda.synchronize()
+    _check(host_bits(qd), R.rope_apply(q, cu, 500.0, interleaved=True), f"interleaved d={d}", q,
+           P.positions_from_cu(cu), 500.0, True)
+
+
+def test_interleaved_full_size_sampled_tokens(pvc):
+    w = make_workload("sft")
+    q = qkv_bits(w, "q")
+    cu = P.pack_build(w.lengths)["cu_seqlens"]
+    qd = dev_bf16(q)
+    pvc.rope_thd_apply(qd, None, dev_i32(cu), w.rope_base, interleaved=True)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([cu[:-1], cu[1:] - 1, np.random.default_rng(2).integers(0, w.total_tokens, 3000)]))
+    pos = P.positions_from_cu(cu)[rows]
+    _check(host_bits(qd)[rows], R.rope_apply(q, cu, w.rope_base, rows=rows, interleaved=True),
+           "interleaved q sampled", q[rows], pos, w.rope_base, True)
