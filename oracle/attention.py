@@ -18,6 +18,17 @@ Three forms are provided:
   attention_unpacked  each segment run alone as one ordinary sequence
                    ([m020] "08": packed vs per-sample execution;
                    [charlestar] "change A, not B").
+the padded-storage form (Megatron's cu_seqlens_padded, which [vllbc] "five
+steps" names beside cu_seqlens: logical boundaries apart from storage
+offsets):
+  attention_padded / attention_bwd_padded  segment r's L_r tokens sit at
+                   storage rows [cu_padded[r], cu_padded[r] + L_r); the rest of
+                   its slot up to cu_padded[r+1] is padding that no row sees.
+                   Reading (the pages leave it open): real tokens at the start
+                   of their slot; a padding row has no keys, its output and
+                   gradients are 0 and its LSE is -inf;
+  allow_matrix_padded + attention_brute_masked  the same as an explicit
+                   storage x storage mask, for tiny T;
 and the gradients of that definition:
   attention_bwd    dQ, dK, dV for an upstream dO, per segment and head (the C
                    loop oracle_attn_bwd_segment; the softmax-Jacobian formulas
@@ -204,3 +215,80 @@ def attention_bwd(q, k, v, dout, cu, causal: bool = True, threads: int = 1, head
         with ThreadPoolExecutor(threads) as ex:
             list(ex.map(run, jobs))
     return dq, dk, dv
+
+
+def storage_rows(cu, cu_padded) -> np.ndarray:
+    """Storage row of every real token, in order: token t of segment r (the
+    (t - cu[r])-th of its segment) sits at cu_padded[r] + t - cu[r]."""
+    cu = np.asarray(cu, np.int64)
+    cp = np.asarray(cu_padded, np.int64)
+    out = []
+    for r in range(cu.shape[0] - 1):
+        out.extend(range(int(cp[r]), int(cp[r] + cu[r + 1] - cu[r])))
+    return np.asarray(out, np.int64)
+
+
+def attention_padded(q, k, v, cu, cu_padded, causal: bool = True, threads: int = 1):
+    """fp64 out [Ts, H, d] and lse [Ts, H] over storage rows (Ts = q.shape[0]);
+    real rows as ``attention`` on the compact buffer, padding rows 0 / -inf."""
+    idx = storage_rows(cu, cu_padded)
+    Ts, H, d = np.asarray(q).shape
+    o, ls = attention(np.asarray(q)[idx], np.asarray(k)[idx], np.asarray(v)[idx], cu, causal, threads)
+    out = np.zeros((Ts, H, d))
+    lse = np.full((Ts, H), -np.inf)
+    out[idx], lse[idx] = o, ls
+    return out, lse
+
+
+def attention_bwd_padded(q, k, v, dout, cu, cu_padded, causal: bool = True, threads: int = 1, heads=None,
+                         segments=None):
+    """Gradients over storage rows: real rows as ``attention_bwd`` on the
+    compact buffer, padding rows 0 (NaN outside ``heads`` / ``segments``)."""
+    idx = storage_rows(cu, cu_padded)
+    Ts = np.asarray(q).shape[0]
+    g = attention_bwd(np.asarray(q)[idx], np.asarray(k)[idx], np.asarray(v)[idx], np.asarray(dout)[idx], cu,
+                      causal, threads, heads, segments)
+    outs = []
+    for a in g:
+        full = np.zeros((Ts,) + a.shape[1:])
+        if heads is not None:
+            keep = np.zeros(a.shape[1], bool)
+            keep[list(heads)] = True
+            full[:, ~keep] = np.nan
+        full[idx] = a
+        outs.append(full)
+    return tuple(outs)
+
+
+def allow_matrix_padded(cu, cu_padded, total_rows: int, causal: bool = True) -> np.ndarray:
+    """bool [Ts, Ts] over storage rows: i and j real rows of the same slot, and
+    j <= i when causal; padding rows allow nothing."""
+    cu = np.asarray(cu, np.int64)
+    cp = np.asarray(cu_padded, np.int64)
+    slot = np.full(total_rows, -1)
+    for r in range(cu.shape[0] - 1):
+        slot[cp[r]:cp[r] + cu[r + 1] - cu[r]] = r
+    A = np.zeros((total_rows, total_rows), bool)
+    for i in range(total_rows):
+        for j in range(total_rows):
+            A[i, j] = slot[i] >= 0 and slot[i] == slot[j] and (j <= i or not causal)
+    return A
+
+
+def attention_brute_masked(q, k, v, allow):
+    """softmax(Q K^T / sqrt(d) + M) V for an explicit bool mask; a row that
+    allows nothing gets output 0 and LSE -inf.  fp64, tiny T."""
+    Q, K, V = (_as_f64(x) for x in (q, k, v))
+    T, H, d = Q.shape
+    allow = np.asarray(allow, bool)
+    M = np.where(allow, 0.0, -np.inf)
+    has = allow.any(axis=1)
+    out = np.zeros((T, H, d))
+    lse = np.full((T, H), -np.inf)
+    for h in range(H):
+        S = Q[has, h, :] @ K[:, h, :].T / np.sqrt(d) + M[has]
+        m = S.max(axis=1, keepdims=True)
+        E = np.exp(S - m)
+        out[has, h, :] = (E @ V[:, h, :]) / E.sum(axis=1, keepdims=True)
+        lse[has, h] = m[:, 0] + np.log(E.sum(axis=1))
+    return out, lse
