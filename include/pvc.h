@@ -78,8 +78,9 @@ enum {
                                      of [3,2,4] but moves b0 into A) */
     PVC_DEV_RANGE = 64u,          /* the sum of lengths does not fit in int32 */
     PVC_DEV_PLAN = 128u,          /* attention run with a plan built for other arguments */
-    PVC_DEV_LABEL = 256u          /* packed CE: a label outside [0, vocab) that is not
+    PVC_DEV_LABEL = 256u,         /* packed CE: a label outside [0, vocab) that is not
                                      the ignore index (the row is not a target) */
+    PVC_DEV_PADDED = 512u         /* cu_seqlens_padded: a slot shorter than its segment */
 };
 
 /* Static text for a status code (never NULL). */
@@ -191,12 +192,14 @@ enum { PVC_OUT_BF16 = 0, PVC_OUT_F32 = 1 };
 size_t pvc_attn_workspace_size(int64_t total_tokens, int32_t nseg);
 
 /*
- * Build the tile plan for one cu_seqlens: the list of work items (segment,
- * query tile, key range) that covers exactly the same-segment, on-or-below-
- * diagonal blocks ([charlestar] "EOS is content": allow(i,j) = same segment
- * and p_j <= p_i; [opworld] "pitfall one": cross-document blocks are pure
- * waste, which the varlen kernel never computes).  Items are ordered longest
- * first.  cu_seqlens is read on the device only; it is validated as
+ * Build the tile plan for one cu_seqlens: every row's key range (its
+ * segment), from which the attention kernels derive the same-segment,
+ * on-or-below-diagonal blocks they compute ([charlestar] "EOS is content":
+ * allow(i,j) = same segment and p_j <= p_i; [opworld] "pitfall one":
+ * cross-document blocks are pure waste, which the varlen kernel never
+ * computes).  Query tiles of 128 rows run segment by segment in buffer order,
+ * each segment's tiles from its end (the heaviest) to its start.
+ * cu_seqlens is read on the device only; it is validated as
  * pvc_validate_cu_seqlens would (without lengths) and an invalid cu yields an
  * empty plan plus the error bits.  The plan depends only on
  * (cu_seqlens, nseg, total_tokens, causal), so one plan serves every layer
@@ -205,6 +208,29 @@ size_t pvc_attn_workspace_size(int64_t total_tokens, int32_t nseg);
 pvc_status pvc_attn_plan(const int32_t* cu_seqlens, int32_t nseg, int64_t total_tokens,
                          int32_t max_seqlen, int32_t causal, void* workspace,
                          size_t workspace_bytes, uint32_t* dev_error, void* stream);
+
+/*
+ * The plan for padded storage: logical boundaries apart from storage offsets
+ * (the cu_seqlens_padded of Megatron's packed-sequence parameters that [vllbc]
+ * "five steps" describes).  Segment r has L_r = cu_seqlens[r+1] -
+ * cu_seqlens[r] tokens, stored at rows [cu_seqlens_padded[r],
+ * cu_seqlens_padded[r] + L_r) of its slot [cu_seqlens_padded[r],
+ * cu_seqlens_padded[r+1]); the rest of the slot is padding.  q, k, v and the
+ * outputs of the attention entry points are then [total_rows, heads, d] in
+ * that storage; a padding row attends to nothing and is attended by nothing:
+ * its output is 0, its LSE -inf, its gradients 0.  (RoPE needs no variant:
+ * pvc_rope_thd_apply with cu_seqlens_padded counts positions from each slot's
+ * start, which is right for the real tokens.)
+ * cu_seqlens_padded [nseg + 1] int32 on the device: cu_seqlens_padded[0] == 0
+ * (else PVC_DEV_CU0), each slot at least as long as its segment (else
+ * PVC_DEV_PADDED), cu_seqlens_padded[nseg] == total_rows (else PVC_DEV_TOTAL);
+ * cu_seqlens as for pvc_attn_plan except that its last entry is the number of
+ * real tokens.  The workspace is pvc_attn_workspace_size(total_rows, nseg).
+ * Use the plan with total_tokens = total_rows.
+ */
+pvc_status pvc_attn_plan_padded(const int32_t* cu_seqlens, const int32_t* cu_seqlens_padded, int32_t nseg,
+                                int64_t total_rows, int32_t max_seqlen, int32_t causal, void* workspace,
+                                size_t workspace_bytes, uint32_t* dev_error, void* stream);
 
 /*
  * Attention forward with an existing plan:

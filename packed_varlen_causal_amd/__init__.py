@@ -42,7 +42,7 @@ OK, ERR_NULL, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(6
 OUT_BF16, OUT_F32 = 0, 1
 DEV_ERROR_BITS = {
     1: "CU0", 2: "NOT_INCREASING", 4: "TOTAL", 8: "MAXSEQ", 16: "LENGTH",
-    32: "MISMATCH", 64: "RANGE", 128: "PLAN", 256: "LABEL",
+    32: "MISMATCH", 64: "RANGE", 128: "PLAN", 256: "LABEL", 512: "PADDED",
 }
 
 
@@ -67,6 +67,7 @@ def _load() -> ctypes.CDLL:
         "pvc_rope_thd_apply_interleaved": ([P, P, P, P, I64, I32, I32, P, I32, F32, P, P], I32),
         "pvc_attn_workspace_size": ([I64, I32], SZ),
         "pvc_attn_plan": ([P, I32, I64, I32, I32, P, SZ, P, P], I32),
+        "pvc_attn_plan_padded": ([P, P, I32, I64, I32, I32, P, SZ, P, P], I32),
         "pvc_varlen_attn_fwd_planned": ([P, P, P, P, P, I64, I32, I32, I32, I32, P, SZ, P, P], I32),
         "pvc_varlen_attn_fwd": ([P, P, P, P, P, P, I32, I64, I32, I32, I32, I32, I32, P, SZ, P, P], I32),
         "pvc_padded_attn_fwd_sbhd": ([P, P, P, P, P, I32, I32, I32, I32, I32, I32, P], I32),
@@ -239,11 +240,15 @@ def attn_workspace_size(total_tokens: int, nseg: int) -> int:
 
 
 class AttnPlan:
-    """Device tile plan for one cu_seqlens; reusable by every layer and head."""
+    """Device tile plan for one cu_seqlens; reusable by every layer and head.
+
+    With ``cu_seqlens_padded`` the buffers hold padded storage: segment r's
+    tokens at rows [cu_seqlens_padded[r], + L_r) and ``total_tokens`` is the
+    number of storage rows (see pvc_attn_plan_padded)."""
 
     def __init__(self, cu_seqlens: torch.Tensor, total_tokens: int, max_seqlen: int,
                  causal: bool = True, dev_error: torch.Tensor | None = None, stream=None,
-                 workspace: torch.Tensor | None = None):
+                 workspace: torch.Tensor | None = None, cu_seqlens_padded: torch.Tensor | None = None):
         _require(cu_seqlens, "cu_seqlens", torch.int32, 1)
         self.total_tokens = int(total_tokens)
         self.nseg = cu_seqlens.numel() - 1
@@ -256,9 +261,18 @@ class AttnPlan:
         elif workspace.numel() < self.ws_bytes:
             raise ValueError("workspace too small")
         self.workspace = workspace
-        st = _lib.pvc_attn_plan(_ptr(cu_seqlens), self.nseg, self.total_tokens, int(max_seqlen),
-                                int(self.causal), _ptr(workspace), self.ws_bytes, _ptr(self.dev_error),
-                                _stream(stream))
+        self.cu_seqlens_padded = cu_seqlens_padded
+        if cu_seqlens_padded is None:
+            st = _lib.pvc_attn_plan(_ptr(cu_seqlens), self.nseg, self.total_tokens, int(max_seqlen),
+                                    int(self.causal), _ptr(workspace), self.ws_bytes, _ptr(self.dev_error),
+                                    _stream(stream))
+        else:
+            _require(cu_seqlens_padded, "cu_seqlens_padded", torch.int32, 1)
+            if cu_seqlens_padded.numel() != cu_seqlens.numel():
+                raise ValueError("cu_seqlens_padded must have one entry per cu_seqlens entry")
+            st = _lib.pvc_attn_plan_padded(_ptr(cu_seqlens), _ptr(cu_seqlens_padded), self.nseg,
+                                           self.total_tokens, int(max_seqlen), int(self.causal), _ptr(workspace),
+                                           self.ws_bytes, _ptr(self.dev_error), _stream(stream))
         _check(st, "attn_plan")
 
 

@@ -67,9 +67,26 @@ __global__ __launch_bounds__(256) void plan_rows_kernel(const int32_t* __restric
     rows[i] = ok ? make_int2((int)st, (int)en) : make_int2((int)i, (int)(i + 1));
 }
 
+// Padded storage: segment r's L_r = cu[r+1] - cu[r] tokens sit at rows
+// [cu_p[r], cu_p[r] + L_r) of a slot that ends at cu_p[r+1]; the rest of the
+// slot is padding, whose rows get an empty key range {i, i} (no key, output 0).
+__global__ __launch_bounds__(256) void plan_rows_padded_kernel(const int32_t* __restrict__ cu,
+                                                               const int32_t* __restrict__ cu_p, int32_t nseg,
+                                                               int64_t T, int2* __restrict__ rows) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= T) return;
+    const int32_t r = upper_segment(cu_p, nseg, i);
+    const int64_t st = min<int64_t>(max<int64_t>(cu_p[r], 0), T);
+    const int64_t len = (int64_t)cu[r + 1] - cu[r];
+    const int64_t en = min<int64_t>(max<int64_t>(st + len, st), T);
+    const bool ok = st <= i && i < en;
+    rows[i] = ok ? make_int2((int)st, (int)en) : make_int2((int)i, (int)i);
+}
+
+// Validates cu (and, for padded storage, cu_p) and seals the plan header.
 __global__ __launch_bounds__(kCheckThreads) void plan_check_kernel(
-        const int32_t* __restrict__ cu, int32_t nseg, int64_t T, int32_t max_seqlen, int32_t causal,
-        int32_t* __restrict__ header, int32_t ntiles, uint32_t* dev_error) {
+        const int32_t* __restrict__ cu, const int32_t* __restrict__ cu_p, int32_t nseg, int64_t T,
+        int32_t max_seqlen, int32_t causal, int32_t* __restrict__ header, int32_t ntiles, uint32_t* dev_error) {
     __shared__ unsigned s_err;
     const int t = threadIdx.x;
     if (t == 0) s_err = 0;
@@ -80,10 +97,16 @@ __global__ __launch_bounds__(kCheckThreads) void plan_check_kernel(
         const int64_t a = cu[r], b = cu[r + 1];
         if (b <= a) err |= PVC_DEV_NOT_INCREASING;
         if (b - a > max_seqlen) err |= PVC_DEV_MAXSEQ;
+        if (cu_p != nullptr && (int64_t)cu_p[r + 1] - cu_p[r] < b - a) err |= PVC_DEV_PADDED;
     }
     if (t == 0) {
         if (cu[0] != 0) err |= PVC_DEV_CU0;
-        if ((int64_t)cu[nseg] != T) err |= PVC_DEV_TOTAL;
+        if (cu_p == nullptr) {
+            if ((int64_t)cu[nseg] != T) err |= PVC_DEV_TOTAL;
+        } else {
+            if (cu_p[0] != 0) err |= PVC_DEV_CU0;
+            if ((int64_t)cu_p[nseg] != T) err |= PVC_DEV_TOTAL;
+        }
     }
     if (err) atomicOr(&s_err, err);
     __syncthreads();
@@ -472,7 +495,7 @@ void attn_fwd_kernel(AttnParams p) {
     // ---- epilogue: lane (c, g) holds O^T rows d = 32j + 8(r/4) + 4g + r%4
     if (!plan_ok) return;                                  // uniform: nothing was computed
     const float l = lane_pair_sum(l_run);
-    const float inv = 1.0f / l;
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;          // a padding row has no key: output 0
     const bool row_ok = wave_active && wr0 + c < r1;
     if constexpr (OUT_F32) {
         if (row_ok) {
@@ -576,8 +599,28 @@ extern "C" pvc_status pvc_attn_plan(const int32_t* cu_seqlens, int32_t nseg, int
     const int64_t nblk = (total_tokens + 255) / 256;
     hipLaunchKernelGGL(plan_rows_kernel, dim3((unsigned)nblk), dim3(256), 0, s, cu_seqlens, nseg,
                        total_tokens, rows);
-    hipLaunchKernelGGL(plan_check_kernel, dim3(1), dim3(kCheckThreads), 0, s, cu_seqlens, nseg,
+    hipLaunchKernelGGL(plan_check_kernel, dim3(1), dim3(kCheckThreads), 0, s, cu_seqlens, nullptr, nseg,
                        total_tokens, max_seqlen, causal ? 1 : 0, header, (int32_t)L.ntiles, dev_error);
+    return launch_status();
+}
+
+extern "C" pvc_status pvc_attn_plan_padded(const int32_t* cu_seqlens, const int32_t* cu_seqlens_padded,
+                                           int32_t nseg, int64_t total_rows, int32_t max_seqlen, int32_t causal,
+                                           void* workspace, size_t workspace_bytes, uint32_t* dev_error,
+                                           void* stream) {
+    if (cu_seqlens == nullptr || cu_seqlens_padded == nullptr || workspace == nullptr) return PVC_ERR_NULL;
+    if (nseg < 1 || total_rows < 1 || total_rows > 0x7fffffffLL || max_seqlen < 1) return PVC_ERR_INVALID_ARG;
+    const PlanLayout L = plan_layout(total_rows);
+    if (workspace_bytes < L.total) return PVC_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    auto* header = reinterpret_cast<int32_t*>(ws + L.header);
+    auto* rows = reinterpret_cast<int2*>(ws + L.rows);
+    hipStream_t s = as_stream(stream);
+    const int64_t nblk = (total_rows + 255) / 256;
+    hipLaunchKernelGGL(plan_rows_padded_kernel, dim3((unsigned)nblk), dim3(256), 0, s, cu_seqlens,
+                       cu_seqlens_padded, nseg, total_rows, rows);
+    hipLaunchKernelGGL(plan_check_kernel, dim3(1), dim3(kCheckThreads), 0, s, cu_seqlens, cu_seqlens_padded,
+                       nseg, total_rows, max_seqlen, causal ? 1 : 0, header, (int32_t)L.ntiles, dev_error);
     return launch_status();
 }
 

@@ -117,7 +117,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     if (part == 0 && t < Tp) {
-        scratch[(int64_t)h * Tp + t] = t < T ? lse[(int64_t)h * T + t] * kLog2e : 0.0f;
+        // a padding row (no key: LSE -inf) gets +inf, so its recomputed
+        // probabilities exp2(s - lse) are 0 rather than NaN
+        const float l = t < T ? lse[(int64_t)h * T + t] : 0.0f;
+        scratch[(int64_t)h * Tp + t] = l == -INFINITY ? INFINITY : l * kLog2e;
         scratch[((int64_t)H + h) * Tp + t] = t < T ? acc : 0.0f;
     }
 }
