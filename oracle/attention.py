@@ -29,6 +29,19 @@ offsets):
                    gradients are 0 and its LSE is -inf;
   allow_matrix_padded + attention_brute_masked  the same as an explicit
                    storage x storage mask, for tiny T;
+the inference-prefill form ([m020] "07 train vs infer": independent requests
+through a varlen kernel, each with its own KV):
+  attention_qk     separate query and key boundaries cu_q / cu_k (request r
+                   has Lq_r queries over Lk_r keys, e.g. a cached prefix plus
+                   the new tokens) and grouped key/value heads (query head h
+                   reads kv head h // (H / Hkv)).  Causal alignment (a
+                   reading: [charlestar] "varlen interface" warns that the
+                   equal-length lower triangle does not carry over to
+                   non-square Q/K and leaves the convention to the library
+                   version): bottom-right, query a of a request sees keys
+                   b <= a + Lk - Lq, so its last query sees every key and
+                   Lq = Lk is the ordinary causal mask.  A query that sees no
+                   key outputs 0 with LSE -inf;
 and the gradients of that definition:
   attention_bwd    dQ, dK, dV for an upstream dO, per segment and head (the C
                    loop oracle_attn_bwd_segment; the softmax-Jacobian formulas
@@ -291,4 +304,33 @@ def attention_brute_masked(q, k, v, allow):
         E = np.exp(S - m)
         out[has, h, :] = (E @ V[:, h, :]) / E.sum(axis=1, keepdims=True)
         lse[has, h] = m[:, 0] + np.log(E.sum(axis=1))
+    return out, lse
+
+
+def attention_qk(q, k, v, cu_q, cu_k, causal: bool = True):
+    """fp64 out [Tq, H, d], lse [Tq, H] for q [Tq, H, d] over k, v [Tk, Hkv, d]
+    (H a multiple of Hkv), request r = queries [cu_q[r], cu_q[r+1]) over keys
+    [cu_k[r], cu_k[r+1]); plain per request and head."""
+    Q, K, V = (_as_f64(x) for x in (q, k, v))
+    Tq, H, d = Q.shape
+    Hkv = K.shape[1]
+    group = H // Hkv
+    cu_q = np.asarray(cu_q, np.int64)
+    cu_k = np.asarray(cu_k, np.int64)
+    out = np.zeros((Tq, H, d))
+    lse = np.full((Tq, H), -np.inf)
+    for r in range(cu_q.shape[0] - 1):
+        qs, qe, ks, ke = int(cu_q[r]), int(cu_q[r + 1]), int(cu_k[r]), int(cu_k[r + 1])
+        Lq, Lk = qe - qs, ke - ks
+        for a in range(Lq):
+            nvis = min(Lk, a + Lk - Lq + 1) if causal else Lk      # keys 0 .. nvis-1
+            if nvis <= 0:
+                continue
+            for h in range(H):
+                hk = h // group
+                sc = K[ks:ks + nvis, hk, :] @ Q[qs + a, h, :] / np.sqrt(d)
+                m = sc.max()
+                e = np.exp(sc - m)
+                out[qs + a, h, :] = e @ V[ks:ks + nvis, hk, :] / e.sum()
+                lse[qs + a, h] = m + np.log(e.sum())
     return out, lse
