@@ -233,6 +233,44 @@ pvc_status pvc_attn_plan_padded(const int32_t* cu_seqlens, const int32_t* cu_seq
                                 size_t workspace_bytes, uint32_t* dev_error, void* stream);
 
 /*
+ * The plan for separate query and key boundaries: an inference prefill of
+ * independent requests, each with its own keys ([m020] "07 train vs infer":
+ * variable-length kernels organise the requests; every request keeps its own
+ * KV).  Request r has queries [cu_seqlens_q[r], cu_seqlens_q[r+1]) and keys
+ * [cu_seqlens_k[r], cu_seqlens_k[r+1]) (a cached prefix plus its new tokens,
+ * for example).  Causal alignment is bottom-right: query a of a request sees
+ * keys b <= a + Lk - Lq, so its last query sees every key and Lq == Lk is the
+ * ordinary causal mask ([charlestar] "varlen interface" notes that
+ * non-square alignment is a separate convention; this is the reading taken).
+ * A query that sees no key outputs 0 with LSE -inf.  Both cu arrays
+ * [nseg + 1] int32 on the device, strictly increasing from 0 to total_q /
+ * total_k, segments at most max_seqlen_q / max_seqlen_k (else the usual error
+ * bits and an empty plan).  Workspace pvc_attn_workspace_size(total_q, nseg).
+ * Query tiles run in buffer order.  Used by pvc_varlen_attn_fwd_qk_planned
+ * only (a forward: the backward entry refuses this plan).
+ */
+pvc_status pvc_attn_plan_qk(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t nseg,
+                            int64_t total_q, int64_t total_k, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                            int32_t causal, void* workspace, size_t workspace_bytes, uint32_t* dev_error,
+                            void* stream);
+
+/*
+ * Attention forward over a plan of pvc_attn_plan_qk, with grouped key /
+ * value heads: q and out [total_q, heads, head_dim], k and v
+ * [total_k, kv_heads, head_dim] (bf16, contiguous, 16-byte aligned); query
+ * head h reads key / value head h / (heads / kv_heads); heads a multiple of
+ * kv_heads.  causal must be the plan's.  lse [heads, total_q] fp32 (natural
+ * log), nullable.  out_dtype, head_dim and the errors as for
+ * pvc_varlen_attn_fwd_planned; a plan built for other arguments sets
+ * PVC_DEV_PLAN and nothing is written.
+ */
+pvc_status pvc_varlen_attn_fwd_qk_planned(const void* q, const void* k, const void* v, void* out, float* lse,
+                                          int64_t total_q, int64_t total_k, int32_t heads, int32_t kv_heads,
+                                          int32_t head_dim, int32_t causal, int32_t out_dtype,
+                                          const void* workspace, size_t workspace_bytes, uint32_t* dev_error,
+                                          void* stream);
+
+/*
  * Attention forward with an existing plan:
  *   out[i,h,:] = sum_j softmax_j(q_i.k_j / sqrt(head_dim) + M_ij) v_j
  * with M_ij = 0 where segment(i) == segment(j) and (j <= i or !causal), -inf

@@ -307,10 +307,11 @@ def attention_brute_masked(q, k, v, allow):
     return out, lse
 
 
-def attention_qk(q, k, v, cu_q, cu_k, causal: bool = True):
+def attention_qk(q, k, v, cu_q, cu_k, causal: bool = True, rows=None):
     """fp64 out [Tq, H, d], lse [Tq, H] for q [Tq, H, d] over k, v [Tk, Hkv, d]
     (H a multiple of Hkv), request r = queries [cu_q[r], cu_q[r+1]) over keys
-    [cu_k[r], cu_k[r+1]); plain per request and head."""
+    [cu_k[r], cu_k[r+1]); plain per request and head.  ``rows``: compute only
+    those query rows (the others stay 0 / -inf)."""
     Q, K, V = (_as_f64(x) for x in (q, k, v))
     Tq, H, d = Q.shape
     Hkv = K.shape[1]
@@ -319,10 +320,13 @@ def attention_qk(q, k, v, cu_q, cu_k, causal: bool = True):
     cu_k = np.asarray(cu_k, np.int64)
     out = np.zeros((Tq, H, d))
     lse = np.full((Tq, H), -np.inf)
+    rowset = None if rows is None else {int(x) for x in rows}
     for r in range(cu_q.shape[0] - 1):
         qs, qe, ks, ke = int(cu_q[r]), int(cu_q[r + 1]), int(cu_k[r]), int(cu_k[r + 1])
         Lq, Lk = qe - qs, ke - ks
         for a in range(Lq):
+            if rowset is not None and (qs + a) not in rowset:
+                continue
             nvis = min(Lk, a + Lk - Lq + 1) if causal else Lk      # keys 0 .. nvis-1
             if nvis <= 0:
                 continue

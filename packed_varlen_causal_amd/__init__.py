@@ -16,6 +16,8 @@ Entry points (same names as the C ABI without the ``pvc_`` prefix):
   varlen_attn_fwd       block-diagonal (causal) attention over THD q/k/v
   varlen_attn_bwd       its gradients dq, dk, dv on the same plan
   padded_attn_fwd_sbhd  the same kernel on a padded SBHD buffer (measurement)
+  attn_plan_qk, varlen_attn_fwd_qk  prefill: separate query / key boundaries
+                        (bottom-right causal) and grouped key / value heads
   packed_ce_loss        cross-entropy over the packed rows: loss sum, int64
                         target count, optional per-row / per-segment values and
                         the fused gradient
@@ -32,7 +34,7 @@ __all__ = [
     "PvcError", "DEV_ERROR_BITS", "lib_path", "pack_build", "validate_cu_seqlens",
     "rope_thd_apply", "AttnPlan", "attn_plan", "varlen_attn_fwd", "varlen_attn_bwd",
     "padded_attn_fwd_sbhd", "error_names", "attn_workspace_size", "attn_bwd_scratch_size",
-    "packed_ce_loss", "ce_workspace_size",
+    "packed_ce_loss", "ce_workspace_size", "AttnPlanQK", "attn_plan_qk", "varlen_attn_fwd_qk",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -68,6 +70,8 @@ def _load() -> ctypes.CDLL:
         "pvc_attn_workspace_size": ([I64, I32], SZ),
         "pvc_attn_plan": ([P, I32, I64, I32, I32, P, SZ, P, P], I32),
         "pvc_attn_plan_padded": ([P, P, I32, I64, I32, I32, P, SZ, P, P], I32),
+        "pvc_attn_plan_qk": ([P, P, I32, I64, I64, I32, I32, I32, P, SZ, P, P], I32),
+        "pvc_varlen_attn_fwd_qk_planned": ([P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, P, SZ, P, P], I32),
         "pvc_varlen_attn_fwd_planned": ([P, P, P, P, P, I64, I32, I32, I32, I32, P, SZ, P, P], I32),
         "pvc_varlen_attn_fwd": ([P, P, P, P, P, P, I32, I64, I32, I32, I32, I32, I32, P, SZ, P, P], I32),
         "pvc_padded_attn_fwd_sbhd": ([P, P, P, P, P, I32, I32, I32, I32, I32, I32, P], I32),
@@ -278,6 +282,78 @@ class AttnPlan:
 
 def attn_plan(cu_seqlens, total_tokens, max_seqlen, causal=True, **kw) -> AttnPlan:
     return AttnPlan(cu_seqlens, total_tokens, max_seqlen, causal, **kw)
+
+
+class AttnPlanQK:
+    """Plan for separate query / key boundaries (pvc_attn_plan_qk)."""
+
+    def __init__(self, cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, total_q: int, total_k: int,
+                 max_seqlen_q: int, max_seqlen_k: int, causal: bool = True,
+                 dev_error: torch.Tensor | None = None, stream=None, workspace: torch.Tensor | None = None):
+        _require(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+        _require(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+        if cu_seqlens_q.numel() != cu_seqlens_k.numel():
+            raise ValueError("cu_seqlens_q and cu_seqlens_k must have one entry per request + 1")
+        self.total_q, self.total_k = int(total_q), int(total_k)
+        self.nseg = cu_seqlens_q.numel() - 1
+        self.causal = bool(causal)
+        self.dev_error = _new_error_word(cu_seqlens_q.device) if dev_error is None else dev_error
+        self.ws_bytes = attn_workspace_size(self.total_q, self.nseg)
+        if workspace is None:
+            workspace = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=cu_seqlens_q.device)
+        elif workspace.numel() < self.ws_bytes:
+            raise ValueError("workspace too small")
+        self.workspace = workspace
+        st = _lib.pvc_attn_plan_qk(_ptr(cu_seqlens_q), _ptr(cu_seqlens_k), self.nseg, self.total_q, self.total_k,
+                                   int(max_seqlen_q), int(max_seqlen_k), int(self.causal), _ptr(workspace),
+                                   self.ws_bytes, _ptr(self.dev_error), _stream(stream))
+        _check(st, "attn_plan_qk")
+
+
+def attn_plan_qk(cu_seqlens_q, cu_seqlens_k, total_q, total_k, max_seqlen_q, max_seqlen_k, causal=True,
+                 **kw) -> AttnPlanQK:
+    return AttnPlanQK(cu_seqlens_q, cu_seqlens_k, total_q, total_k, max_seqlen_q, max_seqlen_k, causal, **kw)
+
+
+def varlen_attn_fwd_qk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                       cu_seqlens_q: torch.Tensor | None = None, cu_seqlens_k: torch.Tensor | None = None,
+                       max_seqlen_q: int | None = None, max_seqlen_k: int | None = None, causal: bool = True,
+                       return_lse: bool = False, out_dtype: torch.dtype = torch.bfloat16,
+                       plan: AttnPlanQK | None = None, out: torch.Tensor | None = None, check: bool = False,
+                       stream=None):
+    """Prefill attention: q [Tq, H, d] over k, v [Tk, Hkv, d] (H a multiple of
+    Hkv) with separate request boundaries; bottom-right causal alignment."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(t, name, torch.bfloat16, 3)
+    Tq, H, D = q.shape
+    Tk, Hkv, Dk = k.shape
+    if v.shape != k.shape or Dk != D:
+        raise ValueError("k and v must share the shape [Tk, Hkv, d] with q's d")
+    if H % Hkv:
+        raise ValueError("the query heads must be a multiple of the key / value heads")
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+    if plan is None:
+        if cu_seqlens_q is None or cu_seqlens_k is None or max_seqlen_q is None or max_seqlen_k is None:
+            raise ValueError("give both cu_seqlens and max_seqlens, or a plan")
+        plan = AttnPlanQK(cu_seqlens_q, cu_seqlens_k, Tq, Tk, max_seqlen_q, max_seqlen_k, causal, stream=stream)
+    elif plan.total_q != Tq or plan.total_k != Tk or plan.causal != bool(causal):
+        raise ValueError("plan was built for other totals / causal")
+    if out is None:
+        out = torch.empty((Tq, H, D), dtype=out_dtype, device=q.device)
+    else:
+        _require(out, "out", out_dtype, 3)
+        if tuple(out.shape) != (Tq, H, D):
+            raise ValueError("out must be [Tq, H, d] like q")
+    lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device) if return_lse else None
+    st = _lib.pvc_varlen_attn_fwd_qk_planned(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), Tq, Tk, H, Hkv, D, int(bool(causal)),
+        OUT_F32 if out_dtype == torch.float32 else OUT_BF16, _ptr(plan.workspace), plan.ws_bytes,
+        _ptr(plan.dev_error), _stream(stream))
+    _check(st, "varlen_attn_fwd_qk")
+    if check:
+        _raise_dev(plan.dev_error, "varlen_attn_fwd_qk")
+    return (out, lse) if return_lse else out
 
 
 def varlen_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

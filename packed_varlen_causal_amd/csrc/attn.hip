@@ -117,6 +117,62 @@ __global__ __launch_bounds__(kCheckThreads) void plan_check_kernel(
         header[HDR_NTILES] = ntiles;
         header[HDR_ERR] = (int32_t)s_err;
         header[HDR_VALID] = s_err == 0 ? 1 : 0;
+        header[HDR_FOLDED] = 0;
+        header[HDR_TK] = (int32_t)T;
+        raise_error(dev_error, s_err);
+    }
+}
+
+// Separate query and key boundaries (requests of an inference prefill):
+// query a of request r (rows [cu_q[r], cu_q[r+1])) sees keys
+// [cu_k[r], cu_k[r] + n) with n = min(Lk, a + Lk - Lq + 1) when causal (the
+// bottom-right alignment: the last query sees every key) and n = Lk
+// otherwise; n <= 0 gives an empty range (output 0).
+__global__ __launch_bounds__(256) void plan_rows_qk_kernel(const int32_t* __restrict__ cu_q,
+                                                           const int32_t* __restrict__ cu_k, int32_t nseg,
+                                                           int64_t Tq, int64_t Tk, int32_t causal,
+                                                           int2* __restrict__ rows) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= Tq) return;
+    const int32_t r = upper_segment(cu_q, nseg, i);
+    const int64_t qs = cu_q[r], qe = cu_q[r + 1];
+    const int64_t ks = min<int64_t>(max<int64_t>(cu_k[r], 0), Tk);
+    const int64_t ke = min<int64_t>(max<int64_t>(cu_k[r + 1], ks), Tk);
+    const int64_t Lk = ke - ks;
+    const int64_t n = causal ? min<int64_t>(Lk, (i - qs) + Lk - (qe - qs) + 1) : Lk;
+    const bool ok = qs <= i && i < qe;
+    rows[i] = ok ? make_int2((int)ks, (int)(ks + max<int64_t>(n, 0))) : make_int2((int)ks, (int)ks);
+}
+
+__global__ __launch_bounds__(kCheckThreads) void plan_check_qk_kernel(
+        const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int32_t nseg, int64_t Tq, int64_t Tk,
+        int32_t max_q, int32_t max_k, int32_t causal, int32_t* __restrict__ header, int32_t ntiles,
+        uint32_t* dev_error) {
+    __shared__ unsigned s_err;
+    const int t = threadIdx.x;
+    if (t == 0) s_err = 0;
+    __syncthreads();
+    uint32_t err = 0;
+    for (int64_t r = t; r < nseg; r += kCheckThreads) {
+        const int64_t a = cu_q[r], b = cu_q[r + 1], ka = cu_k[r], kb = cu_k[r + 1];
+        if (b <= a || kb <= ka) err |= PVC_DEV_NOT_INCREASING;
+        if (b - a > max_q || kb - ka > max_k) err |= PVC_DEV_MAXSEQ;
+    }
+    if (t == 0) {
+        if (cu_q[0] != 0 || cu_k[0] != 0) err |= PVC_DEV_CU0;
+        if ((int64_t)cu_q[nseg] != Tq || (int64_t)cu_k[nseg] != Tk) err |= PVC_DEV_TOTAL;
+    }
+    if (err) atomicOr(&s_err, err);
+    __syncthreads();
+    if (t == 0) {
+        header[HDR_MAGIC] = kPlanMagic;
+        header[HDR_T] = (int32_t)Tq;
+        header[HDR_CAUSAL] = causal ? 1 : 0;
+        header[HDR_NTILES] = ntiles;
+        header[HDR_ERR] = (int32_t)s_err;
+        header[HDR_VALID] = s_err == 0 ? 1 : 0;
+        header[HDR_FOLDED] = 1;
+        header[HDR_TK] = (int32_t)Tk;
         raise_error(dev_error, s_err);
     }
 }
@@ -132,8 +188,12 @@ struct AttnParams {
     const int32_t* header;     // THD: plan header
     const int2* rows;          // THD: per-row key range
     const int32_t* seqlens;    // SBHD: valid length per sample
-    int64_t T;                 // THD: total tokens
-    int32_t H;
+    int64_t T;                 // THD: query rows
+    int64_t Tk;                // THD: key / value rows
+    int32_t H;                 // query heads
+    int32_t group;             // query heads per key / value head
+    int32_t folded;            // the plan's row ranges hold the causal limit
+    int32_t causal_flag;       // causal as the caller asked (checked against the plan)
     int32_t ntiles;            // THD: tiles; SBHD: tiles per sample
     int32_t items;             // heads x tiles (x batch for SBHD)
     int32_t B, L;              // SBHD: batch and padded length
@@ -186,15 +246,17 @@ void attn_fwd_kernel(AttnParams p) {
         // neighbours that share K/V in its L2.  The tiles whose first row lies
         // in segment s are [ceil(start_s / BM), ceil(end_s / BM)); position
         // pos of that run takes the tile mirrored in it.
+        // (A plan of separate key boundaries keeps the buffer order: its row
+        // ranges are key rows, not the query segment.)
         head = logical / p.ntiles;
         const int pos = logical - head * p.ntiles;
         const int2 sr = p.rows[(int64_t)pos * kBM];          // segment of the first row at pos
         const int ta = (sr.x + kBM - 1) / kBM;
         const int tb = min((sr.y + kBM - 1) / kBM, p.ntiles);
-        const int tile = (pos >= ta && pos < tb) ? ta + tb - 1 - pos : pos;
+        const int tile = (!p.folded && pos >= ta && pos < tb) ? ta + tb - 1 - pos : pos;
         r0 = tile * kBM;
         r1 = (int)min<int64_t>((int64_t)r0 + kBM, p.T);
-        last_row = (int)(p.T - 1);
+        last_row = (int)(p.Tk - 1);
     }
     const int H = p.H;
     const int seq_len = SBHD ? p.seqlens[b] : 0;
@@ -258,9 +320,9 @@ void attn_fwd_kernel(AttnParams p) {
     bool plan_ok = true;
     if constexpr (!SBHD) {
         const int4 h0 = *reinterpret_cast<const int4*>(p.header);
-        const int2 h1 = *reinterpret_cast<const int2*>(p.header + 4);
-        const bool sealed = (h0.x == kPlanMagic) & (h0.y == (int32_t)p.T) & (h0.z == (CAUSAL ? 1 : 0)) &
-                            (h0.w == p.ntiles);
+        const int4 h1 = *reinterpret_cast<const int4*>(p.header + 4);
+        const bool sealed = (h0.x == kPlanMagic) & (h0.y == (int32_t)p.T) & (h0.z == p.causal_flag) &
+                            (h0.w == p.ntiles) & (h1.z == p.folded) & (h1.w == (int32_t)p.Tk);
         plan_ok = sealed & (h1.y == 1);
         if (!sealed && threadIdx.x == 0) raise_error(p.dev_error, PVC_DEV_PLAN);
     }
@@ -274,8 +336,9 @@ void attn_fwd_kernel(AttnParams p) {
     // chunk only moves the uniform base pointer.
     constexpr int CHUNK_ROWS = kWaves * ROWS_PER_CHUNK;     // rows between a wave's chunks
     static_assert(CHUNK_ROWS % 16 == 0, "swizzle period");
-    const int64_t row_stride = SBHD ? (int64_t)p.B * H * D : (int64_t)H * D;   // elements per key row
-    const int64_t head_off = SBHD ? ((int64_t)b * H + head) * D : (int64_t)head * D;
+    // elements per key row, and the key / value head this query head reads
+    const int64_t row_stride = SBHD ? (int64_t)p.B * H * D : (int64_t)(H / p.group) * D;
+    const int64_t head_off = SBHD ? ((int64_t)b * H + head) * D : (int64_t)(head / p.group) * D;
     const int fetch_rr = wave * ROWS_PER_CHUNK + lane / L16;   // row of chunk 0 in the stage
     uint32_t k_loff, v_loff;
     {
@@ -654,7 +717,11 @@ extern "C" pvc_status pvc_varlen_attn_fwd_planned(const void* q, const void* k, 
     prm.header = reinterpret_cast<const int32_t*>(ws + L.header);
     prm.rows = reinterpret_cast<const int2*>(ws + L.rows);
     prm.T = total_tokens;
+    prm.Tk = total_tokens;
     prm.H = heads;
+    prm.group = 1;
+    prm.folded = 0;
+    prm.causal_flag = causal != 0 ? 1 : 0;
     prm.ntiles = (int32_t)L.ntiles;
     prm.items = (int32_t)(L.ntiles * heads);
     prm.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
@@ -663,6 +730,78 @@ extern "C" pvc_status pvc_varlen_attn_fwd_planned(const void* q, const void* k, 
     const bool f32 = out_dtype == PVC_OUT_F32;
     if (head_dim == 128) return launch_fwd<128, false>(prm, causal != 0, f32, s);
     return launch_fwd<64, false>(prm, causal != 0, f32, s);
+}
+
+extern "C" pvc_status pvc_attn_plan_qk(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t nseg,
+                                       int64_t total_q, int64_t total_k, int32_t max_seqlen_q,
+                                       int32_t max_seqlen_k, int32_t causal, void* workspace,
+                                       size_t workspace_bytes, uint32_t* dev_error, void* stream) {
+    if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr || workspace == nullptr) return PVC_ERR_NULL;
+    if (nseg < 1 || total_q < 1 || total_q > 0x7fffffffLL || total_k < 1 || total_k > 0x7fffffffLL ||
+        max_seqlen_q < 1 || max_seqlen_k < 1)
+        return PVC_ERR_INVALID_ARG;
+    const PlanLayout L = plan_layout(total_q);
+    if (workspace_bytes < L.total) return PVC_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    auto* header = reinterpret_cast<int32_t*>(ws + L.header);
+    auto* rows = reinterpret_cast<int2*>(ws + L.rows);
+    hipStream_t s = as_stream(stream);
+    const int64_t nblk = (total_q + 255) / 256;
+    hipLaunchKernelGGL(plan_rows_qk_kernel, dim3((unsigned)nblk), dim3(256), 0, s, cu_seqlens_q, cu_seqlens_k,
+                       nseg, total_q, total_k, causal ? 1 : 0, rows);
+    hipLaunchKernelGGL(plan_check_qk_kernel, dim3(1), dim3(kCheckThreads), 0, s, cu_seqlens_q, cu_seqlens_k, nseg,
+                       total_q, total_k, max_seqlen_q, max_seqlen_k, causal ? 1 : 0, header, (int32_t)L.ntiles,
+                       dev_error);
+    return launch_status();
+}
+
+extern "C" pvc_status pvc_varlen_attn_fwd_qk_planned(const void* q, const void* k, const void* v, void* out,
+                                                     float* lse, int64_t total_q, int64_t total_k, int32_t heads,
+                                                     int32_t kv_heads, int32_t head_dim, int32_t causal,
+                                                     int32_t out_dtype, const void* workspace,
+                                                     size_t workspace_bytes, uint32_t* dev_error, void* stream) {
+    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || workspace == nullptr)
+        return PVC_ERR_NULL;
+    if (total_q < 1 || total_q > 0x7fffffffLL || total_k < 1 || total_k > 0x7fffffffLL || heads < 1 ||
+        kv_heads < 1 || heads % kv_heads != 0)
+        return PVC_ERR_INVALID_ARG;
+    if (out_dtype != PVC_OUT_BF16 && out_dtype != PVC_OUT_F32) return PVC_ERR_INVALID_ARG;
+    if (head_dim != 64 && head_dim != 128) return PVC_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PVC_ERR_INVALID_ARG;
+    const PlanLayout L = plan_layout(total_q);
+    if (workspace_bytes < L.total) return PVC_ERR_WORKSPACE;
+    const size_t q_bytes = (size_t)total_q * heads * head_dim * 2;
+    const size_t kv_bytes = (size_t)total_k * kv_heads * head_dim * 2;
+    const size_t out_bytes = q_bytes * (out_dtype == PVC_OUT_F32 ? 2 : 1);
+    if (overlaps(out, out_bytes, q, q_bytes) || overlaps(out, out_bytes, k, kv_bytes) ||
+        overlaps(out, out_bytes, v, kv_bytes))
+        return PVC_ERR_INVALID_ARG;
+    if (L.ntiles * (int64_t)heads > 0x7ffffff0LL) return PVC_ERR_INVALID_ARG;
+    if ((int64_t)heads * head_dim > kMaxRowElems) return PVC_ERR_INVALID_ARG;
+    const char* ws = static_cast<const char*>(workspace);
+    AttnParams prm{};
+    prm.q = static_cast<const uint16_t*>(q);
+    prm.k = static_cast<const uint16_t*>(k);
+    prm.v = static_cast<const uint16_t*>(v);
+    prm.out = out;
+    prm.lse = lse;
+    prm.header = reinterpret_cast<const int32_t*>(ws + L.header);
+    prm.rows = reinterpret_cast<const int2*>(ws + L.rows);
+    prm.T = total_q;
+    prm.Tk = total_k;
+    prm.H = heads;
+    prm.group = heads / kv_heads;
+    prm.folded = 1;
+    prm.causal_flag = causal != 0 ? 1 : 0;
+    prm.ntiles = (int32_t)L.ntiles;
+    prm.items = (int32_t)(L.ntiles * heads);
+    prm.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
+    prm.dev_error = dev_error;
+    hipStream_t s = as_stream(stream);
+    const bool f32 = out_dtype == PVC_OUT_F32;
+    // the causal limit is in the plan's row ranges: the kernel runs without its own diagonal
+    if (head_dim == 128) return launch_fwd<128, false>(prm, false, f32, s);
+    return launch_fwd<64, false>(prm, false, f32, s);
 }
 
 extern "C" pvc_status pvc_varlen_attn_fwd(const void* q, const void* k, const void* v, void* out,
@@ -711,6 +850,7 @@ extern "C" pvc_status pvc_padded_attn_fwd_sbhd(const void* q, const void* k, con
     prm.H = heads;
     prm.ntiles = (int32_t)tiles;
     prm.items = (int32_t)items;
+    prm.group = 1;
     prm.B = batch;
     prm.L = max_len;
     prm.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));

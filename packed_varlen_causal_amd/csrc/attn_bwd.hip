@@ -136,8 +136,10 @@ __device__ inline int xcd_logical() {
 // Plan header check, read in one piece (see the forward).
 __device__ inline bool plan_sealed(const BwdParams& p, bool causal, bool& sealed) {
     const int4 h0 = *reinterpret_cast<const int4*>(p.header);
-    const int2 h1 = *reinterpret_cast<const int2*>(p.header + 4);
-    sealed = (h0.x == kPlanMagic) & (h0.y == (int32_t)p.T) & (h0.z == (causal ? 1 : 0)) & (h0.w == p.ntiles);
+    const int4 h1 = *reinterpret_cast<const int4*>(p.header + 4);
+    // a self-attention plan only: no separate key boundaries
+    sealed = (h0.x == kPlanMagic) & (h0.y == (int32_t)p.T) & (h0.z == (causal ? 1 : 0)) & (h0.w == p.ntiles) &
+             (h1.z == 0) & (h1.w == (int32_t)p.T);
     return sealed & (h1.y == 1);
 }
 

@@ -21,7 +21,11 @@ constexpr int kCheckThreads = 1024;
 constexpr int kNumXcd = 8;
 constexpr int32_t kPlanMagic = 0x31435650;   // "PVC1"
 
-enum { HDR_MAGIC = 0, HDR_T = 1, HDR_CAUSAL = 2, HDR_NTILES = 3, HDR_ERR = 4, HDR_VALID = 5 };
+// Plan header (int32 slots).  HDR_FOLDED: the plan of separate query / key
+// boundaries, whose row ranges already hold the causal limit (the kernels
+// then run without their own diagonal); HDR_TK: rows of K and V.
+enum { HDR_MAGIC = 0, HDR_T = 1, HDR_CAUSAL = 2, HDR_NTILES = 3, HDR_ERR = 4, HDR_VALID = 5, HDR_FOLDED = 6,
+       HDR_TK = 7 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -1,0 +1,128 @@
+"""GPU parity for the prefill path: separate query / key boundaries with the
+bottom-right causal alignment, grouped key / value heads (pvc_attn_plan_qk +
+pvc_varlen_attn_fwd_qk_planned), against the fp64 oracle attention_qk with the
+attention forward's three-part check (fp32 output within 1e-2, bf16 output the
+RNE of it, raw bf16 error reported)."""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import dev_bf16, dev_i32, host_bits, say, three_part_check
+from oracle import attention as A
+from workloads import f32_to_bf16_bits, make_prefill, prefill_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pvc():
+    import packed_varlen_causal_amd as m
+    assert torch.cuda.is_available()
+    return m
+
+
+def _bits(shape, seed):
+    return f32_to_bf16_bits(np.random.default_rng(seed).standard_normal(shape, dtype=np.float32))
+
+
+def _run(pvc, q, k, v, cu_q, cu_k, causal=True):
+    cu_q, cu_k = np.asarray(cu_q), np.asarray(cu_k)
+    qd, kd, vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    plan = pvc.attn_plan_qk(dev_i32(cu_q), dev_i32(cu_k), q.shape[0], k.shape[0],
+                            int(np.diff(cu_q).max()), int(np.diff(cu_k).max()), causal)
+    ob = pvc.varlen_attn_fwd_qk(qd, kd, vd, plan=plan, causal=causal)
+    of, ls = pvc.varlen_attn_fwd_qk(qd, kd, vd, plan=plan, causal=causal, out_dtype=torch.float32,
+                                    return_lse=True)
+    torch.cuda.synchronize()
+    assert int(plan.dev_error.item()) == 0
+    return ob, of, ls
+
+
+def _cu(lengths):
+    return np.concatenate([[0], np.cumsum(np.asarray(lengths, np.int64))])
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_small_prefill_every_row(pvc, causal):
+    pw = make_prefill(scale="small")
+    q, k, v = (prefill_bits(pw, x) for x in "qkv")
+    cu_q, cu_k = _cu(pw.lq), _cu(pw.lk)
+    say(f"  prefill small causal={causal}: Tq={pw.total_q} Tk={pw.total_k} requests={len(pw.lq)} "
+        f"H={pw.heads} Hkv={pw.kv_heads}")
+    ob, of, ls = _run(pvc, q, k, v, cu_q, cu_k, causal)
+    ref, ref_lse = A.attention_qk(q, k, v, cu_q, cu_k, causal)
+    three_part_check(of, ob, ref)
+    assert np.abs(ls.cpu().numpy().T - ref_lse).max() < 5e-3
+
+
+@pytest.mark.parametrize("lq,lk,hq,hkv", [
+    ([5, 1, 130, 33, 64], [3, 7, 130, 300, 64], 4, 1),    # Lk < Lq, decode, square, long prefix
+    ([1] * 40, [200] * 40, 8, 8),                          # forty single-token decodes
+    ([257, 2, 129], [257, 2, 129], 6, 3),                  # square requests, grouped heads
+])
+def test_edge_requests(pvc, lq, lk, hq, hkv):
+    d = 128 if hq % 2 == 0 else 64
+    cu_q, cu_k = _cu(lq), _cu(lk)
+    say(f"  prefill edge lq={lq[:5]} lk={lk[:5]} H={hq} Hkv={hkv}")
+    q = _bits((int(cu_q[-1]), hq, d), 1)
+    k, v = _bits((int(cu_k[-1]), hkv, d), 2), _bits((int(cu_k[-1]), hkv, d), 3)
+    ob, of, ls = _run(pvc, q, k, v, cu_q, cu_k)
+    ref, ref_lse = A.attention_qk(q, k, v, cu_q, cu_k, True)
+    three_part_check(of, ob, ref)
+    none = np.isneginf(ref_lse[:, 0])
+    assert (of.cpu().numpy()[none] == 0).all() and np.isneginf(ls.cpu().numpy().T[none]).all()
+
+
+def test_square_grouped_equals_repeated_heads_through_the_self_plan(pvc):
+    """Square boundaries: the grouped kernel run equals the self-attention
+    kernel on K/V heads repeated to the query head count, within the bar."""
+    lengths = [100, 37, 300, 64]
+    cu = _cu(lengths)
+    T = int(cu[-1])
+    q, k, v = _bits((T, 8, 128), 4), _bits((T, 2, 128), 5), _bits((T, 2, 128), 6)
+    _, of, _ = _run(pvc, q, k, v, cu, cu)
+    kr, vr = np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1)
+    o_self = pvc.varlen_attn_fwd(dev_bf16(q), dev_bf16(kr), dev_bf16(vr), dev_i32(cu), 300,
+                                 out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert (of - o_self).abs().max().item() <= 2e-3
+
+
+def test_full_size_sampled_rows(pvc):
+    pw = make_prefill()
+    q, k, v = (prefill_bits(pw, x) for x in "qkv")
+    cu_q, cu_k = _cu(pw.lq), _cu(pw.lk)
+    say(f"  prefill full: Tq={pw.total_q} Tk={pw.total_k} requests={len(pw.lq)}")
+    ob, of, _ = _run(pvc, q, k, v, cu_q, cu_k)
+    rows = np.unique(np.concatenate([cu_q[:-1], cu_q[1:] - 1, np.random.default_rng(0).integers(0, pw.total_q, 150)]))
+    ref, _ = A.attention_qk(q, k, v, cu_q, cu_k, True, rows=rows)
+    three_part_check(of, ob, ref[rows], rows=rows)
+
+
+def test_plans_are_not_interchangeable(pvc):
+    """A prefill plan given to the self-attention forward (and a self plan to
+    the prefill forward) sets PVC_DEV_PLAN and writes nothing."""
+    cu = dev_i32([0, 30, 64])
+    T, H, d = 64, 2, 64
+    q, k, v = (dev_bf16(_bits((T, H, d), s)) for s in (1, 2, 3))
+    qk = pvc.attn_plan_qk(cu, cu, T, T, 34, 34, True)
+    out = torch.full((T, H, d), 7.0, dtype=torch.bfloat16, device="cuda")
+    st = pvc._lib.pvc_varlen_attn_fwd_planned(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+        ctypes.c_void_p(out.data_ptr()), None, T, H, d, 1, 0, ctypes.c_void_p(qk.workspace.data_ptr()),
+        qk.ws_bytes, ctypes.c_void_p(qk.dev_error.data_ptr()),
+        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert st == 0 and int(qk.dev_error.item()) & 128 and (out.float() == 7.0).all()
+    selfp = pvc.attn_plan(cu, T, 34, True)
+    out2 = torch.full((T, H, d), 7.0, dtype=torch.bfloat16, device="cuda")
+    st = pvc._lib.pvc_varlen_attn_fwd_qk_planned(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+        ctypes.c_void_p(out2.data_ptr()), None, T, T, H, H, d, 1, 0, ctypes.c_void_p(selfp.workspace.data_ptr()),
+        selfp.ws_bytes, ctypes.c_void_p(selfp.dev_error.data_ptr()),
+        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert st == 0 and int(selfp.dev_error.item()) & 128 and (out2.float() == 7.0).all()

@@ -41,7 +41,8 @@ def test_header_declares_the_hot_path():
                  "pvc_varlen_attn_fwd", "pvc_varlen_attn_fwd_planned", "pvc_padded_attn_fwd_sbhd",
                  "pvc_attn_workspace_size", "pvc_pack_build_workspace_size", "pvc_status_string",
                  "pvc_varlen_attn_bwd_planned", "pvc_attn_bwd_scratch_size", "pvc_packed_ce_loss",
-                 "pvc_ce_workspace_size", "pvc_attn_plan_padded", "pvc_rope_thd_apply_interleaved"):
+                 "pvc_ce_workspace_size", "pvc_attn_plan_padded", "pvc_rope_thd_apply_interleaved",
+                 "pvc_attn_plan_qk", "pvc_varlen_attn_fwd_qk_planned"):
         assert must in names
 
 
@@ -132,6 +133,19 @@ def test_null_and_range_checks_return_before_gpu_work(lib):
     assert lib.pvc_attn_plan_padded(fake, None, 3, 12, 4, 1, fake, 1 << 20, None, None) == 1
     assert lib.pvc_attn_plan_padded(fake, fake, 0, 12, 4, 1, fake, 1 << 20, None, None) == 2
     assert lib.pvc_attn_plan_padded(fake, fake, 3, 12, 4, 1, fake, 16, None, None) == 4
+    lib.pvc_attn_plan_qk.restype = I32
+    lib.pvc_attn_plan_qk.argtypes = [P, P, I32, I64, I64, I32, I32, I32, P, SZ, P, P]
+    assert lib.pvc_attn_plan_qk(fake, None, 2, 9, 20, 8, 16, 1, fake, 1 << 20, None, None) == 1
+    assert lib.pvc_attn_plan_qk(fake, fake, 2, 9, 0, 8, 16, 1, fake, 1 << 20, None, None) == 2
+    lib.pvc_varlen_attn_fwd_qk_planned.restype = I32
+    lib.pvc_varlen_attn_fwd_qk_planned.argtypes = [P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, P, SZ, P, P]
+    qq, kk, vv, oo = (_vp(0x10000000 * (i + 1)) for i in range(4))
+    assert lib.pvc_varlen_attn_fwd_qk_planned(qq, kk, vv, oo, None, 9, 20, 6, 4, 64, 1, 0, fake, 1 << 20,
+                                              None, None) == 2   # 6 heads over 4 kv heads
+    assert lib.pvc_varlen_attn_fwd_qk_planned(qq, kk, vv, oo, None, 9, 20, 8, 2, 80, 1, 0, fake, 1 << 20,
+                                              None, None) == 3
+    assert lib.pvc_varlen_attn_fwd_qk_planned(qq, kk, vv, kk, None, 9, 20, 8, 2, 64, 1, 0, fake, 1 << 20,
+                                              None, None) == 2   # out aliasing k
 
     lib.pvc_varlen_attn_fwd_planned.restype = I32
     lib.pvc_varlen_attn_fwd_planned.argtypes = [P, P, P, P, P, I64, I32, I32, I32, I32, P, SZ, P, P]

@@ -14,6 +14,9 @@ from .generators import (  # noqa: F401
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     logits_bits,
+    make_prefill,
+    prefill_bits,
+    Prefill,
     make_workload,
     qkv_bits,
     token_ids,

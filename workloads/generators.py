@@ -9,7 +9,8 @@ Page tags used in citations (the pages are the specification):
 
 Every random draw comes from ``numpy.random.default_rng([cfg_id, stream, seed])``
 (PCG64).  Streams: 0 = sample lengths, 1 = token ids, 2/3/4 = q/k/v, 5 = an upstream
-gradient of the attention output, 6 = logits for the packed cross-entropy.  q/k/v are
+gradient of the attention output, 6 = logits for the packed cross-entropy,
+7 = prefill request lengths, 8/9/10 = prefill q/k/v.  q/k/v are
 standard normal float32 values rounded to bf16 (round to nearest even) and are
 carried as uint16 bit patterns, shape ``[T, H, d]`` (THD, no batch dim).
 
@@ -301,3 +302,61 @@ def logits_bits(w: Workload, vocab: int, sigma: float = 2.0, rows: int | None = 
         e = min(n, s + chunk)
         out[s:e] = f32_to_bf16_bits(rng.standard_normal(e - s, dtype=np.float32) * np.float32(sigma))
     return out.reshape(T, vocab)
+
+
+@dataclasses.dataclass
+class Prefill:
+    """An inference prefill of independent requests: request r brings
+    new_len[r] new tokens (its queries) after a cached prefix of
+    prefix_len[r] tokens; its keys are the prefix plus the new tokens."""
+
+    name: str
+    seed: int
+    new_len: np.ndarray          # int32 [n] = Lq
+    prefix_len: np.ndarray       # int32 [n]
+    heads: int
+    kv_heads: int
+    head_dim: int
+
+    @property
+    def lq(self) -> np.ndarray:
+        return self.new_len.astype(np.int64)
+
+    @property
+    def lk(self) -> np.ndarray:
+        return (self.new_len.astype(np.int64) + self.prefix_len)
+
+    @property
+    def total_q(self) -> int:
+        return int(self.lq.sum())
+
+    @property
+    def total_k(self) -> int:
+        return int(self.lk.sum())
+
+
+def make_prefill(seed: int = 0, *, scale: str = "full") -> Prefill:
+    """Requests until total_q new tokens: new lengths lognormal(median 256,
+    sigma 1) clipped to [1, 2048]; cached prefixes 0 with probability 0.3,
+    else uniform in [1, 4096]; 32 query heads over 8 key / value heads (the
+    "full" size, 32,768 query rows) or 4 over 2 ("small", 2,048 rows)."""
+    small = scale == "small"
+    total = 2048 if small else 32768
+    rng = np.random.default_rng([len(CONFIG_NAMES), 7, seed])
+    new, pre = [], []
+    while sum(new) < total:
+        L = int(np.clip(np.rint(np.exp(math.log(256.0) + rng.standard_normal())), 1, 2048))
+        L = min(L, total - sum(new))
+        new.append(L)
+        pre.append(0 if rng.random() < 0.3 else int(rng.integers(1, (1024 if small else 4096) + 1)))
+    H, Hkv = (4, 2) if small else (32, 8)
+    return Prefill("prefill", seed, np.asarray(new, np.int32), np.asarray(pre, np.int32), H, Hkv, 128)
+
+
+def prefill_bits(pw: Prefill, which: str) -> np.ndarray:
+    """uint16 bf16 bits of N(0,1): q [Tq, H, d], k / v [Tk, Hkv, d]."""
+    stream = {"q": 8, "k": 9, "v": 10}[which]
+    rng = np.random.default_rng([len(CONFIG_NAMES), stream, pw.seed])
+    rows, heads = (pw.total_q, pw.heads) if which == "q" else (pw.total_k, pw.kv_heads)
+    x = rng.standard_normal(rows * heads * pw.head_dim, dtype=np.float32)
+    return f32_to_bf16_bits(x).reshape(rows, heads, pw.head_dim)
