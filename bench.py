@@ -12,7 +12,8 @@ segments are computed but not counted).  Per-kernel durations come from HIP
 events recorded on the stream the kernels run on.  Beside it, in the same
 process: the backward (varlen_attn_bwd, not part of the step: useful FLOPs
 2.5x the forward's), the packed cross-entropy over the step's labels with
-[T, 32000] logits (packed_ce_loss, not part of the step), the same kernel on the padded SBHD layout, the other
+[T, 32000] logits (packed_ce_loss, not part of the step), an inference
+prefill through the separate-boundary forward (varlen_attn_fwd_qk), the same kernel on the padded SBHD layout, the other
 workloads' attention rates, and the fp64 CPU oracle timed on a bounded sample
 of rows.
 """
@@ -234,6 +235,51 @@ def time_ce(torch, pvc, x, steps, warmup, vocab=CE_VOCAB):
     del logits, ws
     torch.cuda.empty_cache()
     return res
+
+
+def time_prefill(torch, pvc, steps, warmup):
+    """The prefill path on its own workload: independent requests with cached
+    prefixes (separate query / key boundaries, bottom-right causal), 32 query
+    heads over 8 key / value heads, d = 128.  Useful FLOPs: 4 d H per visible
+    (query, key) pair."""
+    from workloads import make_prefill
+    pw = make_prefill()
+    lq, lk = pw.lq, pw.lk
+    pairs = 0
+    for a_len, k_len in zip(lq.tolist(), lk.tolist()):
+        # query a sees min(Lk, a + Lk - Lq + 1) keys
+        a = np.arange(a_len)
+        pairs += int(np.clip(a + k_len - a_len + 1, 0, k_len).sum())
+    flops = 4.0 * pw.head_dim * pw.heads * pairs
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(8)
+    q = torch.randn((pw.total_q, pw.heads, pw.head_dim), generator=gen, device="cuda", dtype=torch.bfloat16)
+    k = torch.randn((pw.total_k, pw.kv_heads, pw.head_dim), generator=gen, device="cuda", dtype=torch.bfloat16)
+    v = torch.randn_like(k)
+    cu_q = torch.from_numpy(np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)).cuda()
+    cu_k = torch.from_numpy(np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)).cuda()
+    plan = pvc.attn_plan_qk(cu_q, cu_k, pw.total_q, pw.total_k, int(lq.max()), int(lk.max()), True)
+    out = torch.empty_like(q)
+    for _ in range(warmup):
+        pvc.varlen_attn_fwd_qk(q, k, v, plan=plan, out=out)
+    torch.cuda.synchronize()
+    a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a_ev.record()
+    for _ in range(steps):
+        pvc.varlen_attn_fwd_qk(q, k, v, plan=plan, out=out)
+    b_ev.record()
+    torch.cuda.synchronize()
+    if int(plan.dev_error.item()) != 0:
+        raise RuntimeError(f"device error bits {pvc.error_names(int(plan.dev_error.item()))}")
+    ms = a_ev.elapsed_time(b_ev) / steps
+    nbytes = 2.0 * pw.head_dim * (2 * pw.total_q * pw.heads + 2 * pw.total_k * pw.kv_heads)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"requests": int(lq.size), "total_q": pw.total_q, "total_k": pw.total_k, "heads": pw.heads,
+            "kv_heads": pw.kv_heads, "head_dim": pw.head_dim, "ms": round(ms, 4), "useful_tflops": round(tf, 2),
+            "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+            "roofline_tflops": round(min(PEAK_BF16_TFLOPS, flops / nbytes * PEAK_HBM_GBPS / 1e3), 1),
+            "setup": "prefixes 0 (p 0.3) or U[1, 4096], new lengths lognormal(256, 1) in [1, 2048]; "
+                     "q/k/v N(0,1) seeded on the device"}
 
 
 def padded_baseline(torch, pvc, x, reps=3, max_chunk_bytes=24 << 30):
@@ -561,6 +607,7 @@ def main():
             del y
             torch.cuda.empty_cache()
         res["other_workloads"] = others
+        res["prefill"] = time_prefill(torch, pvc, max(3, args.steps // 2), 2)
 
     if not args.no_cpu_baseline:
         cb = cpu_baseline(x, args.cpu_seconds)

@@ -246,7 +246,8 @@ pvc_status pvc_attn_plan_padded(const int32_t* cu_seqlens, const int32_t* cu_seq
  * [nseg + 1] int32 on the device, strictly increasing from 0 to total_q /
  * total_k, segments at most max_seqlen_q / max_seqlen_k (else the usual error
  * bits and an empty plan).  Workspace pvc_attn_workspace_size(total_q, nseg).
- * Query tiles run in buffer order.  Used by pvc_varlen_attn_fwd_qk_planned
+ * Query tiles run request by request, each request's from its end (the
+ * heaviest) to its start.  Used by pvc_varlen_attn_fwd_qk_planned
  * only (a forward: the backward entry refuses this plan).
  */
 pvc_status pvc_attn_plan_qk(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t nseg,

@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kCheckThreads) void plan_check_kernel(
 __global__ __launch_bounds__(256) void plan_rows_qk_kernel(const int32_t* __restrict__ cu_q,
                                                            const int32_t* __restrict__ cu_k, int32_t nseg,
                                                            int64_t Tq, int64_t Tk, int32_t causal,
-                                                           int2* __restrict__ rows) {
+                                                           int2* __restrict__ rows, int2* __restrict__ qseg) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= Tq) return;
     const int32_t r = upper_segment(cu_q, nseg, i);
@@ -142,6 +142,7 @@ __global__ __launch_bounds__(256) void plan_rows_qk_kernel(const int32_t* __rest
     const int64_t n = causal ? min<int64_t>(Lk, (i - qs) + Lk - (qe - qs) + 1) : Lk;
     const bool ok = qs <= i && i < qe;
     rows[i] = ok ? make_int2((int)ks, (int)(ks + max<int64_t>(n, 0))) : make_int2((int)ks, (int)ks);
+    qseg[i] = ok ? make_int2((int)qs, (int)qe) : make_int2((int)i, (int)i);
 }
 
 __global__ __launch_bounds__(kCheckThreads) void plan_check_qk_kernel(
@@ -187,6 +188,7 @@ struct AttnParams {
     float* lse;
     const int32_t* header;     // THD: plan header
     const int2* rows;          // THD: per-row key range
+    const int2* qseg;          // THD: per-row query segment (tile order of folded plans)
     const int32_t* seqlens;    // SBHD: valid length per sample
     int64_t T;                 // THD: query rows
     int64_t Tk;                // THD: key / value rows
@@ -246,14 +248,14 @@ void attn_fwd_kernel(AttnParams p) {
         // neighbours that share K/V in its L2.  The tiles whose first row lies
         // in segment s are [ceil(start_s / BM), ceil(end_s / BM)); position
         // pos of that run takes the tile mirrored in it.
-        // (A plan of separate key boundaries keeps the buffer order: its row
-        // ranges are key rows, not the query segment.)
+        // (A plan of separate key boundaries keeps the query segments apart:
+        // its row ranges are key rows.)
         head = logical / p.ntiles;
         const int pos = logical - head * p.ntiles;
-        const int2 sr = p.rows[(int64_t)pos * kBM];          // segment of the first row at pos
+        const int2 sr = (p.folded ? p.qseg : p.rows)[(int64_t)pos * kBM];   // segment of the first row at pos
         const int ta = (sr.x + kBM - 1) / kBM;
         const int tb = min((sr.y + kBM - 1) / kBM, p.ntiles);
-        const int tile = (!p.folded && pos >= ta && pos < tb) ? ta + tb - 1 - pos : pos;
+        const int tile = (pos >= ta && pos < tb) ? ta + tb - 1 - pos : pos;
         r0 = tile * kBM;
         r1 = (int)min<int64_t>((int64_t)r0 + kBM, p.T);
         last_row = (int)(p.Tk - 1);
@@ -716,6 +718,7 @@ extern "C" pvc_status pvc_varlen_attn_fwd_planned(const void* q, const void* k, 
     prm.lse = lse;
     prm.header = reinterpret_cast<const int32_t*>(ws + L.header);
     prm.rows = reinterpret_cast<const int2*>(ws + L.rows);
+    prm.qseg = reinterpret_cast<const int2*>(ws + L.qseg);
     prm.T = total_tokens;
     prm.Tk = total_tokens;
     prm.H = heads;
@@ -745,10 +748,11 @@ extern "C" pvc_status pvc_attn_plan_qk(const int32_t* cu_seqlens_q, const int32_
     char* ws = static_cast<char*>(workspace);
     auto* header = reinterpret_cast<int32_t*>(ws + L.header);
     auto* rows = reinterpret_cast<int2*>(ws + L.rows);
+    auto* qseg = reinterpret_cast<int2*>(ws + L.qseg);
     hipStream_t s = as_stream(stream);
     const int64_t nblk = (total_q + 255) / 256;
     hipLaunchKernelGGL(plan_rows_qk_kernel, dim3((unsigned)nblk), dim3(256), 0, s, cu_seqlens_q, cu_seqlens_k,
-                       nseg, total_q, total_k, causal ? 1 : 0, rows);
+                       nseg, total_q, total_k, causal ? 1 : 0, rows, qseg);
     hipLaunchKernelGGL(plan_check_qk_kernel, dim3(1), dim3(kCheckThreads), 0, s, cu_seqlens_q, cu_seqlens_k, nseg,
                        total_q, total_k, max_seqlen_q, max_seqlen_k, causal ? 1 : 0, header, (int32_t)L.ntiles,
                        dev_error);
@@ -787,6 +791,7 @@ extern "C" pvc_status pvc_varlen_attn_fwd_qk_planned(const void* q, const void* 
     prm.lse = lse;
     prm.header = reinterpret_cast<const int32_t*>(ws + L.header);
     prm.rows = reinterpret_cast<const int2*>(ws + L.rows);
+    prm.qseg = reinterpret_cast<const int2*>(ws + L.qseg);
     prm.T = total_q;
     prm.Tk = total_k;
     prm.H = heads;

@@ -35,7 +35,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct PlanLayout {
-    size_t header, rows, total;
+    size_t header, rows, qseg, total;
     int64_t ntiles;
 };
 
@@ -46,6 +46,10 @@ inline PlanLayout plan_layout(int64_t T) {
     L.header = off;
     off += align_up(16 * sizeof(int32_t));
     L.rows = off;
+    off += align_up((size_t)T * sizeof(int2));
+    // the query segment of each row, for plans whose row ranges are key rows
+    // (tile order only)
+    L.qseg = off;
     off += align_up((size_t)T * sizeof(int2));
     L.total = off;
     return L;
