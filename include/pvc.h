@@ -183,10 +183,27 @@ pvc_status pvc_rope_thd_apply_interleaved(const void* q_in, void* q_out, const v
                                           const int32_t* cu_seqlens, int32_t nseg, float base,
                                           uint32_t* dev_error, void* stream);
 
+/* Flags of pvc_rope_thd_apply_ex. */
+enum { PVC_ROPE_INTERLEAVED = 1, PVC_ROPE_F16 = 2 };
+
+/* pvc_rope_thd_apply with flags: PVC_ROPE_INTERLEAVED selects the
+ * interleaved pairing; PVC_ROPE_F16 makes q and k fp16 ([charlestar]
+ * "varlen interface": fp16 or bf16 inputs), the one rounding of the double
+ * rotation going to fp16 (nearest even, subnormals kept) instead of bf16.
+ * Unknown flag bits -> PVC_ERR_INVALID_ARG; otherwise as pvc_rope_thd_apply. */
+pvc_status pvc_rope_thd_apply_ex(const void* q_in, void* q_out, const void* k_in, void* k_out,
+                                 int64_t total_tokens, int32_t heads, int32_t head_dim,
+                                 const int32_t* cu_seqlens, int32_t nseg, float base, int32_t flags,
+                                 uint32_t* dev_error, void* stream);
+
 /* ------------------------------------------------------- attention */
 
-/* Output element types of the attention entry points. */
-enum { PVC_OUT_BF16 = 0, PVC_OUT_F32 = 1 };
+/* Element types of the attention entry points (out_dtype / grad_dtype) and of
+ * the cross-entropy logits.  PVC_OUT_BF16 / PVC_OUT_F32: bf16 inputs, bf16 or
+ * fp32 output.  PVC_OUT_F16 / PVC_OUT_F16_F32: fp16 inputs ([charlestar]
+ * "varlen interface": q, k, v in fp16 or bf16), fp16 or fp32 output.  Entry
+ * points that take only some of them say so. */
+enum { PVC_OUT_BF16 = 0, PVC_OUT_F32 = 1, PVC_OUT_F16 = 2, PVC_OUT_F16_F32 = 3 };
 
 /* Bytes of workspace for a plan over `total_tokens` tokens in `nseg` segments. */
 size_t pvc_attn_workspace_size(int64_t total_tokens, int32_t nseg);
@@ -280,18 +297,22 @@ pvc_status pvc_varlen_attn_fwd_qk_planned(const void* q, const void* k, const vo
  * mask).  causal == 0 lets a query see its whole segment.  The softmax scale is
  * fixed at 1/sqrt(head_dim) ([charlestar]: QK^T / sqrt(d)).
  *
- * q, k, v    [total_tokens, heads, head_dim] bf16 (same head count)
- * out        [total_tokens, heads, head_dim], bf16 (out_dtype PVC_OUT_BF16) or
- *            fp32 (PVC_OUT_F32: the same schedule and accumulators, written
- *            before the final bf16 rounding); must not alias q, k or v
+ * q, k, v    [total_tokens, heads, head_dim] (same head count), bf16 for
+ *            out_dtype PVC_OUT_BF16 / PVC_OUT_F32, fp16 for PVC_OUT_F16 /
+ *            PVC_OUT_F16_F32
+ * out        [total_tokens, heads, head_dim], in the input type (PVC_OUT_BF16,
+ *            PVC_OUT_F16) or fp32 (PVC_OUT_F32, PVC_OUT_F16_F32: the same
+ *            schedule and accumulators, written before the final rounding);
+ *            must not alias q, k or v
  * lse        NULL or [heads, total_tokens] fp32: natural-log sum of exponentials
  *            of the scaled scores of each row
  * head_dim   64 or 128; heads * head_dim at most 2^24 (PVC_ERR_INVALID_ARG)
  * total_tokens and causal must be those the plan was built with; otherwise
  * PVC_DEV_PLAN is set and nothing is written.
- * Arithmetic: bf16 MFMA products with fp32 accumulation; probabilities are
- * rounded to bf16 for the P.V product and the row sums use those rounded
- * values.  Deterministic: no atomics, results do not depend on scheduling.
+ * Arithmetic: MFMA products in the input type with fp32 accumulation;
+ * probabilities are rounded to the input type (nearest even) for the P.V
+ * product and the row sums use those rounded values.  Deterministic: no
+ * atomics, results do not depend on scheduling.
  */
 pvc_status pvc_varlen_attn_fwd_planned(const void* q, const void* k, const void* v, void* out,
                                        float* lse, int64_t total_tokens, int32_t heads,
@@ -325,6 +346,7 @@ pvc_status pvc_varlen_attn_fwd(const void* q, const void* k, const void* v, void
  * lse         [heads, total_tokens] fp32, the forward's log-sum-exp (natural log)
  * dq, dk, dv  [total_tokens, heads, head_dim], bf16 (grad_dtype PVC_OUT_BF16) or
  *             fp32 (PVC_OUT_F32, the same schedule before the final rounding);
+ *             bf16 inputs only (fp16 types give PVC_ERR_INVALID_ARG);
  *             must not alias each other, the inputs or the scratch
  * scratch     device buffer of pvc_attn_bwd_scratch_size bytes (overwritten)
  * head_dim    64 or 128; 2 * heads * (total_tokens + 95) * 4 bytes must stay
@@ -351,8 +373,9 @@ pvc_status pvc_varlen_attn_bwd_planned(const void* q, const void* k, const void*
  * mask sets scores to -inf without removing the token, the kernel still sees
  * L).  Only blocks wholly above the causal diagonal are skipped.  out has the
  * input's shape; its padded rows hold attention over the sample's valid keys.
- * seqlens [batch] int32 on the device, each in 1..max_len.  out_dtype as for
- * pvc_varlen_attn_fwd_planned; batch * heads * head_dim at most 2^24.
+ * seqlens [batch] int32 on the device, each in 1..max_len.  out_dtype
+ * PVC_OUT_BF16 or PVC_OUT_F32 (bf16 inputs); batch * heads * head_dim at most
+ * 2^24.
  */
 pvc_status pvc_padded_attn_fwd_sbhd(const void* q, const void* k, const void* v, void* out,
                                     const int32_t* seqlens, int32_t batch, int32_t max_len,
@@ -375,8 +398,8 @@ size_t pvc_ce_workspace_size(int64_t total_tokens);
  * gradient of the loss sum.
  *
  * logits       [total_tokens rows, vocab] on the device, row stride ld
- *              elements (ld >= vocab); bf16 (logits_dtype PVC_OUT_BF16) or
- *              fp32 (PVC_OUT_F32).  Rows whose starts are 16-byte aligned are
+ *              elements (ld >= vocab); bf16 (logits_dtype PVC_OUT_BF16),
+ *              fp16 (PVC_OUT_F16) or fp32 (PVC_OUT_F32).  Rows whose starts are 16-byte aligned are
  *              read as 16-byte vectors, others one value at a time.
  * labels       [total_tokens] int32: the pre-shifted labels of pvc_pack_build
  *              (label[i] is the target of row i; ignore_index where row i
@@ -395,8 +418,8 @@ size_t pvc_ce_workspace_size(int64_t total_tokens);
  *              row that is not a target.
  * seg_loss, seg_count  [nseg] fp64 / int64 out, nullable: the sums over
  *              [cu_r, cu_{r+1}).
- * grad         nullable: [total_tokens, vocab], row stride grad_ld, bf16 or
- *              fp32 (grad_dtype): grad_scale * (softmax(z_i) - onehot(y_i)) on
+ * grad         nullable: [total_tokens, vocab], row stride grad_ld, bf16, fp16
+ *              or fp32 (grad_dtype, the same codes): grad_scale * (softmax(z_i) - onehot(y_i)) on
  *              target rows, 0 on the others.  May be the logits buffer itself
  *              (same dtype and stride: computed in place); otherwise it must
  *              not overlap the logits.  grad_scale finite (for example 1/N or

@@ -70,6 +70,17 @@ def f64_to_bf16_bits(x) -> np.ndarray:
     return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
+def f16_bits_to_f64(bits) -> np.ndarray:
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float64)
+
+
+def f64_to_f16_bits(x) -> np.ndarray:
+    """Round doubles straight to fp16 (11 significant bits, subnormals kept),
+    nearest, ties to even: numpy's double-to-half conversion rounds from the
+    double's own bits (checked against exact rationals by the tests)."""
+    return np.ascontiguousarray(x, np.float64).astype(np.float16).view(np.uint16)
+
+
 def rotate_f64(x: np.ndarray, theta: np.ndarray) -> np.ndarray:
     """Rotate-half rotation in double. x [n, H, d] doubles, theta [n, d/2] fp32 angles."""
     half = x.shape[-1] // 2
@@ -90,12 +101,16 @@ def rotate_interleaved_f64(x: np.ndarray, theta: np.ndarray) -> np.ndarray:
     return y
 
 
-def rope_apply(x_bits: np.ndarray, cu, base: float = 10000.0, rows=None, interleaved: bool = False) -> np.ndarray:
-    """bf16 bits [T, H, d] -> rotated bf16 bits; ``rows`` restricts to those tokens."""
+def rope_apply(x_bits: np.ndarray, cu, base: float = 10000.0, rows=None, interleaved: bool = False,
+               f16: bool = False) -> np.ndarray:
+    """bf16 (or fp16 with ``f16``) bits [T, H, d] -> rotated bits of the same
+    type; ``rows`` restricts to those tokens."""
     pos = positions_from_cu(cu)
     if rows is not None:
         rows = np.asarray(rows, np.int64)
         pos, x_bits = pos[rows], x_bits[rows]
     theta = rope_angles(pos, x_bits.shape[-1], base)
     rot = rotate_interleaved_f64 if interleaved else rotate_f64
+    if f16:
+        return f64_to_f16_bits(rot(f16_bits_to_f64(x_bits), theta))
     return f64_to_bf16_bits(rot(bf16_bits_to_f64(x_bits), theta))

@@ -41,7 +41,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libpvc.so")
 
 OK, ERR_NULL, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(6)
-OUT_BF16, OUT_F32 = 0, 1
+OUT_BF16, OUT_F32, OUT_F16, OUT_F16_F32 = 0, 1, 2, 3
 DEV_ERROR_BITS = {
     1: "CU0", 2: "NOT_INCREASING", 4: "TOTAL", 8: "MAXSEQ", 16: "LENGTH",
     32: "MISMATCH", 64: "RANGE", 128: "PLAN", 256: "LABEL", 512: "PADDED",
@@ -67,6 +67,7 @@ def _load() -> ctypes.CDLL:
         "pvc_validate_cu_seqlens": ([P, I32, I64, I32, P, P, P], I32),
         "pvc_rope_thd_apply": ([P, P, P, P, I64, I32, I32, P, I32, F32, P, P], I32),
         "pvc_rope_thd_apply_interleaved": ([P, P, P, P, I64, I32, I32, P, I32, F32, P, P], I32),
+        "pvc_rope_thd_apply_ex": ([P, P, P, P, I64, I32, I32, P, I32, F32, I32, P, P], I32),
         "pvc_attn_workspace_size": ([I64, I32], SZ),
         "pvc_attn_plan": ([P, I32, I64, I32, I32, P, SZ, P, P], I32),
         "pvc_attn_plan_padded": ([P, P, I32, I64, I32, I32, P, SZ, P, P], I32),
@@ -108,6 +109,25 @@ def _ptr(t: torch.Tensor | None):
 def _stream(stream=None):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _io_code(in_dtype: torch.dtype, out_dtype: torch.dtype) -> int:
+    """The library's out_dtype code for 16-bit inputs of in_dtype."""
+    if in_dtype == torch.bfloat16 and out_dtype in (torch.bfloat16, torch.float32):
+        return OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+    if in_dtype == torch.float16 and out_dtype in (torch.float16, torch.float32):
+        return OUT_F16_F32 if out_dtype == torch.float32 else OUT_F16
+    raise TypeError(f"out_dtype must be the inputs' dtype or torch.float32 (inputs {in_dtype}, out {out_dtype})")
+
+
+def _require16(ts, names) -> torch.dtype:
+    """bf16 or fp16 tensors, all of one dtype; returns it."""
+    dt = ts[0].dtype
+    if dt not in (torch.bfloat16, torch.float16):
+        raise TypeError(f"{names[0]} must be bf16 or fp16")
+    for t, n in zip(ts, names):
+        _require(t, n, dt, 3)
+    return dt
 
 
 def _require(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int | None = None) -> None:
@@ -211,28 +231,29 @@ def rope_thd_apply(q: torch.Tensor, k: torch.Tensor | None, cu_seqlens: torch.Te
                    base: float = 10000.0, q_out: torch.Tensor | None = None,
                    k_out: torch.Tensor | None = None, dev_error: torch.Tensor | None = None,
                    stream=None, interleaved: bool = False):
-    """Per-segment RoPE on bf16 [T, H, d] q (and k).  In place unless outputs are given.
-    Rotate-half pairing, or (x_2j, x_2j+1) pairs with ``interleaved=True``."""
-    _require(q, "q", torch.bfloat16, 3)
+    """Per-segment RoPE on bf16 or fp16 [T, H, d] q (and k).  In place unless
+    outputs are given.  Rotate-half pairing, or (x_2j, x_2j+1) pairs with
+    ``interleaved=True``."""
+    dt = _require16((q,), ("q",))
     _require(cu_seqlens, "cu_seqlens", torch.int32, 1)
     T, H, D = q.shape
     q_out = q if q_out is None else q_out
-    _require(q_out, "q_out", torch.bfloat16, 3)
+    _require(q_out, "q_out", dt, 3)
     if q_out.shape != q.shape:
         raise ValueError("q_out must match q")
     if k is not None:
-        _require(k, "k", torch.bfloat16, 3)
+        _require(k, "k", dt, 3)
         if k.shape != q.shape:
             raise ValueError("k must have q's shape")
         k_out = k if k_out is None else k_out
-        _require(k_out, "k_out", torch.bfloat16, 3)
+        _require(k_out, "k_out", dt, 3)
         if k_out.shape != q.shape:
             raise ValueError("k_out must match k")
     err = dev_error
-    fn = _lib.pvc_rope_thd_apply_interleaved if interleaved else _lib.pvc_rope_thd_apply
-    st = fn(_ptr(q), _ptr(q_out), _ptr(k), _ptr(k_out if k is not None else None),
-                                 T, H, D, _ptr(cu_seqlens), cu_seqlens.numel() - 1, float(base),
-                                 _ptr(err), _stream(stream))
+    flags = (1 if interleaved else 0) | (2 if dt == torch.float16 else 0)
+    st = _lib.pvc_rope_thd_apply_ex(_ptr(q), _ptr(q_out), _ptr(k), _ptr(k_out if k is not None else None),
+                                    T, H, D, _ptr(cu_seqlens), cu_seqlens.numel() - 1, float(base), flags,
+                                    _ptr(err), _stream(stream))
     _check(st, "rope_thd_apply")
     return q_out, (k_out if k is not None else None)
 
@@ -318,21 +339,20 @@ def attn_plan_qk(cu_seqlens_q, cu_seqlens_k, total_q, total_k, max_seqlen_q, max
 def varlen_attn_fwd_qk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                        cu_seqlens_q: torch.Tensor | None = None, cu_seqlens_k: torch.Tensor | None = None,
                        max_seqlen_q: int | None = None, max_seqlen_k: int | None = None, causal: bool = True,
-                       return_lse: bool = False, out_dtype: torch.dtype = torch.bfloat16,
+                       return_lse: bool = False, out_dtype: torch.dtype | None = None,
                        plan: AttnPlanQK | None = None, out: torch.Tensor | None = None, check: bool = False,
                        stream=None):
-    """Prefill attention: q [Tq, H, d] over k, v [Tk, Hkv, d] (H a multiple of
-    Hkv) with separate request boundaries; bottom-right causal alignment."""
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _require(t, name, torch.bfloat16, 3)
+    """Prefill attention: q [Tq, H, d] over k, v [Tk, Hkv, d] (bf16 or fp16, H a
+    multiple of Hkv) with separate request boundaries; bottom-right causal alignment."""
+    in_dt = _require16((q, k, v), ("q", "k", "v"))
     Tq, H, D = q.shape
     Tk, Hkv, Dk = k.shape
     if v.shape != k.shape or Dk != D:
         raise ValueError("k and v must share the shape [Tk, Hkv, d] with q's d")
     if H % Hkv:
         raise ValueError("the query heads must be a multiple of the key / value heads")
-    if out_dtype not in (torch.bfloat16, torch.float32):
-        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+    out_dtype = in_dt if out_dtype is None else out_dtype
+    code = _io_code(in_dt, out_dtype)
     if plan is None:
         if cu_seqlens_q is None or cu_seqlens_k is None or max_seqlen_q is None or max_seqlen_k is None:
             raise ValueError("give both cu_seqlens and max_seqlens, or a plan")
@@ -347,8 +367,8 @@ def varlen_attn_fwd_qk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             raise ValueError("out must be [Tq, H, d] like q")
     lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device) if return_lse else None
     st = _lib.pvc_varlen_attn_fwd_qk_planned(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), Tq, Tk, H, Hkv, D, int(bool(causal)),
-        OUT_F32 if out_dtype == torch.float32 else OUT_BF16, _ptr(plan.workspace), plan.ws_bytes,
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), Tq, Tk, H, Hkv, D, int(bool(causal)), code,
+        _ptr(plan.workspace), plan.ws_bytes,
         _ptr(plan.dev_error), _stream(stream))
     _check(st, "varlen_attn_fwd_qk")
     if check:
@@ -359,21 +379,20 @@ def varlen_attn_fwd_qk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
 def varlen_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                     cu_seqlens: torch.Tensor | None = None, max_seqlen: int | None = None,
                     causal: bool = True, return_lse: bool = False,
-                    out_dtype: torch.dtype = torch.bfloat16, plan: AttnPlan | None = None,
+                    out_dtype: torch.dtype | None = None, plan: AttnPlan | None = None,
                     out: torch.Tensor | None = None, check: bool = False, stream=None):
-    """Block-diagonal attention over THD bf16 q, k, v [T, H, d] (d = 64 or 128).
+    """Block-diagonal attention over THD q, k, v [T, H, d] (bf16 or fp16; d = 64 or 128).
 
     Either ``cu_seqlens`` + ``max_seqlen`` (a plan is built) or a ready ``plan``.
-    Returns out [T, H, d] (bf16, or fp32 with out_dtype=torch.float32) and,
-    with ``return_lse``, lse fp32 [H, T].
+    Returns out [T, H, d] (the inputs' dtype, or fp32 with out_dtype=torch.float32)
+    and, with ``return_lse``, lse fp32 [H, T].
     """
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _require(t, name, torch.bfloat16, 3)
+    in_dt = _require16((q, k, v), ("q", "k", "v"))
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k and v must share the shape [T, H, d]")
     T, H, D = q.shape
-    if out_dtype not in (torch.bfloat16, torch.float32):
-        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+    out_dtype = in_dt if out_dtype is None else out_dtype
+    code = _io_code(in_dt, out_dtype)
     if plan is None:
         if cu_seqlens is None or max_seqlen is None:
             raise ValueError("give cu_seqlens and max_seqlen, or a plan")
@@ -388,9 +407,8 @@ def varlen_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             raise ValueError("out must be [T, H, d] like q")
     lse = torch.empty((H, T), dtype=torch.float32, device=q.device) if return_lse else None
     st = _lib.pvc_varlen_attn_fwd_planned(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), T, H, D, int(bool(causal)),
-        OUT_F32 if out_dtype == torch.float32 else OUT_BF16, _ptr(plan.workspace), plan.ws_bytes,
-        _ptr(plan.dev_error), _stream(stream))
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), T, H, D, int(bool(causal)), code,
+        _ptr(plan.workspace), plan.ws_bytes, _ptr(plan.dev_error), _stream(stream))
     _check(st, "varlen_attn_fwd")
     if check:
         _raise_dev(plan.dev_error, "varlen_attn_fwd")
@@ -488,7 +506,7 @@ def packed_ce_loss(logits: torch.Tensor, labels: torch.Tensor, cu_seqlens: torch
                    dev_error: torch.Tensor | None = None, check: bool = False, stream=None) -> dict:
     """Cross-entropy over packed rows (see pvc_packed_ce_loss in include/pvc.h).
 
-    logits [T, V] bf16 or fp32 (rows may be strided: stride(1) must be 1);
+    logits [T, V] bf16, fp16 or fp32 (rows may be strided: stride(1) must be 1);
     labels [T] int32, the pre-shifted labels of pack_build.  Returns a dict of
     device tensors: loss_sum (fp64 [1]), target_count (int64 [1]), and on
     request row_loss (fp32 [T]), seg_loss / seg_count ([nseg], needs
@@ -496,8 +514,9 @@ def packed_ce_loss(logits: torch.Tensor, labels: torch.Tensor, cu_seqlens: torch
     default the logits' dtype), "inplace" (written over the logits) or a
     caller tensor of the logits' shape.
     """
-    if logits.dtype not in (torch.bfloat16, torch.float32):
-        raise TypeError("logits must be bf16 or fp32")
+    codes = {torch.bfloat16: OUT_BF16, torch.float32: OUT_F32, torch.float16: OUT_F16}
+    if logits.dtype not in codes:
+        raise TypeError("logits must be bf16, fp16 or fp32")
     if logits.device.type != "cuda" or logits.dim() != 2 or logits.stride(1) != 1:
         raise ValueError("logits must be a 2-D GPU tensor with unit stride along the vocabulary")
     T, V = logits.shape
@@ -505,7 +524,7 @@ def packed_ce_loss(logits: torch.Tensor, labels: torch.Tensor, cu_seqlens: torch
     if labels.numel() != T:
         raise ValueError("one label per row")
     dev = logits.device
-    dt = OUT_F32 if logits.dtype == torch.float32 else OUT_BF16
+    dt = codes[logits.dtype]
     nseg = 0
     if cu_seqlens is not None:
         _require(cu_seqlens, "cu_seqlens", torch.int32, 1)
@@ -531,9 +550,9 @@ def packed_ce_loss(logits: torch.Tensor, labels: torch.Tensor, cu_seqlens: torch
             raise ValueError('grad must be None, "new", "inplace" or a tensor')
     elif grad is not None:
         g = grad
-        if g.dtype not in (torch.bfloat16, torch.float32) or g.dim() != 2 or tuple(g.shape) != (T, V) \
+        if g.dtype not in codes or g.dim() != 2 or tuple(g.shape) != (T, V) \
                 or g.stride(1) != 1 or g.device != dev:
-            raise ValueError("grad must be a [T, V] bf16 / fp32 GPU tensor with unit vocabulary stride")
+            raise ValueError("grad must be a [T, V] bf16 / fp16 / fp32 GPU tensor with unit vocabulary stride")
     if g is not None:
         out["grad"] = g
     nb = ce_workspace_size(T)
@@ -545,7 +564,7 @@ def packed_ce_loss(logits: torch.Tensor, labels: torch.Tensor, cu_seqlens: torch
             raise ValueError(f"workspace must hold {nb} bytes (ce_workspace_size)")
     if dev_error is None:
         dev_error = torch.zeros(1, dtype=torch.int32, device=dev)
-    gdt = 0 if g is None else (OUT_F32 if g.dtype == torch.float32 else OUT_BF16)
+    gdt = 0 if g is None else codes[g.dtype]
     st = _lib.pvc_packed_ce_loss(
         _ptr(logits), dt, logits.stride(0), _ptr(labels), T, V, ignore_index, _ptr(cu_seqlens), nseg,
         _ptr(out["loss_sum"]), _ptr(out["target_count"]), _ptr(out.get("row_loss")), _ptr(out.get("seg_loss")),

@@ -207,10 +207,13 @@ struct AttnParams {
 // accumulator is rescaled: probabilities stay below 2^8.
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D, bool CAUSAL, bool OUT_F32, bool SBHD>
+template <int D, bool CAUSAL, bool OUT_F32, bool SBHD, bool F16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void attn_fwd_kernel(AttnParams p) {
     static_assert(D == 64 || D == 128, "head_dim");
+    using E = Elt<F16>;                      // bf16 or fp16 inputs
+    using x8 = typename E::x8;
+    using x2 = typename E::x2;
     constexpr int NS = D / 16;               // MFMA k-steps for q.k
     constexpr int ND = D / 32;               // 32-wide d blocks of the output
     constexpr int ROW_B = D * 2;             // bytes per key row in LDS
@@ -309,11 +312,11 @@ void attn_fwd_kernel(AttnParams p) {
     }
 
     // ---- Q^T operand in registers: lane (c, g) holds Q[row][16s + 8g .. +8]
-    bf16x8 qreg[NS];
+    x8 qreg[NS];
     {
         const uint16_t* qp = p.q + row_off(row) + 8 * g;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+        for (int s = 0; s < NS; ++s) qreg[s] = *reinterpret_cast<const x8*>(qp + 16 * s);
     }
     // The plan header is read in one piece beside the row ranges (all of
     // those loads stay inside their buffers whatever the header holds).
@@ -402,7 +405,6 @@ void attn_fwd_kernel(AttnParams p) {
     float m_run = -INFINITY;
     float l_run = 0.0f;
     const float sl2 = p.scale_log2;
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
     // ---- per-stage work.  A wave takes part in stage st only if some key of
     // the stage is visible to one of its rows; it masks only stages that
@@ -419,15 +421,15 @@ void attn_fwd_kernel(AttnParams p) {
     char* const vbase = kbase + kRing * TILE_B;
 
     // K operand: key 32h + c of the stage in buffer kb, k-step s
-    auto kop = [&](const char* kb, int h, int s) -> bf16x8 {
-        return *reinterpret_cast<const bf16x8*>(kb + k_roff[s] + 32 * h * ROW_B);
+    auto kop = [&](const char* kb, int h, int s) -> x8 {
+        return *reinterpret_cast<const x8*>(kb + k_roff[s] + 32 * h * ROW_B);
     };
     // V^T operand (d block j, 16-key step ks of half h) through the transposing read
-    auto vop = [&](const char* vb, int h, int ks, int j) -> bf16x8 {
+    auto vop = [&](const char* vb, int h, int ks, int j) -> x8 {
         const char* vp = vb + v_roff[j] + (32 * h + 16 * ks) * ROW_B;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vp + 8 * ROW_B));
-        return __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
+        return __builtin_bit_cast(x8, (short __attribute__((ext_vector_type(8)))){
             lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
     };
     // S^T of one stage: one 32-key block per half, chains interleaved
@@ -437,28 +439,28 @@ void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
         for (int s = 0; s < NS; ++s)
 #pragma unroll
-            for (int h = 0; h < NH; ++h) S[h] = mfma32(kop(kb, h, s), qreg[s], S[h]);
+            for (int h = 0; h < NH; ++h) S[h] = E::mfma(kop(kb, h, s), qreg[s], S[h]);
     };
     // O^T += V^T P^T for one stage; P[h][ks] holds the bf16 probabilities of
     // keys 32h + 16ks + 8(e/4) + 4g + e%4 of this lane's query
-    auto pv = [&](const char* vb, const bf16x8 (&P)[NH][2]) {
+    auto pv = [&](const char* vb, const x8 (&P)[NH][2]) {
 #pragma unroll
         for (int h = 0; h < NH; ++h)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                for (int j = 0; j < ND; ++j) acc[j] = mfma32(vop(vb, h, ks, j), P[h][ks], acc[j]);
+                for (int j = 0; j < ND; ++j) acc[j] = E::mfma(vop(vb, h, ks, j), P[h][ks], acc[j]);
     };
     // eight bf16 pairs of one 32-key half into the two B operands of P.V
-    auto pack = [&](const bf16x2 (&pk)[8], bf16x8 (&out)[2]) {
+    auto pack = [&](const x2 (&pk)[8], x8 (&out)[2]) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-            out[ks] = bf16x8{pk[4 * ks][0], pk[4 * ks][1], pk[4 * ks + 1][0], pk[4 * ks + 1][1],
+            out[ks] = x8{pk[4 * ks][0], pk[4 * ks][1], pk[4 * ks + 1][0], pk[4 * ks + 1][1],
                              pk[4 * ks + 2][0], pk[4 * ks + 2][1], pk[4 * ks + 3][0], pk[4 * ks + 3][1]};
     };
-    auto prob_pair = [&](const f32x16& S, int i, float m_use) -> bf16x2 {
-        return bf16x2{(__bf16)__builtin_amdgcn_exp2f(fmaf(S[2 * i], sl2, -m_use)),
-                      (__bf16)__builtin_amdgcn_exp2f(fmaf(S[2 * i + 1], sl2, -m_use))};
+    auto prob_pair = [&](const f32x16& S, int i, float m_use) -> x2 {
+        return E::pair(__builtin_amdgcn_exp2f(fmaf(S[2 * i], sl2, -m_use)),
+                       __builtin_amdgcn_exp2f(fmaf(S[2 * i + 1], sl2, -m_use)));
     };
     // stage max in exp2 units, shared by the lane pair
     auto stage_max = [&](const f32x16 (&S)[NH]) {
@@ -485,7 +487,7 @@ void attn_fwd_kernel(AttnParams p) {
             }
     };
     // softmax of one stage: mask, running max (with rescale), probabilities
-    auto softmax_stage = [&](int st, f32x16 (&S)[NH], bf16x8 (&P)[NH][2]) {
+    auto softmax_stage = [&](int st, f32x16 (&S)[NH], x8 (&P)[NH][2]) {
         if (!stage_full(st)) mask(st, S);
         const float m_st = stage_max(S);
         // move the running max only when it would lag by more than the slack;
@@ -500,14 +502,14 @@ void attn_fwd_kernel(AttnParams p) {
             m_run = grow ? m_st : m_run;
         }
         const float m_use = m_run == -INFINITY ? 0.0f : m_run;
-        bf16x2 pk[NH][8];
+        x2 pk[NH][8];
         float rs = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int h = 0; h < NH; ++h) {
                 pk[h][i] = prob_pair(S[h], i, m_use);
-                rs = __builtin_amdgcn_fdot2_f32_bf16(pk[h][i], ones, rs, false);
+                rs = E::sum2(pk[h][i], rs);
             }
         l_run += rs;
 #pragma unroll
@@ -549,7 +551,7 @@ void attn_fwd_kernel(AttnParams p) {
             if (st + kRing - 1 < nstages) fetch_stage(st + kRing - 1, (SLOT + kRing - 1) % kRing);
             if (stage_active(st)) {
                 f32x16 S[NH];
-                bf16x8 P[NH][2];
+                x8 P[NH][2];
                 qk(kbase + SLOT * TILE_B, S);
                 softmax_stage(st, S, P);
                 pv(vbase + SLOT * TILE_B, P);
@@ -589,8 +591,8 @@ void attn_fwd_kernel(AttnParams p) {
         for (int j = 0; j < ND; ++j)
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
-                const bf16x2 a = {(__bf16)(acc[j][4 * rq] * inv), (__bf16)(acc[j][4 * rq + 1] * inv)};
-                const bf16x2 bb = {(__bf16)(acc[j][4 * rq + 2] * inv), (__bf16)(acc[j][4 * rq + 3] * inv)};
+                const x2 a = E::pair(acc[j][4 * rq] * inv, acc[j][4 * rq + 1] * inv);
+                const x2 bb = E::pair(acc[j][4 * rq + 2] * inv, acc[j][4 * rq + 3] * inv);
                 const int chunk = (4 * j + rq) ^ (c & (CPR - 1));
                 *reinterpret_cast<u32x2*>(ob_lds + c * ROW_B + chunk * 16 + g * 8) =
                         u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, bb)};
@@ -613,19 +615,31 @@ void attn_fwd_kernel(AttnParams p) {
     }
 }
 
-template <int D, bool SBHD>
-pvc_status launch_fwd(const AttnParams& prm, bool causal, bool out_f32, hipStream_t s) {
+template <int D, bool SBHD, bool F16>
+pvc_status launch_fwd_t(const AttnParams& prm, bool causal, bool out_f32, hipStream_t s) {
     const int64_t grid = ((int64_t)prm.items + kNumXcd - 1) / kNumXcd * kNumXcd;
     if (grid > 0x7fffffffLL) return PVC_ERR_INVALID_ARG;
     dim3 g((unsigned)grid), blk(kThreads);
     if (causal) {
-        if (out_f32) hipLaunchKernelGGL((attn_fwd_kernel<D, true, true, SBHD>), g, blk, 0, s, prm);
-        else hipLaunchKernelGGL((attn_fwd_kernel<D, true, false, SBHD>), g, blk, 0, s, prm);
+        if (out_f32) hipLaunchKernelGGL((attn_fwd_kernel<D, true, true, SBHD, F16>), g, blk, 0, s, prm);
+        else hipLaunchKernelGGL((attn_fwd_kernel<D, true, false, SBHD, F16>), g, blk, 0, s, prm);
     } else {
-        if (out_f32) hipLaunchKernelGGL((attn_fwd_kernel<D, false, true, SBHD>), g, blk, 0, s, prm);
-        else hipLaunchKernelGGL((attn_fwd_kernel<D, false, false, SBHD>), g, blk, 0, s, prm);
+        if (out_f32) hipLaunchKernelGGL((attn_fwd_kernel<D, false, true, SBHD, F16>), g, blk, 0, s, prm);
+        else hipLaunchKernelGGL((attn_fwd_kernel<D, false, false, SBHD, F16>), g, blk, 0, s, prm);
     }
     return launch_status();
+}
+
+// out_dtype: PVC_OUT_BF16 / PVC_OUT_F32 for bf16 inputs, PVC_OUT_F16 /
+// PVC_OUT_F16_F32 for fp16 inputs.
+inline bool io_valid(int32_t t) { return t == PVC_OUT_BF16 || t == PVC_OUT_F32 || t == PVC_OUT_F16 || t == PVC_OUT_F16_F32; }
+inline bool io_f16(int32_t t) { return t == PVC_OUT_F16 || t == PVC_OUT_F16_F32; }
+inline bool io_f32(int32_t t) { return t == PVC_OUT_F32 || t == PVC_OUT_F16_F32; }
+
+template <int D>
+pvc_status launch_thd(const AttnParams& prm, bool causal, int32_t out_dtype, hipStream_t s) {
+    if (io_f16(out_dtype)) return launch_fwd_t<D, false, true>(prm, causal, io_f32(out_dtype), s);
+    return launch_fwd_t<D, false, false>(prm, causal, io_f32(out_dtype), s);
 }
 
 // Per-lane staging offsets span one 32-row stage in 32 bits (32 * 2^24 * 2 B).
@@ -697,13 +711,13 @@ extern "C" pvc_status pvc_varlen_attn_fwd_planned(const void* q, const void* k, 
     if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || workspace == nullptr)
         return PVC_ERR_NULL;
     if (total_tokens < 1 || total_tokens > 0x7fffffffLL || heads < 1) return PVC_ERR_INVALID_ARG;
-    if (out_dtype != PVC_OUT_BF16 && out_dtype != PVC_OUT_F32) return PVC_ERR_INVALID_ARG;
+    if (!io_valid(out_dtype)) return PVC_ERR_INVALID_ARG;
     if (head_dim != 64 && head_dim != 128) return PVC_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PVC_ERR_INVALID_ARG;
     const PlanLayout L = plan_layout(total_tokens);
     if (workspace_bytes < L.total) return PVC_ERR_WORKSPACE;
     const size_t in_bytes = (size_t)total_tokens * heads * head_dim * 2;
-    const size_t out_bytes = in_bytes * (out_dtype == PVC_OUT_F32 ? 2 : 1);
+    const size_t out_bytes = in_bytes * (io_f32(out_dtype) ? 2 : 1);
     if (overlaps(out, out_bytes, q, in_bytes) || overlaps(out, out_bytes, k, in_bytes) ||
         overlaps(out, out_bytes, v, in_bytes))
         return PVC_ERR_INVALID_ARG;
@@ -730,9 +744,8 @@ extern "C" pvc_status pvc_varlen_attn_fwd_planned(const void* q, const void* k, 
     prm.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
     prm.dev_error = dev_error;
     hipStream_t s = as_stream(stream);
-    const bool f32 = out_dtype == PVC_OUT_F32;
-    if (head_dim == 128) return launch_fwd<128, false>(prm, causal != 0, f32, s);
-    return launch_fwd<64, false>(prm, causal != 0, f32, s);
+    if (head_dim == 128) return launch_thd<128>(prm, causal != 0, out_dtype, s);
+    return launch_thd<64>(prm, causal != 0, out_dtype, s);
 }
 
 extern "C" pvc_status pvc_attn_plan_qk(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t nseg,
@@ -769,14 +782,14 @@ extern "C" pvc_status pvc_varlen_attn_fwd_qk_planned(const void* q, const void* 
     if (total_q < 1 || total_q > 0x7fffffffLL || total_k < 1 || total_k > 0x7fffffffLL || heads < 1 ||
         kv_heads < 1 || heads % kv_heads != 0)
         return PVC_ERR_INVALID_ARG;
-    if (out_dtype != PVC_OUT_BF16 && out_dtype != PVC_OUT_F32) return PVC_ERR_INVALID_ARG;
+    if (!io_valid(out_dtype)) return PVC_ERR_INVALID_ARG;
     if (head_dim != 64 && head_dim != 128) return PVC_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return PVC_ERR_INVALID_ARG;
     const PlanLayout L = plan_layout(total_q);
     if (workspace_bytes < L.total) return PVC_ERR_WORKSPACE;
     const size_t q_bytes = (size_t)total_q * heads * head_dim * 2;
     const size_t kv_bytes = (size_t)total_k * kv_heads * head_dim * 2;
-    const size_t out_bytes = q_bytes * (out_dtype == PVC_OUT_F32 ? 2 : 1);
+    const size_t out_bytes = q_bytes * (io_f32(out_dtype) ? 2 : 1);
     if (overlaps(out, out_bytes, q, q_bytes) || overlaps(out, out_bytes, k, kv_bytes) ||
         overlaps(out, out_bytes, v, kv_bytes))
         return PVC_ERR_INVALID_ARG;
@@ -803,10 +816,9 @@ extern "C" pvc_status pvc_varlen_attn_fwd_qk_planned(const void* q, const void* 
     prm.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
     prm.dev_error = dev_error;
     hipStream_t s = as_stream(stream);
-    const bool f32 = out_dtype == PVC_OUT_F32;
     // the causal limit is in the plan's row ranges: the kernel runs without its own diagonal
-    if (head_dim == 128) return launch_fwd<128, false>(prm, false, f32, s);
-    return launch_fwd<64, false>(prm, false, f32, s);
+    if (head_dim == 128) return launch_thd<128>(prm, false, out_dtype, s);
+    return launch_thd<64>(prm, false, out_dtype, s);
 }
 
 extern "C" pvc_status pvc_varlen_attn_fwd(const void* q, const void* k, const void* v, void* out,
@@ -817,7 +829,7 @@ extern "C" pvc_status pvc_varlen_attn_fwd(const void* q, const void* k, const vo
                                           void* stream) {
     if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return PVC_ERR_NULL;
     if (head_dim != 64 && head_dim != 128) return PVC_ERR_UNSUPPORTED;
-    if (heads < 1 || (out_dtype != PVC_OUT_BF16 && out_dtype != PVC_OUT_F32)) return PVC_ERR_INVALID_ARG;
+    if (heads < 1 || !io_valid(out_dtype)) return PVC_ERR_INVALID_ARG;
     pvc_status st = pvc_attn_plan(cu_seqlens, nseg, total_tokens, max_seqlen, causal, workspace,
                                   workspace_bytes, dev_error, stream);
     if (st != PVC_OK) return st;
@@ -861,6 +873,6 @@ extern "C" pvc_status pvc_padded_attn_fwd_sbhd(const void* q, const void* k, con
     prm.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
     hipStream_t s = as_stream(stream);
     const bool f32 = out_dtype == PVC_OUT_F32;
-    if (head_dim == 128) return launch_fwd<128, true>(prm, causal != 0, f32, s);
-    return launch_fwd<64, true>(prm, causal != 0, f32, s);
+    if (head_dim == 128) return launch_fwd_t<128, true, false>(prm, causal != 0, f32, s);
+    return launch_fwd_t<64, true, false>(prm, causal != 0, f32, s);
 }

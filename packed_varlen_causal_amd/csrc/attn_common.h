@@ -84,6 +84,38 @@ __device__ inline f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& 
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// The 16-bit element type of q, k, v (and of a 16-bit output): bf16 or fp16.
+// Operands are loaded as raw 16-byte vectors; the type matters only to the
+// MFMA, the probability rounding (nearest even either way), the row-sum dot
+// and the output rounding.
+template <bool F16>
+struct Elt;
+template <>
+struct Elt<false> {
+    using x8 = bf16x8;
+    using x2 = bf16x2;
+    __device__ static x2 pair(float a, float b) { return x2{(__bf16)a, (__bf16)b}; }
+    __device__ static f32x16 mfma(const x8& a, const x8& b, const f32x16& c) { return mfma32(a, b, c); }
+    __device__ static float sum2(const x2& a, float c) {
+        return __builtin_amdgcn_fdot2_f32_bf16(a, x2{(__bf16)1.0f, (__bf16)1.0f}, c, false);
+    }
+};
+template <>
+struct Elt<true> {
+    using x8 = f16x8;
+    using x2 = f16x2;
+    __device__ static x2 pair(float a, float b) { return x2{(_Float16)a, (_Float16)b}; }
+    __device__ static f32x16 mfma(const x8& a, const x8& b, const f32x16& c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    __device__ static float sum2(const x2& a, float c) {
+        return __builtin_amdgcn_fdot2(a, x2{(_Float16)1.0f, (_Float16)1.0f}, c, false);
+    }
+};
+
 // Max over the lane pair (l, l^32): v_permlane32_swap hands each lane its
 // partner's value without a round trip through LDS.
 __device__ inline float lane_pair_max(float x) {

@@ -48,11 +48,12 @@ constexpr float kLn2 = 0.69314718055994531f;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Values per 16-byte vector and their fp32 form.
-template <bool F32>
+// Values per 16-byte vector and their fp32 form; DT is the logits' element
+// type code (PVC_OUT_BF16, PVC_OUT_F32 or PVC_OUT_F16).
+template <int DT>
 struct Vec;
 template <>
-struct Vec<false> {                           // bf16
+struct Vec<PVC_OUT_BF16> {
     static constexpr int N = 8;
     __device__ static void unpack(const u32x4& w, float (&x)[N]) {
 #pragma unroll
@@ -66,7 +67,20 @@ struct Vec<false> {                           // bf16
     }
 };
 template <>
-struct Vec<true> {                            // fp32
+struct Vec<PVC_OUT_F16> {
+    static constexpr int N = 8;
+    __device__ static float h(uint32_t b) { return (float)__builtin_bit_cast(_Float16, uint16_t(b)); }
+    __device__ static void unpack(const u32x4& w, float (&x)[N]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = h(w[i] & 0xFFFFu);
+            x[2 * i + 1] = h(w[i] >> 16);
+        }
+    }
+    __device__ static float scalar(const void* p, int64_t i) { return h(static_cast<const uint16_t*>(p)[i]); }
+};
+template <>
+struct Vec<PVC_OUT_F32> {
     static constexpr int N = 4;
     __device__ static void unpack(const u32x4& w, float (&x)[N]) {
 #pragma unroll
@@ -141,9 +155,17 @@ struct CeParams {
 // thread): they are loaded once, the thread's max is taken over all of them
 // before any exponential, and the gradient pass reads them from registers
 // instead of from memory again.
-template <bool IN_F32, int GRAD /* 0 none, 1 bf16, 2 fp32 */, bool RES>
+// A 16-bit gradient value: bf16 or fp16, nearest even.
+template <int GRAD>
+__device__ inline uint32_t enc16(float g) {
+    if constexpr (GRAD == 3) return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)g);
+    else return (uint32_t)f32_to_bf16_rne(g);
+}
+
+template <int IN_DT, int GRAD /* 0 none, 1 bf16, 2 fp32, 3 fp16 */, bool RES>
 __global__ __launch_bounds__(kCeThreads) void ce_row_kernel(CeParams p, bool vec) {
-    using VT = Vec<IN_F32>;
+    using VT = Vec<IN_DT>;
+    constexpr bool IN_F32 = IN_DT == PVC_OUT_F32;
     constexpr int N = VT::N;
     __shared__ float shm[kCeThreads / 64], shs[kCeThreads / 64];
     const int64_t row = blockIdx.x;
@@ -250,8 +272,8 @@ __global__ __launch_bounds__(kCeThreads) void ce_row_kernel(CeParams p, bool vec
                 uint32_t w[N / 2];
 #pragma unroll
                 for (int q = 0; q < N / 2; ++q)
-                    w[q] = uint32_t(f32_to_bf16_rne(gval(x[2 * q], vi * N + 2 * q))) |
-                           (uint32_t(f32_to_bf16_rne(gval(x[2 * q + 1], vi * N + 2 * q + 1))) << 16);
+                    w[q] = enc16<GRAD>(gval(x[2 * q], vi * N + 2 * q)) |
+                           (enc16<GRAD>(gval(x[2 * q + 1], vi * N + 2 * q + 1)) << 16);
                 if constexpr (N == 8) {
                     reinterpret_cast<u32x4*>(growp)[vi] = u32x4{w[0], w[1], w[2], w[3]};
                 } else {
@@ -270,7 +292,7 @@ __global__ __launch_bounds__(kCeThreads) void ce_row_kernel(CeParams p, bool vec
         for (int i = nvec * N + tid; i < V; i += kCeThreads) {
             const float g = gval(VT::scalar(rowp, i), i);
             if constexpr (GRAD == 2) reinterpret_cast<float*>(growp)[i] = g;
-            else reinterpret_cast<uint16_t*>(growp)[i] = f32_to_bf16_rne(g);
+            else reinterpret_cast<uint16_t*>(growp)[i] = (uint16_t)enc16<GRAD>(g);
         }
     }
 }
@@ -401,20 +423,23 @@ bool ce_overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
-template <bool IN_F32, bool RES>
+template <int IN_DT, bool RES>
 void launch_rows2(const CeParams& prm, bool vec, int grad, hipStream_t s) {
     const dim3 g((unsigned)prm.T), b(kCeThreads);
-    if (grad == 0) hipLaunchKernelGGL((ce_row_kernel<IN_F32, 0, RES>), g, b, 0, s, prm, vec);
-    else if (grad == 1) hipLaunchKernelGGL((ce_row_kernel<IN_F32, 1, RES>), g, b, 0, s, prm, vec);
-    else hipLaunchKernelGGL((ce_row_kernel<IN_F32, 2, RES>), g, b, 0, s, prm, vec);
+    if (grad == 0) hipLaunchKernelGGL((ce_row_kernel<IN_DT, 0, RES>), g, b, 0, s, prm, vec);
+    else if (grad == 1) hipLaunchKernelGGL((ce_row_kernel<IN_DT, 1, RES>), g, b, 0, s, prm, vec);
+    else if (grad == 2) hipLaunchKernelGGL((ce_row_kernel<IN_DT, 2, RES>), g, b, 0, s, prm, vec);
+    else hipLaunchKernelGGL((ce_row_kernel<IN_DT, 3, RES>), g, b, 0, s, prm, vec);
 }
 
-template <bool IN_F32>
+template <int IN_DT>
 void launch_rows(const CeParams& prm, bool vec, int grad, hipStream_t s) {
-    constexpr int N = IN_F32 ? 4 : 8;
-    if (vec && prm.V / N <= kCeResident * kCeThreads) launch_rows2<IN_F32, true>(prm, vec, grad, s);
-    else launch_rows2<IN_F32, false>(prm, vec, grad, s);
+    constexpr int N = IN_DT == PVC_OUT_F32 ? 4 : 8;
+    if (vec && prm.V / N <= kCeResident * kCeThreads) launch_rows2<IN_DT, true>(prm, vec, grad, s);
+    else launch_rows2<IN_DT, false>(prm, vec, grad, s);
 }
+
+inline bool ce_dtype_ok(int32_t t) { return t == PVC_OUT_BF16 || t == PVC_OUT_F32 || t == PVC_OUT_F16; }
 
 }  // namespace
 }  // namespace pvc
@@ -438,9 +463,9 @@ extern "C" pvc_status pvc_packed_ce_loss(const void* logits, int32_t logits_dtyp
         return PVC_ERR_NULL;
     if ((seg_loss != nullptr || seg_count != nullptr) && cu_seqlens == nullptr) return PVC_ERR_NULL;
     if (total_tokens < 1 || total_tokens > 0x7fffffffLL || vocab < 1 || ld < vocab) return PVC_ERR_INVALID_ARG;
-    if (logits_dtype != PVC_OUT_BF16 && logits_dtype != PVC_OUT_F32) return PVC_ERR_INVALID_ARG;
+    if (!ce_dtype_ok(logits_dtype)) return PVC_ERR_INVALID_ARG;
     if (grad != nullptr) {
-        if (grad_dtype != PVC_OUT_BF16 && grad_dtype != PVC_OUT_F32) return PVC_ERR_INVALID_ARG;
+        if (!ce_dtype_ok(grad_dtype)) return PVC_ERR_INVALID_ARG;
         if (grad_ld < vocab || !isfinite(grad_scale)) return PVC_ERR_INVALID_ARG;
     }
     if (cu_seqlens != nullptr && (nseg < 1 || nseg > total_tokens)) return PVC_ERR_INVALID_ARG;
@@ -475,10 +500,11 @@ extern "C" pvc_status pvc_packed_ce_loss(const void* logits, int32_t logits_dtyp
     const bool vec = ce_aligned16(logits) && (ld * esz) % 16 == 0 &&
                      (grad == nullptr ||
                       (ce_aligned16(grad) && (grad_ld * (grad_dtype == PVC_OUT_F32 ? 4 : 2)) % 16 == 0));
-    const int gmode = grad == nullptr ? 0 : (grad_dtype == PVC_OUT_F32 ? 2 : 1);
+    const int gmode = grad == nullptr ? 0 : grad_dtype == PVC_OUT_F32 ? 2 : grad_dtype == PVC_OUT_F16 ? 3 : 1;
     hipStream_t s = as_stream(stream);
-    if (logits_dtype == PVC_OUT_F32) launch_rows<true>(prm, vec, gmode, s);
-    else launch_rows<false>(prm, vec, gmode, s);
+    if (logits_dtype == PVC_OUT_F32) launch_rows<PVC_OUT_F32>(prm, vec, gmode, s);
+    else if (logits_dtype == PVC_OUT_F16) launch_rows<PVC_OUT_F16>(prm, vec, gmode, s);
+    else launch_rows<PVC_OUT_BF16>(prm, vec, gmode, s);
     double* psum = reinterpret_cast<double*>(ws + L.psum);
     long long* pcount = reinterpret_cast<long long*>(ws + L.pcount);
     hipLaunchKernelGGL(ce_reduce_kernel, dim3((unsigned)L.nblk), dim3(kCeThreads), 0, s, prm.row_loss, labels,

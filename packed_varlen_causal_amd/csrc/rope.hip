@@ -54,6 +54,33 @@ __device__ inline uint32_t f64_to_bf16_bits(double y) {
     return fb >> 16;
 }
 
+// Round a double to fp16, nearest even (subnormals included), through fp32
+// round-to-odd (24 bits against fp16's 11).
+__device__ inline uint32_t f64_to_f16_bits(double y) {
+    const float f = (float)y;
+    uint32_t fb = __float_as_uint(f);
+    const double back = (double)f;
+    if (back != y) {
+        if (fabs(back) > fabs(y)) fb -= 1u;
+        fb |= 1u;
+    }
+    const _Float16 h = (_Float16)__uint_as_float(fb);     // v_cvt_f16_f32: nearest even
+    return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+// 16-bit element codec: bf16 (F16 = false) or fp16.
+template <bool F16>
+__device__ inline double in16(uint16_t b) {
+    if constexpr (F16) return (double)(float)__builtin_bit_cast(_Float16, b);
+    else return (double)bf16_to_f32(b);
+}
+template <bool F16>
+__device__ inline uint32_t out16(double y) {
+    if constexpr (F16) return f64_to_f16_bits(y);
+    else return f64_to_bf16_bits(y);
+}
+
+template <bool F16>
 __device__ inline void rotate8(const u32x4& a, const u32x4& b, const double* c, const double* s,
                                u32x4& ya, u32x4& yb) {
     // a holds x_j .. x_{j+7}, b holds x_{j+d/2} .. x_{j+d/2+7}; two bf16 per dword
@@ -63,12 +90,12 @@ __device__ inline void rotate8(const u32x4& a, const u32x4& b, const double* c, 
 #pragma unroll
         for (int hlf = 0; hlf < 2; ++hlf) {
             const int e = 2 * w + hlf;
-            const double x1 = (double)bf16_to_f32(uint16_t(a[w] >> (16 * hlf)));
-            const double x2 = (double)bf16_to_f32(uint16_t(b[w] >> (16 * hlf)));
+            const double x1 = in16<F16>(uint16_t(a[w] >> (16 * hlf)));
+            const double x2 = in16<F16>(uint16_t(b[w] >> (16 * hlf)));
             const double y1 = x1 * c[e] - x2 * s[e];
             const double y2 = x2 * c[e] + x1 * s[e];
-            ra |= f64_to_bf16_bits(y1) << (16 * hlf);
-            rb |= f64_to_bf16_bits(y2) << (16 * hlf);
+            ra |= out16<F16>(y1) << (16 * hlf);
+            rb |= out16<F16>(y2) << (16 * hlf);
         }
         ya[w] = ra;
         yb[w] = rb;
@@ -76,19 +103,20 @@ __device__ inline void rotate8(const u32x4& a, const u32x4& b, const double* c, 
 }
 
 // Interleaved pairs: a holds x_{2j} .. x_{2j+7} (pairs j .. j+3, one per dword).
+template <bool F16>
 __device__ inline u32x4 rotate4_interleaved(const u32x4& a, const double* c, const double* s) {
     u32x4 y;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-        const double x1 = (double)bf16_to_f32(uint16_t(a[w]));
-        const double x2 = (double)bf16_to_f32(uint16_t(a[w] >> 16));
-        y[w] = f64_to_bf16_bits(x1 * c[w] - x2 * s[w]) | (f64_to_bf16_bits(x2 * c[w] + x1 * s[w]) << 16);
+        const double x1 = in16<F16>(uint16_t(a[w]));
+        const double x2 = in16<F16>(uint16_t(a[w] >> 16));
+        y[w] = out16<F16>(x1 * c[w] - x2 * s[w]) | (out16<F16>(x2 * c[w] + x1 * s[w]) << 16);
     }
     return y;
 }
 
 // head_dim a multiple of 16: vectorized path.
-template <bool INTERLEAVED>
+template <bool INTERLEAVED, bool F16>
 __global__ __launch_bounds__(kRopeThreads) void rope_vec_kernel(
         const uint16_t* q_in, uint16_t* q_out, const uint16_t* k_in, uint16_t* k_out, int64_t T,
         int32_t H, int32_t D, const int32_t* __restrict__ cu, int32_t nseg, RopeFreqs freqs,
@@ -131,12 +159,12 @@ __global__ __launch_bounds__(kRopeThreads) void rope_vec_kernel(
             const int64_t row = (i * H + h) * (int64_t)D;
             if constexpr (INTERLEAVED) {
                 const u32x4 a = *reinterpret_cast<const u32x4*>(src + row + 2 * j0);
-                *reinterpret_cast<u32x4*>(dst + row + 2 * j0) = rotate4_interleaved(a, c, s);
+                *reinterpret_cast<u32x4*>(dst + row + 2 * j0) = rotate4_interleaved<F16>(a, c, s);
             } else {
                 const u32x4 a = *reinterpret_cast<const u32x4*>(src + row + j0);
                 const u32x4 b = *reinterpret_cast<const u32x4*>(src + row + half + j0);
                 u32x4 ya, yb;
-                rotate8(a, b, c, s, ya, yb);
+                rotate8<F16>(a, b, c, s, ya, yb);
                 *reinterpret_cast<u32x4*>(dst + row + j0) = ya;
                 *reinterpret_cast<u32x4*>(dst + row + half + j0) = yb;
             }
@@ -145,7 +173,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_vec_kernel(
 }
 
 // Any even head_dim: one thread per (token, pair), heads looped.
-template <bool INTERLEAVED>
+template <bool INTERLEAVED, bool F16>
 __global__ __launch_bounds__(kRopeThreads) void rope_scalar_kernel(
         const uint16_t* q_in, uint16_t* q_out, const uint16_t* k_in, uint16_t* k_out, int64_t T,
         int32_t H, int32_t D, const int32_t* __restrict__ cu, int32_t nseg, RopeFreqs freqs,
@@ -171,10 +199,10 @@ __global__ __launch_bounds__(kRopeThreads) void rope_scalar_kernel(
             const int64_t row = (i * H + h) * (int64_t)D;
             const int64_t e1 = INTERLEAVED ? row + 2 * j : row + j;
             const int64_t e2 = INTERLEAVED ? row + 2 * j + 1 : row + half + j;
-            const double x1 = (double)bf16_to_f32(src[e1]);
-            const double x2 = (double)bf16_to_f32(src[e2]);
-            dst[e1] = (uint16_t)f64_to_bf16_bits(x1 * cs - x2 * sn);
-            dst[e2] = (uint16_t)f64_to_bf16_bits(x2 * cs + x1 * sn);
+            const double x1 = in16<F16>(src[e1]);
+            const double x2 = in16<F16>(src[e2]);
+            dst[e1] = (uint16_t)out16<F16>(x1 * cs - x2 * sn);
+            dst[e2] = (uint16_t)out16<F16>(x2 * cs + x1 * sn);
         }
     }
 }
@@ -186,9 +214,21 @@ using namespace pvc;
 
 namespace {
 
+template <bool INTERLEAVED, bool F16>
+void rope_launch(bool vec, int64_t nblk, hipStream_t s, const uint16_t* qi, uint16_t* qo, const uint16_t* ki,
+                 uint16_t* ko, int64_t T, int32_t H, int32_t D, const int32_t* cu, int32_t nseg,
+                 const RopeFreqs& freqs, uint32_t* dev_error) {
+    if (vec)
+        hipLaunchKernelGGL((rope_vec_kernel<INTERLEAVED, F16>), dim3((unsigned)nblk), dim3(kRopeThreads), 0, s, qi,
+                           qo, ki, ko, T, H, D, cu, nseg, freqs, dev_error);
+    else
+        hipLaunchKernelGGL((rope_scalar_kernel<INTERLEAVED, F16>), dim3((unsigned)nblk), dim3(kRopeThreads), 0, s,
+                           qi, qo, ki, ko, T, H, D, cu, nseg, freqs, dev_error);
+}
+
 pvc_status rope_apply(const void* q_in, void* q_out, const void* k_in, void* k_out, int64_t total_tokens,
                       int32_t heads, int32_t head_dim, const int32_t* cu_seqlens, int32_t nseg, float base,
-                      bool interleaved, uint32_t* dev_error, void* stream) {
+                      bool interleaved, bool f16, uint32_t* dev_error, void* stream) {
     if (q_in == nullptr || q_out == nullptr || cu_seqlens == nullptr) return PVC_ERR_NULL;
     if ((k_in == nullptr) != (k_out == nullptr)) return PVC_ERR_NULL;
     if (total_tokens < 1 || total_tokens > 0x7fffffffLL || heads < 1 || nseg < 1)
@@ -206,25 +246,22 @@ pvc_status rope_apply(const void* q_in, void* q_out, const void* k_in, void* k_o
     auto* ko = static_cast<uint16_t*>(k_out);
     const bool aligned = ((reinterpret_cast<uintptr_t>(q_in) | reinterpret_cast<uintptr_t>(q_out) |
                            reinterpret_cast<uintptr_t>(k_in) | reinterpret_cast<uintptr_t>(k_out)) & 15u) == 0;
-    if (head_dim % 16 == 0 && aligned) {
+    const bool vec = head_dim % 16 == 0 && aligned;
+    int64_t threads;
+    if (vec) {
         const int64_t hgroups = (heads + kHeadsPerThread - 1) / kHeadsPerThread;
-        const int64_t threads = total_tokens * (head_dim / (interleaved ? 8 : 16)) * hgroups;
-        const int64_t nblk = (threads + kRopeThreads - 1) / kRopeThreads;
-        if (interleaved)
-            hipLaunchKernelGGL(rope_vec_kernel<true>, dim3((unsigned)nblk), dim3(kRopeThreads), 0, s, qi, qo, ki,
-                               ko, total_tokens, heads, head_dim, cu_seqlens, nseg, freqs, dev_error);
-        else
-            hipLaunchKernelGGL(rope_vec_kernel<false>, dim3((unsigned)nblk), dim3(kRopeThreads), 0, s, qi, qo,
-                               ki, ko, total_tokens, heads, head_dim, cu_seqlens, nseg, freqs, dev_error);
+        threads = total_tokens * (head_dim / (interleaved ? 8 : 16)) * hgroups;
     } else {
-        const int64_t threads = total_tokens * (head_dim / 2);
-        const int64_t nblk = (threads + kRopeThreads - 1) / kRopeThreads;
-        if (interleaved)
-            hipLaunchKernelGGL(rope_scalar_kernel<true>, dim3((unsigned)nblk), dim3(kRopeThreads), 0, s, qi, qo,
-                               ki, ko, total_tokens, heads, head_dim, cu_seqlens, nseg, freqs, dev_error);
-        else
-            hipLaunchKernelGGL(rope_scalar_kernel<false>, dim3((unsigned)nblk), dim3(kRopeThreads), 0, s, qi,
-                               qo, ki, ko, total_tokens, heads, head_dim, cu_seqlens, nseg, freqs, dev_error);
+        threads = total_tokens * (head_dim / 2);
+    }
+    const int64_t nblk = (threads + kRopeThreads - 1) / kRopeThreads;
+    const int64_t T = total_tokens;
+    if (interleaved) {
+        if (f16) rope_launch<true, true>(vec, nblk, s, qi, qo, ki, ko, T, heads, head_dim, cu_seqlens, nseg, freqs, dev_error);
+        else rope_launch<true, false>(vec, nblk, s, qi, qo, ki, ko, T, heads, head_dim, cu_seqlens, nseg, freqs, dev_error);
+    } else {
+        if (f16) rope_launch<false, true>(vec, nblk, s, qi, qo, ki, ko, T, heads, head_dim, cu_seqlens, nseg, freqs, dev_error);
+        else rope_launch<false, false>(vec, nblk, s, qi, qo, ki, ko, T, heads, head_dim, cu_seqlens, nseg, freqs, dev_error);
     }
     return launch_status();
 }
@@ -236,7 +273,7 @@ extern "C" pvc_status pvc_rope_thd_apply(const void* q_in, void* q_out, const vo
                                          const int32_t* cu_seqlens, int32_t nseg, float base,
                                          uint32_t* dev_error, void* stream) {
     return rope_apply(q_in, q_out, k_in, k_out, total_tokens, heads, head_dim, cu_seqlens, nseg, base, false,
-                      dev_error, stream);
+                      false, dev_error, stream);
 }
 
 extern "C" pvc_status pvc_rope_thd_apply_interleaved(const void* q_in, void* q_out, const void* k_in,
@@ -244,5 +281,14 @@ extern "C" pvc_status pvc_rope_thd_apply_interleaved(const void* q_in, void* q_o
                                                      int32_t head_dim, const int32_t* cu_seqlens, int32_t nseg,
                                                      float base, uint32_t* dev_error, void* stream) {
     return rope_apply(q_in, q_out, k_in, k_out, total_tokens, heads, head_dim, cu_seqlens, nseg, base, true,
-                      dev_error, stream);
+                      false, dev_error, stream);
+}
+
+extern "C" pvc_status pvc_rope_thd_apply_ex(const void* q_in, void* q_out, const void* k_in, void* k_out,
+                                            int64_t total_tokens, int32_t heads, int32_t head_dim,
+                                            const int32_t* cu_seqlens, int32_t nseg, float base, int32_t flags,
+                                            uint32_t* dev_error, void* stream) {
+    if (flags & ~(PVC_ROPE_INTERLEAVED | PVC_ROPE_F16)) return PVC_ERR_INVALID_ARG;
+    return rope_apply(q_in, q_out, k_in, k_out, total_tokens, heads, head_dim, cu_seqlens, nseg, base,
+                      (flags & PVC_ROPE_INTERLEAVED) != 0, (flags & PVC_ROPE_F16) != 0, dev_error, stream);
 }

@@ -42,7 +42,7 @@ def test_header_declares_the_hot_path():
                  "pvc_attn_workspace_size", "pvc_pack_build_workspace_size", "pvc_status_string",
                  "pvc_varlen_attn_bwd_planned", "pvc_attn_bwd_scratch_size", "pvc_packed_ce_loss",
                  "pvc_ce_workspace_size", "pvc_attn_plan_padded", "pvc_rope_thd_apply_interleaved",
-                 "pvc_attn_plan_qk", "pvc_varlen_attn_fwd_qk_planned"):
+                 "pvc_attn_plan_qk", "pvc_varlen_attn_fwd_qk_planned", "pvc_rope_thd_apply_ex"):
         assert must in names
 
 
@@ -122,6 +122,10 @@ def test_null_and_range_checks_return_before_gpu_work(lib):
     assert lib.pvc_rope_thd_apply(fake, fake, None, None, 9, 2, 63, fake, 3, 1e4, None, None) == 3
     assert lib.pvc_rope_thd_apply(fake, fake, None, None, 9, 2, 512, fake, 3, 1e4, None, None) == 3
     assert lib.pvc_rope_thd_apply(fake, fake, None, None, 9, 2, 64, fake, 3, -1.0, None, None) == 2
+    lib.pvc_rope_thd_apply_ex.restype = I32
+    lib.pvc_rope_thd_apply_ex.argtypes = [P, P, P, P, I64, I32, I32, P, I32, F32, I32, P, P]
+    assert lib.pvc_rope_thd_apply_ex(fake, fake, None, None, 9, 2, 64, fake, 3, 1e4, 4, None, None) == 2
+    assert lib.pvc_rope_thd_apply_ex(fake, fake, None, None, 9, 2, 63, fake, 3, 1e4, 3, None, None) == 3
 
     lib.pvc_attn_plan.restype = I32
     lib.pvc_attn_plan.argtypes = [P, I32, I64, I32, I32, P, SZ, P, P]
@@ -152,6 +156,7 @@ def test_null_and_range_checks_return_before_gpu_work(lib):
     a, b, c, o = (_vp(0x100000 * (i + 1)) for i in range(4))
     assert lib.pvc_varlen_attn_fwd_planned(a, b, c, o, None, 9, 2, 96, 1, 0, fake, 1 << 20, None, None) == 3
     assert lib.pvc_varlen_attn_fwd_planned(a, b, c, o, None, 9, 2, 64, 1, 7, fake, 1 << 20, None, None) == 2
+    assert lib.pvc_varlen_attn_fwd_planned(a, b, c, o, None, 9, 2, 64, 1, 4, fake, 1 << 20, None, None) == 2
     assert lib.pvc_varlen_attn_fwd_planned(a, b, c, None, None, 9, 2, 64, 1, 0, fake, 1 << 20, None, None) == 1
     # misaligned q
     assert lib.pvc_varlen_attn_fwd_planned(_vp(0x100002), b, c, o, None, 9, 2, 64, 1, 0, fake, 1 << 20,
@@ -186,6 +191,7 @@ def test_null_and_range_checks_return_before_gpu_work(lib):
     assert bwd(ptrs=g[:9] + [None]) == 1
     assert bwd(D=96) == 3
     assert bwd(gd=5) == 2
+    assert bwd(gd=2) == 2                                      # no fp16 backward
     assert bwd(T=0) == 2
     assert bwd(ws=8) == 4
     assert bwd(sc=8) == 4

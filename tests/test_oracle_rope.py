@@ -161,3 +161,40 @@ def test_interleaved_shift_invariance():
         a = rot(q, ((m + c) * f)[None]).ravel() @ rot(k, ((n + c) * f)[None]).ravel()
         b = q.ravel() @ rot(k, ((n - m) * f)[None]).ravel()
         assert abs(a - b) <= 1e-9 * max(1.0, abs(b))
+
+
+def test_f16_rounding_against_exact_nearest():
+    """f64 -> fp16 rounding against exact rationals: the nearer neighbour on the
+    fp16 grid (11 significant bits; a fixed 2^-24 spacing below 2^-14), ties to
+    the even last bit, including subnormals and exact ties."""
+    rng = np.random.default_rng(8)
+    xs = np.concatenate([rng.standard_normal(2000) * 4,
+                         rng.standard_normal(500) * 1e-6,                       # fp16 subnormal range
+                         1 + (np.arange(200) * 2 + 1) / 2048.0,                 # exact ties at 1..2
+                         (np.arange(1, 101) * 2 + 1) * 2.0 ** -25])            # exact subnormal ties
+    got = R.f64_to_f16_bits(xs)
+    for x, g in zip(xs.tolist(), got.tolist()):
+        fx = abs(Fraction(x))
+        e = max(math.frexp(abs(x))[1] - 1, -14) if x != 0 else -14
+        ulp = Fraction(2) ** (e - 10)
+        lo = (fx // ulp) * ulp
+        hi = lo + ulp
+        dl, dh = fx - lo, hi - fx
+        pick = lo if (dl < dh or (dl == dh and (lo / ulp) % 2 == 0)) else hi
+        pick = -pick if x < 0 else pick
+        gv = float(np.asarray([g], np.uint16).view(np.float16)[0])
+        assert Fraction(gv) == pick, (x, gv, float(pick))
+
+
+def test_f16_rope_matches_the_same_rotation_rounded_to_fp16():
+    """The fp16 path rotates the fp16 input values and rounds once to fp16;
+    position 0 is the identity."""
+    rng = np.random.default_rng(9)
+    x16 = (rng.standard_normal((20, 2, 16)) * 3).astype(np.float16)
+    bits = x16.view(np.uint16)
+    cu = np.array([0, 7, 20])
+    y = R.rope_apply(bits, cu, 500.0, f16=True)
+    theta = R.rope_angles(P.positions_from_cu(cu), 16, 500.0)
+    want = R.rotate_f64(x16.astype(np.float64), theta).astype(np.float16).view(np.uint16)
+    assert (y == want).all()
+    assert (y[[0, 7]] == bits[[0, 7]]).all()
