@@ -349,7 +349,7 @@ pvc_status pvc_varlen_attn_fwd(const void* q, const void* k, const void* v, void
  *             bf16 inputs only (fp16 types give PVC_ERR_INVALID_ARG);
  *             must not alias each other, the inputs or the scratch
  * scratch     device buffer of pvc_attn_bwd_scratch_size bytes (overwritten)
- * head_dim    64 or 128; 2 * heads * (total_tokens + 95) * 4 bytes must stay
+ * head_dim    64 or 128; 2 * heads * (total_tokens + 159) * 4 bytes must stay
  *             below 4 GiB (PVC_ERR_INVALID_ARG otherwise)
  * total_tokens and causal must be those the plan was built with; otherwise
  * PVC_DEV_PLAN is set and nothing is written.  All pointers 16-byte aligned.

@@ -66,9 +66,10 @@ struct BwdParams {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Scratch rows per head: T rounded up to the stage size plus two stages, so
-// every 32-row block a stage reads lies inside the plane.
-inline int64_t scratch_rows(int64_t T) { return (T + kBN - 1) / kBN * kBN + 2 * kBN; }
+// Scratch rows per head: T rounded up to 32 rows plus 128, so every block of
+// up to 128 rows a stage reads lies inside the plane.
+constexpr int kScratchPad = 4 * kBN;
+inline int64_t scratch_rows(int64_t T) { return (T + kBN - 1) / kBN * kBN + kScratchPad; }
 
 #ifndef PVC_DQ_RING
 #define PVC_DQ_RING 2
@@ -76,6 +77,10 @@ inline int64_t scratch_rows(int64_t T) { return (T + kBN - 1) / kBN * kBN + 2 * 
 #ifndef PVC_DKDV_RING
 #define PVC_DKDV_RING 3
 #endif
+#ifndef PVC_DQ_HALVES
+#define PVC_DQ_HALVES 1
+#endif
+constexpr int kDqHalves = PVC_DQ_HALVES;    // 32-key halves per dQ stage
 constexpr int kDqRing = PVC_DQ_RING;        // stage buffers of the dQ kernel
 constexpr int kDkdvRing = PVC_DKDV_RING;    // stage buffers of the dK/dV kernel
 
@@ -149,7 +154,9 @@ template <int D, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdParams p) {
     static_assert(D == 64 || D == 128, "head_dim");
-    static_assert(kBN == 32, "one 32-key block per stage");
+    static_assert(kBN == 32, "32-key halves");
+    constexpr int NH = kDqHalves;
+    constexpr int SKEYS = NH * kBN;                 // keys per stage
     constexpr int NS = D / 16;
     constexpr int ND = D / 32;
     constexpr int ROW_B = D * 2;
@@ -161,7 +168,7 @@ void bwd_dq_kernel(BwdParams p) {
     constexpr int L16 = ROW_B / 16;
     constexpr int CHUNK_ROWS = kWaves * ROWS_PER_CHUNK;
     static_assert(CHUNK_ROWS % 16 == 0, "swizzle period");
-    __shared__ __attribute__((aligned(1024))) uint16_t sKV[2 * kDqRing * kBN * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t sKV[2 * kDqRing * SKEYS * D];
 
     const int logical = xcd_logical();
     if (logical >= p.items) return;
@@ -216,17 +223,17 @@ void bwd_dq_kernel(BwdParams p) {
     bool sealed;
     const bool plan_ok = plan_sealed(p, CAUSAL, sealed);
     if (!sealed && tid == 0) raise_error(p.dev_error, PVC_DEV_PLAN);
-    const int nstages = plan_ok ? (k_hi - k_lo + kBN - 1) / kBN : 0;
+    const int nstages = plan_ok ? (k_hi - k_lo + SKEYS - 1) / SKEYS : 0;
 
-    // ---- K and V stages, both with the K swizzle (both are read as A
-    // operands row by row; K is also read transposed)
+    // ---- K and V stages, both with the swizzle for tiles read both ways
+    // (both are read as A operands row by row; K is also read transposed)
     const int64_t row_stride = (int64_t)H * D;
     const int64_t head_off = (int64_t)head * D;
     const int fetch_rr = wave * ROWS_PER_CHUNK + lane / L16;
     const uint32_t loff =
-            (uint32_t)((fetch_rr * row_stride + ((lane % L16) ^ k_swz<D>(fetch_rr)) * 8) * 2);
+            (uint32_t)((fetch_rr * row_stride + ((lane % L16) ^ t_swz<D>(fetch_rr)) * 8) * 2);
     char* const kbase = reinterpret_cast<char*>(&sKV[0]);
-    char* const vbase = kbase + kDqRing * TILE_B;
+    char* const vbase = kbase + kDqRing * NH * TILE_B;
     auto fetch_rows = [&](const uint16_t* src, lds_char* dst, int kt) {
         const char* base = reinterpret_cast<const char*>(src) + ((int64_t)kt * row_stride + head_off) * 2;
         const int64_t chunk_step = (int64_t)CHUNK_ROWS * row_stride * 2;
@@ -248,11 +255,14 @@ void bwd_dq_kernel(BwdParams p) {
     lds_char* const k_lds = (lds_char*)kbase;
     lds_char* const v_lds = (lds_char*)vbase;
     auto fetch_stage = [&](int st, int slot) {
-        fetch_rows(p.k, k_lds + slot * TILE_B, k_lo + st * kBN);
-        fetch_rows(p.v, v_lds + slot * TILE_B, k_lo + st * kBN);
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            fetch_rows(p.k, k_lds + (slot * NH + h) * TILE_B, k_lo + st * SKEYS + h * kBN);
+            fetch_rows(p.v, v_lds + (slot * NH + h) * TILE_B, k_lo + st * SKEYS + h * kBN);
+        }
     };
 
-    // ---- LDS read offsets (K swizzle: 16-byte piece ^ k_swz(row))
+    // ---- LDS read offsets (16-byte piece ^ t_swz(row))
     //   row read (A operand): row c, piece 2s + g
     //   transposing read: rows 16ks + 8hh + 4g + li/4, d = 32j + 16chi + 4(li%4)
     uint32_t r_off[NS], t_off[ND][2];
@@ -260,13 +270,13 @@ void bwd_dq_kernel(BwdParams p) {
         const int li = lane & 15;
         const int chi = (lane >> 4) & 1;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) r_off[s] = c * ROW_B + (((2 * s + g) ^ k_swz<D>(c)) << 4);
+        for (int s = 0; s < NS; ++s) r_off[s] = c * ROW_B + (((2 * s + g) ^ t_swz<D>(c)) << 4);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int rl = 4 * g + (li >> 2) + 8 * hh;
 #pragma unroll
             for (int j = 0; j < ND; ++j)
-                t_off[j][hh] = rl * ROW_B + (((4 * j + 2 * chi + ((li & 3) >> 1)) ^ k_swz<D>(rl)) << 4) +
+                t_off[j][hh] = rl * ROW_B + (((4 * j + 2 * chi + ((li & 3) >> 1)) ^ t_swz<D>(rl)) << 4) +
                                ((li & 1) << 3);
         }
     }
@@ -285,46 +295,59 @@ void bwd_dq_kernel(BwdParams p) {
     const int vis_end = CAUSAL ? min(end_l, row + 1) : end_l;
 
     auto stage_active = [&](int st) -> bool {
-        const int kt = k_lo + st * kBN;
-        return wave_active && kt < w_hi && kt + kBN > w_lo;
+        const int kt = k_lo + st * SKEYS;
+        return wave_active && kt < w_hi && kt + SKEYS > w_lo;
     };
-    auto stage_full = [&](int st) -> bool {
-        const int kt = k_lo + st * kBN;
+    auto half_full = [&](int kt) -> bool {
         return kt >= max_start && kt + kBN <= min_end && (!CAUSAL || kt + kBN - 1 <= wr0);
     };
-    auto stage = [&](int st, const char* kb, const char* vb) __attribute__((always_inline)) {
-        f32x16 S = f32x16(0.0f), dP = f32x16(0.0f);
+    // one stage: S^T and dP^T of every half first, so one half's MFMA chains
+    // overlap the other's exponentials
+    auto stage = [&](int st, int slot) __attribute__((always_inline)) {
+        f32x16 S[NH], dP[NH];
+        static_for<NH>([&](auto H_) {
+            constexpr int h = decltype(H_)::value;
+            const char* kb = kbase + (slot * NH + h) * TILE_B;
+            const char* vb = vbase + (slot * NH + h) * TILE_B;
+            S[h] = f32x16(0.0f);
+            dP[h] = f32x16(0.0f);
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            S = mfma32(rop(kb, s), qreg[s], S);          // S^T = K Q^T
-            dP = mfma32(rop(vb, s), doreg[s], dP);       // dP^T = V dO^T
-        }
-        if (!stage_full(st)) {
-            const int x0 = k_lo + st * kBN + 4 * g;
-            const int lo = start_l - x0, hi = vis_end - x0;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int C = 8 * (r >> 2) + (r & 3);
-                S[r] = ((C >= lo) & (C < hi)) ? S[r] : -INFINITY;
+            for (int s = 0; s < NS; ++s) {
+                S[h] = mfma32(rop(kb, s), qreg[s], S[h]);          // S^T = K Q^T
+                dP[h] = mfma32(rop(vb, s), doreg[s], dP[h]);       // dP^T = V dO^T
             }
-        }
-        // dS^T = P^T o (dP^T - D); keys 16ks + 8(e/4) + 4g + e%4 of pack ks
-        bf16x2 pk[8];
+        });
+        static_for<NH>([&](auto H_) {
+            constexpr int h = decltype(H_)::value;
+            const int kt = k_lo + st * SKEYS + h * kBN;
+            if (!half_full(kt)) {
+                const int x0 = kt + 4 * g;
+                const int lo = start_l - x0, hi = vis_end - x0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(S[2 * i], sl2, -lse2));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(S[2 * i + 1], sl2, -lse2));
-            pk[i] = bf16x2{(__bf16)(p0 * (dP[2 * i] - dlt)), (__bf16)(p1 * (dP[2 * i + 1] - dlt))};
-        }
-        bf16x8 ds[2];
+                for (int r = 0; r < 16; ++r) {
+                    const int C = 8 * (r >> 2) + (r & 3);
+                    S[h][r] = ((C >= lo) & (C < hi)) ? S[h][r] : -INFINITY;
+                }
+            }
+            // dS^T = P^T o (dP^T - D); keys 16ks + 8(e/4) + 4g + e%4 of pack ks
+            bf16x2 pk[8];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            ds[ks] = bf16x8{pk[4 * ks][0], pk[4 * ks][1], pk[4 * ks + 1][0], pk[4 * ks + 1][1],
-                            pk[4 * ks + 2][0], pk[4 * ks + 2][1], pk[4 * ks + 3][0], pk[4 * ks + 3][1]};
+            for (int i = 0; i < 8; ++i) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(S[h][2 * i], sl2, -lse2));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(S[h][2 * i + 1], sl2, -lse2));
+                pk[i] = bf16x2{(__bf16)(p0 * (dP[h][2 * i] - dlt)), (__bf16)(p1 * (dP[h][2 * i + 1] - dlt))};
+            }
+            bf16x8 ds[2];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+            for (int ks = 0; ks < 2; ++ks)
+                ds[ks] = bf16x8{pk[4 * ks][0], pk[4 * ks][1], pk[4 * ks + 1][0], pk[4 * ks + 1][1],
+                                pk[4 * ks + 2][0], pk[4 * ks + 2][1], pk[4 * ks + 3][0], pk[4 * ks + 3][1]};
+            const char* kb = kbase + (slot * NH + h) * TILE_B;
 #pragma unroll
-            for (int j = 0; j < ND; ++j) acc[j] = mfma32(top(kb, ks, j), ds[ks], acc[j]);   // dQ^T += K^T dS^T
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int j = 0; j < ND; ++j) acc[j] = mfma32(top(kb, ks, j), ds[ks], acc[j]);   // dQ^T += K^T dS^T
+        });
     };
 
     // stages through a ring of kDqRing K and V buffers: stage st is computed
@@ -338,10 +361,10 @@ void bwd_dq_kernel(BwdParams p) {
             constexpr int SLOT = decltype(I)::value;
             const int st = st0 + SLOT;
             if (st >= nstages) return;
-            wait_stages<RING, 2 * CPW>(min(RING - 2, nstages - 1 - st));   // stage st has landed
+            wait_stages<RING, 2 * NH * CPW>(min(RING - 2, nstages - 1 - st));   // stage st has landed
             __syncthreads();
             if (st + RING - 1 < nstages) fetch_stage(st + RING - 1, (SLOT + RING - 1) % RING);
-            if (stage_active(st)) stage(st, kbase + SLOT * TILE_B, vbase + SLOT * TILE_B);
+            if (stage_active(st)) stage(st, SLOT);
         });
     }
 
@@ -363,7 +386,7 @@ void bwd_dq_kernel(BwdParams p) {
     } else {
         // through LDS for whole-row stores, as in the forward
         constexpr int CPR = ROW_B / 16;
-        static_assert(kBM * ROW_B <= 2 * kDqRing * TILE_B, "output tile fits the stage buffers");
+        static_assert(kBM * ROW_B <= 2 * kDqRing * NH * TILE_B, "output tile fits the stage buffers");
         __syncthreads();
         char* const ob = kbase + wave * 32 * ROW_B;
 #pragma unroll
@@ -398,7 +421,7 @@ void bwd_dkdv_kernel(BwdParams p) {
     static_assert(D == 64 || D == 128, "head_dim");
     static_assert(kBN == 32, "32-query halves");
     constexpr int SROWS = NH * kBN;               // query rows per stage
-    static_assert(SROWS <= 64, "the lse / D planes are padded by 64 rows");
+    static_assert(SROWS <= kScratchPad, "the lse / D planes are padded past T by kScratchPad rows");
     constexpr int NS = D / 16;
     constexpr int ND = D / 32;
     constexpr int ROW_B = D * 2;
@@ -468,12 +491,12 @@ void bwd_dkdv_kernel(BwdParams p) {
     if (!sealed && tid == 0) raise_error(p.dev_error, PVC_DEV_PLAN);
     const int nstages = plan_ok ? (q_hi - q_lo + SROWS - 1) / SROWS : 0;
 
-    // ---- Q and dO stages (K swizzle), lse and D blocks (128 bytes each)
+    // ---- Q and dO stages (swizzled by t_swz), lse and D blocks (128 bytes each)
     const int64_t row_stride = (int64_t)H * D;
     const int64_t head_off = (int64_t)head * D;
     const int fetch_rr = wave * ROWS_PER_CHUNK + lane / L16;
     const uint32_t loff =
-            (uint32_t)((fetch_rr * row_stride + ((lane % L16) ^ k_swz<D>(fetch_rr)) * 8) * 2);
+            (uint32_t)((fetch_rr * row_stride + ((lane % L16) ^ t_swz<D>(fetch_rr)) * 8) * 2);
     char* const qbase = reinterpret_cast<char*>(&sQO[0]);
     char* const obase = qbase + kDkdvRing * NH * TILE_B;
     auto fetch_rows = [&](const uint16_t* src, lds_char* dst, int kt) {
@@ -500,8 +523,8 @@ void bwd_dkdv_kernel(BwdParams p) {
     // [half][plane][8 pieces]; every wave loads 4 NH of them (lanes 0 ..
     // 4 NH - 1), so all waves issue the same number of loads per stage.
     // Piece P = 4 NH wave + lane holds rows qt + 32 (P / 16) + 4 (P % 8) .. +3
-    // of plane (P / 8) % 2 (the planes are padded by 64 rows past T, so every
-    // piece lies inside them).
+    // of plane (P / 8) % 2 (the planes are padded by kScratchPad rows past T,
+    // so every piece lies inside them).
     const char* const sbase = reinterpret_cast<const char*>(p.scratch);
     constexpr int PPW = 4 * NH;                      // pieces per wave
     const int piece = PPW * wave + (lane & (PPW - 1));
@@ -524,13 +547,13 @@ void bwd_dkdv_kernel(BwdParams p) {
         const int li = lane & 15;
         const int chi = (lane >> 4) & 1;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) r_off[s] = c * ROW_B + (((2 * s + g) ^ k_swz<D>(c)) << 4);
+        for (int s = 0; s < NS; ++s) r_off[s] = c * ROW_B + (((2 * s + g) ^ t_swz<D>(c)) << 4);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int rl = 4 * g + (li >> 2) + 8 * hh;
 #pragma unroll
             for (int j = 0; j < ND; ++j)
-                t_off[j][hh] = rl * ROW_B + (((4 * j + 2 * chi + ((li & 3) >> 1)) ^ k_swz<D>(rl)) << 4) +
+                t_off[j][hh] = rl * ROW_B + (((4 * j + 2 * chi + ((li & 3) >> 1)) ^ t_swz<D>(rl)) << 4) +
                                ((li & 1) << 3);
         }
     }

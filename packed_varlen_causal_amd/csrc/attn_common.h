@@ -149,6 +149,18 @@ template <int D> __device__ inline int v_swz(int row) {
     if constexpr (D == 128) return ((row & 3) << 1) | ((row >> 1) & 1);
     else return row & 3;
 }
+// Tiles the backward reads both ways (row by row as an A operand, and through
+// the transposing read): 16-byte chunks, chunk ^ ft(row).  A row read serves
+// 16 consecutive rows per pass, so ft must be one-to-one on them; a
+// transposing read serves 4 rows per pass, each spanning 4 consecutive
+// chunks (64 bytes), so those 4 rows must land in different 64-byte groups.
+// At d = 128 (a row is exactly the 64 banks) ft swaps the row's two low 2-bit
+// fields; at d = 64 (two rows per 64 banks, split by parity) ft maps rows of
+// one parity one-to-one onto the 8 chunks, with bit 2 taken from row bit 1.
+template <int D> __device__ inline int t_swz(int row) {
+    if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return (((row >> 1) & 1) << 2) | (((row >> 3) & 1) << 1) | ((row >> 2) & 1);
+}
 
 }  // namespace attn
 }  // namespace pvc
