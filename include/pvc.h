@@ -341,20 +341,23 @@ pvc_status pvc_varlen_attn_fwd(const void* q, const void* k, const void* v, void
  * "EOS is content": the masked-softmax equation; masked pairs have P = 0, so
  * no gradient crosses a segment boundary).  P is recomputed from q, k and lse.
  *
- * q, k, v, out, dout  [total_tokens, heads, head_dim] bf16; out is the forward's
- *             bf16 output for these q, k, v
+ * q, k, v, out, dout  [total_tokens, heads, head_dim], all bf16 (grad_dtype
+ *             PVC_OUT_BF16 / PVC_OUT_F32) or all fp16 (PVC_OUT_F16 /
+ *             PVC_OUT_F16_F32: [charlestar] "varlen interface", q, k, v in fp16
+ *             or bf16); out is the forward's 16-bit output for these q, k, v
  * lse         [heads, total_tokens] fp32, the forward's log-sum-exp (natural log)
- * dq, dk, dv  [total_tokens, heads, head_dim], bf16 (grad_dtype PVC_OUT_BF16) or
- *             fp32 (PVC_OUT_F32, the same schedule before the final rounding);
- *             bf16 inputs only (fp16 types give PVC_ERR_INVALID_ARG);
- *             must not alias each other, the inputs or the scratch
+ * dq, dk, dv  [total_tokens, heads, head_dim], in the input type (PVC_OUT_BF16,
+ *             PVC_OUT_F16) or fp32 (PVC_OUT_F32, PVC_OUT_F16_F32: the same
+ *             schedule before the final rounding); must not alias each other,
+ *             the inputs or the scratch
  * scratch     device buffer of pvc_attn_bwd_scratch_size bytes (overwritten)
  * head_dim    64 or 128; 2 * heads * (total_tokens + 159) * 4 bytes must stay
  *             below 4 GiB (PVC_ERR_INVALID_ARG otherwise)
  * total_tokens and causal must be those the plan was built with; otherwise
  * PVC_DEV_PLAN is set and nothing is written.  All pointers 16-byte aligned.
- * Arithmetic: bf16 MFMA products with fp32 accumulation; P and dS are rounded
- * to bf16 for their products.  Deterministic: no atomics.
+ * Arithmetic: MFMA products in the input type with fp32 accumulation; P and
+ * dS are rounded to the input type (nearest even) for their products.
+ * Deterministic: no atomics.
  */
 size_t pvc_attn_bwd_scratch_size(int64_t total_tokens, int32_t heads);
 pvc_status pvc_varlen_attn_bwd_planned(const void* q, const void* k, const void* v, const void* out,

@@ -421,24 +421,24 @@ def attn_bwd_scratch_size(total_tokens: int, heads: int) -> int:
 
 def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
                     dout: torch.Tensor, lse: torch.Tensor, plan: AttnPlan, causal: bool = True,
-                    grad_dtype: torch.dtype = torch.bfloat16, grads=None, scratch: torch.Tensor | None = None,
+                    grad_dtype: torch.dtype | None = None, grads=None, scratch: torch.Tensor | None = None,
                     check: bool = False, stream=None):
     """Gradients (dq, dk, dv) of varlen_attn_fwd for an upstream gradient ``dout``.
 
-    q, k, v, out, dout bf16 [T, H, d]; lse fp32 [H, T] from the forward
-    (return_lse=True); ``plan`` the forward's plan.  Gradients are bf16, or
-    fp32 with grad_dtype=torch.float32; ``grads`` may pass three output tensors.
+    q, k, v, out, dout [T, H, d], all bf16 or all fp16; lse fp32 [H, T] from
+    the forward (return_lse=True); ``plan`` the forward's plan.  Gradients are
+    in the inputs' dtype (the default), or fp32 with grad_dtype=torch.float32;
+    ``grads`` may pass three output tensors.
     """
-    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
-        _require(t, name, torch.bfloat16, 3)
+    in_dt = _require16((q, k, v, out, dout), ("q", "k", "v", "out", "dout"))
     if any(t.shape != q.shape for t in (k, v, out, dout)):
         raise ValueError("q, k, v, out and dout must share the shape [T, H, d]")
     T, H, D = q.shape
     _require(lse, "lse", torch.float32, 2)
     if tuple(lse.shape) != (H, T):
         raise ValueError("lse must be [H, T]")
-    if grad_dtype not in (torch.bfloat16, torch.float32):
-        raise TypeError("grad_dtype must be torch.bfloat16 or torch.float32")
+    grad_dtype = in_dt if grad_dtype is None else grad_dtype
+    code = _io_code(in_dt, grad_dtype)
     if plan.total_tokens != T or plan.causal != bool(causal):
         raise ValueError("plan was built for other total_tokens / causal")
     if grads is None:
@@ -460,7 +460,7 @@ def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
     dq, dk, dv = grads
     st = _lib.pvc_varlen_attn_bwd_planned(
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), T, H, D,
-        int(bool(causal)), OUT_F32 if grad_dtype == torch.float32 else OUT_BF16, _ptr(plan.workspace),
+        int(bool(causal)), code, _ptr(plan.workspace),
         plan.ws_bytes, _ptr(scratch), scratch.numel(), _ptr(plan.dev_error), _stream(stream))
     _check(st, "varlen_attn_bwd")
     if check:

@@ -27,8 +27,8 @@
 //                     the other half's exponentials.  One wave per SIMD
 //                     (about 370 registers: the two fp32 accumulators alone
 //                     take 128).
-// Every product rounds its probability operand (P or dS) to bf16 and
-// accumulates in fp32.  No atomics: each output element is written once, so
+// Every product rounds its probability operand (P or dS) to the input type
+// (bf16 or fp16) and accumulates in fp32.  No atomics: each output element is written once, so
 // results do not depend on scheduling.  Stages that lie wholly outside a
 // wave's segments or on the wrong side of its diagonal are skipped, as in the
 // forward.  The dQ kernel recomputes S and dP, which the dK/dV kernel also
@@ -98,7 +98,7 @@ __device__ __attribute__((always_inline)) inline void wait_stages(int ahead) {
 
 // ------------------------------------------------------------------- prep
 
-template <int D>
+template <int D, bool F16>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ out,
                                                        const uint16_t* __restrict__ dout,
                                                        const float* __restrict__ lse, float* __restrict__ scratch,
@@ -115,8 +115,17 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
         const u32x4 b = *reinterpret_cast<const u32x4*>(dout + item * D + part * 8);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-            acc = fmaf(__uint_as_float(a[w] << 16), __uint_as_float(b[w] << 16), acc);
-            acc = fmaf(__uint_as_float(a[w] & 0xFFFF0000u), __uint_as_float(b[w] & 0xFFFF0000u), acc);
+            if constexpr (F16) {
+                // the elements go through named scalars: a bit cast of a vector
+                // element expression read element 0 whatever the index
+                const uint32_t aw = a[w], bw = b[w];
+                const f16x2 x = __builtin_bit_cast(f16x2, aw), y = __builtin_bit_cast(f16x2, bw);
+                acc = fmaf((float)x[0], (float)y[0], acc);
+                acc = fmaf((float)x[1], (float)y[1], acc);
+            } else {
+                acc = fmaf(__uint_as_float(a[w] << 16), __uint_as_float(b[w] << 16), acc);
+                acc = fmaf(__uint_as_float(a[w] & 0xFFFF0000u), __uint_as_float(b[w] & 0xFFFF0000u), acc);
+            }
         }
     }
 #pragma unroll
@@ -150,9 +159,12 @@ __device__ inline bool plan_sealed(const BwdParams& p, bool causal, bool& sealed
 
 // ------------------------------------------------------------------ dQ
 
-template <int D, bool CAUSAL, bool OUT_F32>
+template <int D, bool CAUSAL, bool OUT_F32, bool F16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdParams p) {
+    using E = Elt<F16>;                      // bf16 or fp16 inputs
+    using x8 = typename E::x8;
+    using x2 = typename E::x2;
     static_assert(D == 64 || D == 128, "head_dim");
     static_assert(kBN == 32, "32-key halves");
     constexpr int NH = kDqHalves;
@@ -208,14 +220,14 @@ void bwd_dq_kernel(BwdParams p) {
 
     auto row_off = [&](int r) -> int64_t { return ((int64_t)r * H + head) * D; };
     // Q^T and dO^T B operands: lane (c, g) holds X[row][16s + 8g .. +8]
-    bf16x8 qreg[NS], doreg[NS];
+    x8 qreg[NS], doreg[NS];
     {
         const uint16_t* qp = p.q + row_off(row) + 8 * g;
         const uint16_t* gp = p.dout + row_off(row) + 8 * g;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
-            doreg[s] = *reinterpret_cast<const bf16x8*>(gp + 16 * s);
+            qreg[s] = *reinterpret_cast<const x8*>(qp + 16 * s);
+            doreg[s] = *reinterpret_cast<const x8*>(gp + 16 * s);
         }
     }
     const float lse2 = p.scratch[(int64_t)head * p.Tp + row];
@@ -280,11 +292,11 @@ void bwd_dq_kernel(BwdParams p) {
                                ((li & 1) << 3);
         }
     }
-    auto rop = [&](const char* b, int s) { return *reinterpret_cast<const bf16x8*>(b + r_off[s]); };
-    auto top = [&](const char* b, int ks, int j) -> bf16x8 {
+    auto rop = [&](const char* b, int s) { return *reinterpret_cast<const x8*>(b + r_off[s]); };
+    auto top = [&](const char* b, int ks, int j) -> x8 {
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + t_off[j][0] + 16 * ks * ROW_B));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + t_off[j][1] + 16 * ks * ROW_B));
-        return __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
+        return __builtin_bit_cast(x8, (short __attribute__((ext_vector_type(8)))){
             lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
     };
 
@@ -313,8 +325,8 @@ void bwd_dq_kernel(BwdParams p) {
             dP[h] = f32x16(0.0f);
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                S[h] = mfma32(rop(kb, s), qreg[s], S[h]);          // S^T = K Q^T
-                dP[h] = mfma32(rop(vb, s), doreg[s], dP[h]);       // dP^T = V dO^T
+                S[h] = E::mfma(rop(kb, s), qreg[s], S[h]);          // S^T = K Q^T
+                dP[h] = E::mfma(rop(vb, s), doreg[s], dP[h]);       // dP^T = V dO^T
             }
         });
         static_for<NH>([&](auto H_) {
@@ -330,23 +342,23 @@ void bwd_dq_kernel(BwdParams p) {
                 }
             }
             // dS^T = P^T o (dP^T - D); keys 16ks + 8(e/4) + 4g + e%4 of pack ks
-            bf16x2 pk[8];
+            x2 pk[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float p0 = __builtin_amdgcn_exp2f(fmaf(S[h][2 * i], sl2, -lse2));
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(S[h][2 * i + 1], sl2, -lse2));
-                pk[i] = bf16x2{(__bf16)(p0 * (dP[h][2 * i] - dlt)), (__bf16)(p1 * (dP[h][2 * i + 1] - dlt))};
+                pk[i] = E::pair(p0 * (dP[h][2 * i] - dlt), p1 * (dP[h][2 * i + 1] - dlt));
             }
-            bf16x8 ds[2];
+            x8 ds[2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
-                ds[ks] = bf16x8{pk[4 * ks][0], pk[4 * ks][1], pk[4 * ks + 1][0], pk[4 * ks + 1][1],
+                ds[ks] = x8{pk[4 * ks][0], pk[4 * ks][1], pk[4 * ks + 1][0], pk[4 * ks + 1][1],
                                 pk[4 * ks + 2][0], pk[4 * ks + 2][1], pk[4 * ks + 3][0], pk[4 * ks + 3][1]};
             const char* kb = kbase + (slot * NH + h) * TILE_B;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-                for (int j = 0; j < ND; ++j) acc[j] = mfma32(top(kb, ks, j), ds[ks], acc[j]);   // dQ^T += K^T dS^T
+                for (int j = 0; j < ND; ++j) acc[j] = E::mfma(top(kb, ks, j), ds[ks], acc[j]);   // dQ^T += K^T dS^T
         });
     };
 
@@ -393,8 +405,8 @@ void bwd_dq_kernel(BwdParams p) {
         for (int j = 0; j < ND; ++j)
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
-                const bf16x2 a = {(__bf16)(acc[j][4 * rq] * sc), (__bf16)(acc[j][4 * rq + 1] * sc)};
-                const bf16x2 b = {(__bf16)(acc[j][4 * rq + 2] * sc), (__bf16)(acc[j][4 * rq + 3] * sc)};
+                const x2 a = E::pair(acc[j][4 * rq] * sc, acc[j][4 * rq + 1] * sc);
+                const x2 b = E::pair(acc[j][4 * rq + 2] * sc, acc[j][4 * rq + 3] * sc);
                 const int chunk = (4 * j + rq) ^ (c & (CPR - 1));
                 *reinterpret_cast<u32x2*>(ob + c * ROW_B + chunk * 16 + g * 8) =
                         u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
@@ -415,9 +427,12 @@ void bwd_dq_kernel(BwdParams p) {
 
 // --------------------------------------------------------------- dK, dV
 
-template <int D, bool CAUSAL, bool OUT_F32, int NH>
+template <int D, bool CAUSAL, bool OUT_F32, bool F16, int NH>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdParams p) {
+    using E = Elt<F16>;                      // bf16 or fp16 inputs
+    using x8 = typename E::x8;
+    using x2 = typename E::x2;
     static_assert(D == 64 || D == 128, "head_dim");
     static_assert(kBN == 32, "32-query halves");
     constexpr int SROWS = NH * kBN;               // query rows per stage
@@ -476,14 +491,14 @@ void bwd_dkdv_kernel(BwdParams p) {
 
     auto row_off = [&](int r) -> int64_t { return ((int64_t)r * H + head) * D; };
     // K^T and V^T B operands: lane (c, g) holds X[key][16s + 8g .. +8]
-    bf16x8 kreg[NS], vreg[NS];
+    x8 kreg[NS], vreg[NS];
     {
         const uint16_t* kp = p.k + row_off(key) + 8 * g;
         const uint16_t* vp = p.v + row_off(key) + 8 * g;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
-            kreg[s] = *reinterpret_cast<const bf16x8*>(kp + 16 * s);
-            vreg[s] = *reinterpret_cast<const bf16x8*>(vp + 16 * s);
+            kreg[s] = *reinterpret_cast<const x8*>(kp + 16 * s);
+            vreg[s] = *reinterpret_cast<const x8*>(vp + 16 * s);
         }
     }
     bool sealed;
@@ -557,11 +572,11 @@ void bwd_dkdv_kernel(BwdParams p) {
                                ((li & 1) << 3);
         }
     }
-    auto rop = [&](const char* b, int s) { return *reinterpret_cast<const bf16x8*>(b + r_off[s]); };
-    auto top = [&](const char* b, int ks, int j) -> bf16x8 {
+    auto rop = [&](const char* b, int s) { return *reinterpret_cast<const x8*>(b + r_off[s]); };
+    auto top = [&](const char* b, int ks, int j) -> x8 {
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + t_off[j][0] + 16 * ks * ROW_B));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + t_off[j][1] + 16 * ks * ROW_B));
-        return __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
+        return __builtin_bit_cast(x8, (short __attribute__((ext_vector_type(8)))){
             lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
     };
 
@@ -578,10 +593,10 @@ void bwd_dkdv_kernel(BwdParams p) {
         return wave_active && qt + SROWS > w_qlo && qt < w_qhi;
     };
     auto half_full = [&](int qt) -> bool { return qt >= full_lo && qt + kBN <= full_hi; };
-    auto pack = [&](const bf16x2 (&pk)[8], bf16x8 (&outp)[2]) {
+    auto pack = [&](const x2 (&pk)[8], x8 (&outp)[2]) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-            outp[ks] = bf16x8{pk[4 * ks][0], pk[4 * ks][1], pk[4 * ks + 1][0], pk[4 * ks + 1][1],
+            outp[ks] = x8{pk[4 * ks][0], pk[4 * ks][1], pk[4 * ks + 1][0], pk[4 * ks + 1][1],
                               pk[4 * ks + 2][0], pk[4 * ks + 2][1], pk[4 * ks + 3][0], pk[4 * ks + 3][1]};
     };
     // one stage: S = Q K^T and dP = dO V^T for every half first, so the
@@ -597,8 +612,8 @@ void bwd_dkdv_kernel(BwdParams p) {
             dP[h] = f32x16(0.0f);
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                S[h] = mfma32(rop(qb, s), kreg[s], S[h]);      // S = Q K^T
-                dP[h] = mfma32(rop(ob, s), vreg[s], dP[h]);    // dP = dO V^T
+                S[h] = E::mfma(rop(qb, s), kreg[s], S[h]);      // S = Q K^T
+                dP[h] = E::mfma(rop(ob, s), vreg[s], dP[h]);    // dP = dO V^T
             }
         });
         static_for<NH>([&](auto H_) {
@@ -621,17 +636,17 @@ void bwd_dkdv_kernel(BwdParams p) {
                 l4[kq] = *reinterpret_cast<const f32x4*>(ld + 8 * kq + 4 * g);
                 d4[kq] = *reinterpret_cast<const f32x4*>(ld + kBN + 8 * kq + 4 * g);
             }
-            bf16x2 pp[8], pd[8];
+            x2 pp[8], pd[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int r0_ = 2 * i, r1_ = 2 * i + 1;
                 const float p0 = __builtin_amdgcn_exp2f(fmaf(S[h][r0_], sl2, -l4[r0_ >> 2][r0_ & 3]));
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(S[h][r1_], sl2, -l4[r1_ >> 2][r1_ & 3]));
-                pp[i] = bf16x2{(__bf16)p0, (__bf16)p1};
-                pd[i] = bf16x2{(__bf16)(p0 * (dP[h][r0_] - d4[r0_ >> 2][r0_ & 3])),
-                               (__bf16)(p1 * (dP[h][r1_] - d4[r1_ >> 2][r1_ & 3]))};
+                pp[i] = E::pair(p0, p1);
+                pd[i] = E::pair(p0 * (dP[h][r0_] - d4[r0_ >> 2][r0_ & 3]),
+                                p1 * (dP[h][r1_] - d4[r1_ >> 2][r1_ & 3]));
             }
-            bf16x8 Pb[2], Db[2];
+            x8 Pb[2], Db[2];
             pack(pp, Pb);
             pack(pd, Db);
             const char* qb = qbase + (slot * NH + h) * TILE_B;
@@ -640,8 +655,8 @@ void bwd_dkdv_kernel(BwdParams p) {
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                 for (int j = 0; j < ND; ++j) {
-                    accV[j] = mfma32(top(ob, ks, j), Pb[ks], accV[j]);   // dV^T += dO^T P
-                    accK[j] = mfma32(top(qb, ks, j), Db[ks], accK[j]);   // dK^T += Q^T dS
+                    accV[j] = E::mfma(top(ob, ks, j), Pb[ks], accV[j]);   // dV^T += dO^T P
+                    accK[j] = E::mfma(top(qb, ks, j), Db[ks], accK[j]);   // dK^T += Q^T dS
                 }
         });
     };
@@ -693,8 +708,8 @@ void bwd_dkdv_kernel(BwdParams p) {
             for (int j = 0; j < ND; ++j)
 #pragma unroll
                 for (int rq = 0; rq < 4; ++rq) {
-                    const bf16x2 a = {(__bf16)(acc[j][4 * rq] * mul), (__bf16)(acc[j][4 * rq + 1] * mul)};
-                    const bf16x2 b = {(__bf16)(acc[j][4 * rq + 2] * mul), (__bf16)(acc[j][4 * rq + 3] * mul)};
+                    const x2 a = E::pair(acc[j][4 * rq] * mul, acc[j][4 * rq + 1] * mul);
+                    const x2 b = E::pair(acc[j][4 * rq + 2] * mul, acc[j][4 * rq + 3] * mul);
                     const int chunk = (4 * j + rq) ^ (c & (CPR - 1));
                     *reinterpret_cast<u32x2*>(ob + c * ROW_B + chunk * 16 + g * 8) =
                             u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
@@ -723,33 +738,33 @@ void bwd_dkdv_kernel(BwdParams p) {
 #endif
 constexpr int kDkdvHalves = PVC_DKDV_HALVES;
 
-template <int D>
+template <int D, bool F16>
 pvc_status launch_bwd(const BwdParams& prm, bool causal, bool out_f32, hipStream_t s) {
     {
         constexpr int RPB = 256 / (D / 8);
         const int64_t items = prm.Tp * prm.H;
         const int64_t nblk = (items + RPB - 1) / RPB;
-        hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3((unsigned)nblk), dim3(256), 0, s, prm.out, prm.dout, prm.lse,
-                           prm.scratch, prm.T, prm.Tp, prm.H);
+        hipLaunchKernelGGL((bwd_prep_kernel<D, F16>), dim3((unsigned)nblk), dim3(256), 0, s, prm.out, prm.dout,
+                           prm.lse, prm.scratch, prm.T, prm.Tp, prm.H);
     }
     const int64_t grid = ((int64_t)prm.items + kNumXcd - 1) / kNumXcd * kNumXcd;
     if (grid > 0x7fffffffLL) return PVC_ERR_INVALID_ARG;
     dim3 g((unsigned)grid), blk(kThreads);
     if (causal) {
         if (out_f32) {
-            hipLaunchKernelGGL((bwd_dq_kernel<D, true, true>), g, blk, 0, s, prm);
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, true, kDkdvHalves>), g, blk, 0, s, prm);
+            hipLaunchKernelGGL((bwd_dq_kernel<D, true, true, F16>), g, blk, 0, s, prm);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, true, F16, kDkdvHalves>), g, blk, 0, s, prm);
         } else {
-            hipLaunchKernelGGL((bwd_dq_kernel<D, true, false>), g, blk, 0, s, prm);
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false, kDkdvHalves>), g, blk, 0, s, prm);
+            hipLaunchKernelGGL((bwd_dq_kernel<D, true, false, F16>), g, blk, 0, s, prm);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false, F16, kDkdvHalves>), g, blk, 0, s, prm);
         }
     } else {
         if (out_f32) {
-            hipLaunchKernelGGL((bwd_dq_kernel<D, false, true>), g, blk, 0, s, prm);
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true, kDkdvHalves>), g, blk, 0, s, prm);
+            hipLaunchKernelGGL((bwd_dq_kernel<D, false, true, F16>), g, blk, 0, s, prm);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true, F16, kDkdvHalves>), g, blk, 0, s, prm);
         } else {
-            hipLaunchKernelGGL((bwd_dq_kernel<D, false, false>), g, blk, 0, s, prm);
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, false, kDkdvHalves>), g, blk, 0, s, prm);
+            hipLaunchKernelGGL((bwd_dq_kernel<D, false, false, F16>), g, blk, 0, s, prm);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, false, F16, kDkdvHalves>), g, blk, 0, s, prm);
         }
     }
     return launch_status();
@@ -785,7 +800,11 @@ extern "C" pvc_status pvc_varlen_attn_bwd_planned(const void* q, const void* k, 
         dq == nullptr || dk == nullptr || dv == nullptr || workspace == nullptr || scratch == nullptr)
         return PVC_ERR_NULL;
     if (total_tokens < 1 || total_tokens > 0x7fffffffLL || heads < 1) return PVC_ERR_INVALID_ARG;
-    if (grad_dtype != PVC_OUT_BF16 && grad_dtype != PVC_OUT_F32) return PVC_ERR_INVALID_ARG;
+    if (grad_dtype != PVC_OUT_BF16 && grad_dtype != PVC_OUT_F32 && grad_dtype != PVC_OUT_F16 &&
+        grad_dtype != PVC_OUT_F16_F32)
+        return PVC_ERR_INVALID_ARG;
+    const bool f16 = grad_dtype == PVC_OUT_F16 || grad_dtype == PVC_OUT_F16_F32;
+    const bool f32 = grad_dtype == PVC_OUT_F32 || grad_dtype == PVC_OUT_F16_F32;
     if (head_dim != 64 && head_dim != 128) return PVC_ERR_UNSUPPORTED;
     const void* in16[] = {q, k, v, out, dout, dq, dk, dv, lse, scratch};
     for (const void* ptr : in16)
@@ -798,7 +817,7 @@ extern "C" pvc_status pvc_varlen_attn_bwd_planned(const void* q, const void* k, 
     // the lse / D blocks are addressed by 32-bit byte offsets into the scratch
     if ((int64_t)2 * heads * scratch_rows(total_tokens) * 4 >= ((int64_t)1 << 32)) return PVC_ERR_INVALID_ARG;
     const size_t in_bytes = (size_t)total_tokens * heads * head_dim * 2;
-    const size_t g_bytes = in_bytes * (grad_dtype == PVC_OUT_F32 ? 2 : 1);
+    const size_t g_bytes = in_bytes * (f32 ? 2 : 1);
     const void* ins[] = {q, k, v, out, dout};
     void* outs[] = {dq, dk, dv};
     for (void* o : outs) {
@@ -831,7 +850,10 @@ extern "C" pvc_status pvc_varlen_attn_bwd_planned(const void* q, const void* k, 
     prm.scale = (float)(1.0 / sqrt((double)head_dim));
     prm.dev_error = dev_error;
     hipStream_t s = as_stream(stream);
-    const bool f32 = grad_dtype == PVC_OUT_F32;
-    if (head_dim == 128) return launch_bwd<128>(prm, causal != 0, f32, s);
-    return launch_bwd<64>(prm, causal != 0, f32, s);
+    if (f16) {
+        if (head_dim == 128) return launch_bwd<128, true>(prm, causal != 0, f32, s);
+        return launch_bwd<64, true>(prm, causal != 0, f32, s);
+    }
+    if (head_dim == 128) return launch_bwd<128, false>(prm, causal != 0, f32, s);
+    return launch_bwd<64, false>(prm, causal != 0, f32, s);
 }

@@ -75,12 +75,18 @@ U_F32 = 2.0 ** -24
 TAU = 2.0 ** -126           # smallest normal fp32: values below it are flushed
 
 
-def grad_error_bounds(q, k, v, dout, cu, causal=True, heads=None, segments=None):
+U_F16 = 2.0 ** -11          # unit roundoff of fp16 (11 significand bits)
+TAU_F16 = 2.0 ** -24        # smallest fp16 subnormal: the absolute error floor of an fp16 rounding
+
+
+def grad_error_bounds(q, k, v, dout, cu, causal=True, heads=None, segments=None, f16=False):
     """Elementwise first-order bounds on the backward kernels' fp32 gradient error.
 
-    The kernels take the forward's bf16 output O and its fp32 log-sum-exp,
+    The kernels take the forward's 16-bit output O and its fp32 log-sum-exp,
     recompute P in fp32, round P (for dV) and dS = P o (dP - D) (for dQ, dK)
-    to bf16, and accumulate in fp32.  With u the bf16 unit roundoff,
+    to the 16-bit input type, and accumulate in fp32.  Inputs are bf16 bit
+    patterns, or fp16 arrays with ``f16``.  With u the unit roundoff of that
+    type,
     e = 2u + (n + d) 2^-24 per product term (one rounding of the operand, the
     log-sum-exp's relative error from summing bf16 probabilities, fp32 sums),
     W = P |V| (an upper bound of |O| and of the forward's PV error scale) and
@@ -88,16 +94,23 @@ def grad_error_bounds(q, k, v, dout, cu, causal=True, heads=None, segments=None)
       |d dV_jd| <= e sum_i P_ij |dO_id|
       |d dQ_id| <= s sum_j (e |dS_ij| + P_ij dD_i) |K_jd|
       |d dK_jd| <= s sum_i (e |dS_ij| + P_ij dD_i) |Q_id|
-    P and dS here are fp64 values computed from the same bf16 inputs; second
+    P and dS here are fp64 values computed from the same 16-bit inputs; second
     order terms are dropped.  fp32 values below 2^-126 are flushed to zero by
     the hardware (exp2, the bf16 conversions, MFMA), so every probability and
     every dS term also carries an absolute error tau = 2^-126 (times
-    1 + |dP - D| for dS), and every sum n tau; with M the visibility mask:
+    1 + |dP - D| for dS), and every sum n 2^-126; with fp16 operands tau is
+    the fp16 rounding's absolute floor 2^-24 instead (values below fp16's
+    normal range keep fewer bits).  With M the visibility mask:
       |d dV_jd| += tau sum_i M_ij |dO_id| + n tau
       |d dQ_id|, |d dK_jd| += s sum tau (1 + |dP_ij - D_i|) M_ij |K_jd| (|Q_id|) + n tau
     Entries outside ``heads`` / ``segments`` are NaN.
     """
-    Q, K, V, G = (bf16_bits_to_f64(x) for x in (q, k, v, dout))
+    if f16:
+        Q, K, V, G = (np.asarray(x, np.float16).astype(np.float64) for x in (q, k, v, dout))
+        u, tau = U_F16, TAU_F16
+    else:
+        Q, K, V, G = (bf16_bits_to_f64(x) for x in (q, k, v, dout))
+        u, tau = U_BF16, TAU
     T, H, d = Q.shape
     s = 1.0 / np.sqrt(d)
     cu = np.asarray(cu, np.int64)
@@ -107,7 +120,7 @@ def grad_error_bounds(q, k, v, dout, cu, causal=True, heads=None, segments=None)
     for r in segments:
         a, b = int(cu[r]), int(cu[r + 1])
         n = b - a
-        e = 2 * U_BF16 + (n + d) * U_F32
+        e = 2 * u + (n + d) * U_F32
         for h in heads:
             q_, k_, v_, g_ = Q[a:b, h], K[a:b, h], V[a:b, h], G[a:b, h]
             S = s * (q_ @ k_.T)
@@ -120,9 +133,9 @@ def grad_error_bounds(q, k, v, dout, cu, causal=True, heads=None, segments=None)
             W = P @ np.abs(v_)
             dPD = g_ @ v_.T - (g_ * O).sum(axis=1)[:, None]
             dS = P * dPD
-            dD = 3 * U_BF16 * (np.abs(g_) * W).sum(axis=1)
-            E = e * np.abs(dS) + P * dD[:, None] + TAU * (1 + np.abs(dPD)) * M
-            bv[a:b, h] = (e * P + TAU * M).T @ np.abs(g_) + n * TAU
+            dD = 3 * u * (np.abs(g_) * W).sum(axis=1)
+            E = e * np.abs(dS) + P * dD[:, None] + tau * (1 + np.abs(dPD)) * M
+            bv[a:b, h] = (e * P + tau * M).T @ np.abs(g_) + n * TAU
             bq[a:b, h] = s * (E @ np.abs(k_)) + n * TAU
             bk[a:b, h] = s * (E.T @ np.abs(q_)) + n * TAU
     return bq, bk, bv
@@ -130,8 +143,8 @@ def grad_error_bounds(q, k, v, dout, cu, causal=True, heads=None, segments=None)
 
 def grad_check(got_f32, got_bf16, refs, bounds, rows=None) -> dict:
     """fp32 gradients within their elementwise bounds of the fp64 oracle (where
-    the oracle was evaluated), and bf16 gradients equal to the RNE rounding of
-    the fp32 ones bit for bit."""
+    the oracle was evaluated), and 16-bit gradients (bf16 or fp16) equal to the
+    RNE rounding of the fp32 ones bit for bit."""
     rep = {}
     idx = None if rows is None else torch.as_tensor(np.asarray(rows, np.int64), device=got_f32[0].device)
     for name, f, b16, ref, bnd in zip(("dq", "dk", "dv"), got_f32, got_bf16, refs, bounds):
@@ -143,15 +156,15 @@ def grad_check(got_f32, got_bf16, refs, bounds, rows=None) -> dict:
         sel = np.isfinite(ref)
         err = np.abs(f - ref)[sel]
         lim = bnd[sel]
-        rne = host_bits(torch.from_numpy(f.astype(np.float32)).to(torch.bfloat16))
+        rne = host_bits(torch.from_numpy(f.astype(np.float32)).to(b16.dtype))
         rep[name] = {
             "max_abs_err": float(err.max()),
             "max_err_over_bound": float((err / np.maximum(lim, 1e-300)).max()),
             "max_abs_ref": float(np.abs(ref[sel]).max()),
-            "bf16_vs_rne_mismatches": int((rne != bits).sum()),
+            "rne_mismatches_16bit": int((rne != bits).sum()),
         }
     say("    grad parity", rep)
     for name, r in rep.items():
         assert r["max_err_over_bound"] <= 1.0, (name, r)
-        assert r["bf16_vs_rne_mismatches"] == 0, (name, r)
+        assert r["rne_mismatches_16bit"] == 0, (name, r)
     return rep

@@ -1,9 +1,11 @@
 """GPU parity for fp16 inputs ([charlestar] "varlen interface": q, k, v in fp16
-or bf16): the attention forward (self and prefill plans), RoPE and the packed
-cross-entropy, each against the fp64 oracle on the fp16 values.
+or bf16): the attention forward (self and prefill plans), its backward, RoPE
+and the packed cross-entropy, each against the fp64 oracle on the fp16 values.
 
 Attention: the fp32 output within 1e-2 max-abs of the oracle and the fp16
-output equal to the nearest-even fp16 rounding of the fp32 output.  RoPE:
+output equal to the nearest-even fp16 rounding of the fp32 output.  Backward:
+fp32 gradients within the first-order bounds of the bf16 tests with fp16's
+unit roundoff and absolute floor, fp16 gradients the RNE of the fp32 ones.  RoPE:
 bit-exact fp16 results (one ulp allowed only where the exact value lies within
 the double evaluation's error of an fp16 rounding midpoint).  CE: row losses
 within the bound of the bf16 tests, counts exact, fp16 gradient the RNE of the
@@ -14,7 +16,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import ATOL, dev_i32, say
+from gpu_util import ATOL, dev_i32, grad_check, grad_error_bounds, say
 from oracle import attention as A
 from oracle import loss as L
 from oracle import pack as P
@@ -70,6 +72,38 @@ def test_attention_fp16_small(pvc, name, causal):
     ref, ref_lse = A.attention_qk(q, k, v, cu, cu, causal)
     _check_f16(of, oh, ref)
     assert np.abs(ls.cpu().numpy().T - ref_lse).max() < 5e-3
+
+
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_fp16(pvc, causal, d):
+    w = make_workload("sft", scale="small")
+    T, H = w.total_tokens, w.heads
+    say(f"  fp16 bwd causal={causal} d={d}: T={T} H={H}")
+    q, k, v, g = (_f16((T, H, d), s) for s in (11, 12, 13, 14))
+    cu = P.pack_build(w.lengths)["cu_seqlens"]
+    qd, kd, vd, gd = _dev(q), _dev(k), _dev(v), _dev(g)
+    plan = pvc.attn_plan(dev_i32(cu), T, int(w.lengths.max()), causal)
+    out, lse = pvc.varlen_attn_fwd(qd, kd, vd, plan=plan, causal=causal, return_lse=True)
+    g32 = pvc.varlen_attn_bwd(qd, kd, vd, out, gd, lse, plan, causal, grad_dtype=torch.float32)
+    g16 = pvc.varlen_attn_bwd(qd, kd, vd, out, gd, lse, plan, causal)
+    torch.cuda.synchronize()
+    assert all(t.dtype == torch.float16 for t in g16) and int(plan.dev_error.item()) == 0
+    refs = A.attention_bwd(q, k, v, g, cu, causal, threads=16)
+    grad_check(g32, g16, refs, grad_error_bounds(q, k, v, g, cu, causal, f16=True))
+
+
+def test_backward_fp16_refuses_mixed_types(pvc):
+    w = make_workload("tiny")
+    T, H, d = w.total_tokens, w.heads, w.head_dim
+    q = _dev(_f16((T, H, d), 1))
+    cu = P.pack_build(w.lengths)["cu_seqlens"]
+    plan = pvc.attn_plan(dev_i32(cu), T, int(w.lengths.max()), True)
+    out, lse = pvc.varlen_attn_fwd(q, q, q, plan=plan, return_lse=True)
+    with pytest.raises(TypeError):
+        pvc.varlen_attn_bwd(q, q, q, out.to(torch.bfloat16), q, lse, plan)
+    with pytest.raises(TypeError):
+        pvc.varlen_attn_bwd(q, q, q, out, q, lse, plan, grad_dtype=torch.bfloat16)
 
 
 def test_prefill_fp16(pvc):

@@ -191,7 +191,7 @@ def test_null_and_range_checks_return_before_gpu_work(lib):
     assert bwd(ptrs=g[:9] + [None]) == 1
     assert bwd(D=96) == 3
     assert bwd(gd=5) == 2
-    assert bwd(gd=2) == 2                                      # no fp16 backward
+    assert bwd(gd=4) == 2                                      # not an element-type code
     assert bwd(T=0) == 2
     assert bwd(ws=8) == 4
     assert bwd(sc=8) == 4
