@@ -136,6 +136,23 @@ pvc_status pvc_pack_build(const int32_t* lengths, const uint8_t* is_pad,
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The per-token half of pvc_pack_build on an existing cu_seqlens [nseg+1]
+ * (device): segment_ids, position_ids, shifted_labels, loss_mask and
+ * num_targets exactly as defined there ([charlestar] "nine tokens, three
+ * identities"; [m020] "06 positions and labels"), for callers whose
+ * boundaries already exist, or that run this pass apart from the prefix sum
+ * (say, on a second stream beside RoPE, which needs only cu_seqlens).
+ * Arguments, optional outputs and errors as for pvc_pack_build; a token
+ * outside every segment of a malformed cu gets segment -1, position 0 and an
+ * ignored label, and sets PVC_DEV_TOTAL or PVC_DEV_NOT_INCREASING.
+ * num_targets is cleared by this call (a one-thread kernel ahead of the pass).
+ */
+pvc_status pvc_pack_tokens(const int32_t* cu_seqlens, const uint8_t* is_pad, const int32_t* tokens,
+                           int32_t nseg, int64_t total_tokens, int32_t ignore_index, int32_t* segment_ids,
+                           int32_t* position_ids, int32_t* shifted_labels, uint8_t* loss_mask,
+                           int64_t* num_targets, uint32_t* dev_error, void* stream);
+
+/*
  * Check a caller-supplied cu_seqlens [nseg+1] against the contract above and
  * OR the failing PVC_DEV_* bits into *dev_error (required here).  With
  * `lengths` [nseg] non-NULL it also checks cu[r+1] - cu[r] == lengths[r]

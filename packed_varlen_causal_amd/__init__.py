@@ -10,6 +10,7 @@ package fails if the library has not been built.
 Entry points (same names as the C ABI without the ``pvc_`` prefix):
   pack_build            cu_seqlens, segment ids, positions, shifted labels,
                         loss mask, int64 target count, max_seqlen
+  pack_tokens           the per-token part of pack_build on a given cu_seqlens
   validate_cu_seqlens   device-side check of a caller cu_seqlens
   rope_thd_apply        per-segment rotary embedding on q and k
   attn_plan             tile plan for one cu_seqlens (reusable across layers)
@@ -31,7 +32,7 @@ import os
 import torch
 
 __all__ = [
-    "PvcError", "DEV_ERROR_BITS", "lib_path", "pack_build", "validate_cu_seqlens",
+    "PvcError", "DEV_ERROR_BITS", "lib_path", "pack_build", "pack_tokens", "validate_cu_seqlens",
     "rope_thd_apply", "AttnPlan", "attn_plan", "varlen_attn_fwd", "varlen_attn_bwd",
     "padded_attn_fwd_sbhd", "error_names", "attn_workspace_size", "attn_bwd_scratch_size",
     "packed_ce_loss", "ce_workspace_size", "AttnPlanQK", "attn_plan_qk", "varlen_attn_fwd_qk",
@@ -64,6 +65,7 @@ def _load() -> ctypes.CDLL:
         "pvc_version": ([], ctypes.c_char_p),
         "pvc_pack_build_workspace_size": ([I32], SZ),
         "pvc_pack_build": ([P, P, P, I32, I64, I32, P, P, P, P, P, P, P, P, P, SZ, P], I32),
+        "pvc_pack_tokens": ([P, P, P, I32, I64, I32, P, P, P, P, P, P, P], I32),
         "pvc_validate_cu_seqlens": ([P, I32, I64, I32, P, P, P], I32),
         "pvc_rope_thd_apply": ([P, P, P, P, I64, I32, I32, P, I32, F32, P, P], I32),
         "pvc_rope_thd_apply_interleaved": ([P, P, P, P, I64, I32, I32, P, I32, F32, P, P], I32),
@@ -162,13 +164,14 @@ def _new_error_word(device) -> torch.Tensor:
 def pack_build(lengths: torch.Tensor, tokens: torch.Tensor | None = None,
                is_pad: torch.Tensor | None = None, ignore_index: int = -100,
                total_tokens: int | None = None, dev_error: torch.Tensor | None = None,
-               check: bool = False, stream=None) -> dict:
+               check: bool = False, stream=None, per_token: bool = True) -> dict:
     """Packing metadata on the GPU.
 
     lengths int32 [nseg] (device), tokens int32 [T] (device, optional),
     is_pad uint8 [nseg] (optional).  ``total_tokens`` defaults to tokens.numel().
     Returns a dict of device tensors.  ``check=True`` synchronizes and raises on
-    device error bits.
+    device error bits.  ``per_token=False`` computes only cu_seqlens and
+    max_seqlen (the per-token pass can then run apart: :func:`pack_tokens`).
     """
     _require(lengths, "lengths", torch.int32, 1)
     dev = lengths.device
@@ -189,12 +192,13 @@ def pack_build(lengths: torch.Tensor, tokens: torch.Tensor | None = None,
     err = _new_error_word(dev) if dev_error is None else dev_error
     out = {
         "cu_seqlens": torch.empty(nseg + 1, dtype=torch.int32, device=dev),
-        "segment_ids": torch.empty(T, dtype=torch.int32, device=dev),
-        "position_ids": torch.empty(T, dtype=torch.int32, device=dev),
         "max_seqlen": torch.empty(1, dtype=torch.int32, device=dev),
         "dev_error": err,
     }
-    if tokens is not None:
+    if per_token:
+        out["segment_ids"] = torch.empty(T, dtype=torch.int32, device=dev)
+        out["position_ids"] = torch.empty(T, dtype=torch.int32, device=dev)
+    if per_token and tokens is not None:
         out["shifted_labels"] = torch.empty(T, dtype=torch.int32, device=dev)
         out["loss_mask"] = torch.empty(T, dtype=torch.uint8, device=dev)
         out["num_targets"] = torch.empty(1, dtype=torch.int64, device=dev)
@@ -202,12 +206,54 @@ def pack_build(lengths: torch.Tensor, tokens: torch.Tensor | None = None,
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     st = _lib.pvc_pack_build(
         _ptr(lengths), _ptr(is_pad), _ptr(tokens), nseg, T, ignore_index, _ptr(out["cu_seqlens"]),
-        _ptr(out["segment_ids"]), _ptr(out["position_ids"]), _ptr(out.get("shifted_labels")),
+        _ptr(out.get("segment_ids")), _ptr(out.get("position_ids")), _ptr(out.get("shifted_labels")),
         _ptr(out.get("loss_mask")), _ptr(out.get("num_targets")), _ptr(out["max_seqlen"]),
         _ptr(err), _ptr(ws), ws_bytes, _stream(stream))
     _check(st, "pack_build")
     if check:
         _raise_dev(err, "pack_build")
+    return out
+
+
+def pack_tokens(cu_seqlens: torch.Tensor, tokens: torch.Tensor | None = None, is_pad: torch.Tensor | None = None,
+                ignore_index: int = -100, total_tokens: int | None = None, dev_error: torch.Tensor | None = None,
+                check: bool = False, stream=None) -> dict:
+    """The per-token pass of :func:`pack_build` on an existing cu_seqlens
+    (int32 [nseg + 1], device): segment_ids, position_ids and, with tokens,
+    shifted_labels, loss_mask and num_targets."""
+    _require(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    dev = cu_seqlens.device
+    nseg = cu_seqlens.numel() - 1
+    if tokens is not None:
+        _require(tokens, "tokens", torch.int32, 1)
+        T = tokens.numel() if total_tokens is None else int(total_tokens)
+        if tokens.numel() != T:
+            raise ValueError("tokens.numel() must equal total_tokens")
+    elif total_tokens is None:
+        raise ValueError("total_tokens is required when tokens is not given")
+    else:
+        T = int(total_tokens)
+    if is_pad is not None:
+        _require(is_pad, "is_pad", torch.uint8, 1)
+        if is_pad.numel() != nseg:
+            raise ValueError("is_pad must have one flag per segment")
+    err = _new_error_word(dev) if dev_error is None else dev_error
+    out = {
+        "segment_ids": torch.empty(T, dtype=torch.int32, device=dev),
+        "position_ids": torch.empty(T, dtype=torch.int32, device=dev),
+        "dev_error": err,
+    }
+    if tokens is not None:
+        out["shifted_labels"] = torch.empty(T, dtype=torch.int32, device=dev)
+        out["loss_mask"] = torch.empty(T, dtype=torch.uint8, device=dev)
+        out["num_targets"] = torch.empty(1, dtype=torch.int64, device=dev)
+    st = _lib.pvc_pack_tokens(
+        _ptr(cu_seqlens), _ptr(is_pad), _ptr(tokens), nseg, T, ignore_index, _ptr(out["segment_ids"]),
+        _ptr(out["position_ids"]), _ptr(out.get("shifted_labels")), _ptr(out.get("loss_mask")),
+        _ptr(out.get("num_targets")), _ptr(err), _stream(stream))
+    _check(st, "pack_tokens")
+    if check:
+        _raise_dev(err, "pack_tokens")
     return out
 
 

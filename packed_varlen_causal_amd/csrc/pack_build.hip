@@ -260,6 +260,12 @@ __global__ __launch_bounds__(kTokThreads) void pack_tokens_kernel(
     }
 }
 
+// num_targets = 0 ahead of pack_tokens_kernel's atomic adds, when no scan
+// kernel (which clears it) runs first.
+__global__ void zero_count_kernel(int64_t* num_targets) {
+    if (threadIdx.x == 0) *num_targets = 0;
+}
+
 constexpr int kValThreads = 256;
 
 __global__ __launch_bounds__(kValThreads) void validate_kernel(
@@ -331,6 +337,25 @@ extern "C" pvc_status pvc_pack_build(const int32_t* lengths, const uint8_t* is_p
         hipLaunchKernelGGL(pack_tokens_kernel, dim3((unsigned)nblk), dim3(kTokThreads), 0, s,
                            cu_seqlens, is_pad, tokens, nseg, total_tokens, ignore_index, segment_ids,
                            position_ids, shifted_labels, loss_mask, num_targets, dev_error);
+    }
+    return launch_status();
+}
+
+extern "C" pvc_status pvc_pack_tokens(const int32_t* cu_seqlens, const uint8_t* is_pad, const int32_t* tokens,
+                                      int32_t nseg, int64_t total_tokens, int32_t ignore_index,
+                                      int32_t* segment_ids, int32_t* position_ids, int32_t* shifted_labels,
+                                      uint8_t* loss_mask, int64_t* num_targets, uint32_t* dev_error, void* stream) {
+    if (cu_seqlens == nullptr) return PVC_ERR_NULL;
+    if ((shifted_labels != nullptr || loss_mask != nullptr || num_targets != nullptr) && tokens == nullptr)
+        return PVC_ERR_NULL;
+    if (nseg < 1 || total_tokens < 1 || total_tokens > 0x7fffffffLL) return PVC_ERR_INVALID_ARG;
+    hipStream_t s = as_stream(stream);
+    if (num_targets != nullptr) hipLaunchKernelGGL(zero_count_kernel, dim3(1), dim3(64), 0, s, num_targets);
+    if (segment_ids || position_ids || shifted_labels || loss_mask || num_targets) {
+        const int64_t nblk = (total_tokens + kTokBlock - 1) / kTokBlock;
+        hipLaunchKernelGGL(pack_tokens_kernel, dim3((unsigned)nblk), dim3(kTokThreads), 0, s, cu_seqlens, is_pad,
+                           tokens, nseg, total_tokens, ignore_index, segment_ids, position_ids, shifted_labels,
+                           loss_mask, num_targets, dev_error);
     }
     return launch_status();
 }

@@ -75,6 +75,55 @@ def test_many_segments_multi_chunk_scan(pvc):
     _compare(got, P.pack_build(w.lengths, toks, w.is_pad))
 
 
+@pytest.mark.parametrize("name", CONFIG_NAMES)
+def test_pack_tokens_on_given_cu(pvc, name):
+    """The per-token pass alone, on pack_build's cu_seqlens (computed without
+    its own per-token pass) and on a second stream: the same bits as the
+    oracle, and num_targets cleared by the call (the word starts dirty)."""
+    w = make_workload(name)
+    toks = token_ids(w)
+    ref = P.pack_build(w.lengths, toks, w.is_pad)
+    side = torch.cuda.Stream()
+    meta = pvc.pack_build(dev_i32(w.lengths), total_tokens=w.total_tokens, per_token=False)
+    assert "segment_ids" not in meta and "shifted_labels" not in meta
+    done = torch.cuda.Event()
+    done.record()
+    side.wait_event(done)
+    pt = torch.from_numpy(np.asarray(w.is_pad, np.uint8)).cuda()
+    tt = dev_i32(toks)
+    with torch.cuda.stream(side):
+        got = pvc.pack_tokens(meta["cu_seqlens"], tt, pt, stream=side)
+        # through the C ABI into a count word that starts dirty
+        dirty = torch.full((1,), 12345, dtype=torch.int64, device="cuda")
+        st = pvc._lib.pvc_pack_tokens(pvc._ptr(meta["cu_seqlens"]), pvc._ptr(pt), pvc._ptr(tt), w.nseg,
+                                      w.total_tokens, -100, None, None, None, None, pvc._ptr(dirty),
+                                      pvc._ptr(got["dev_error"]), pvc._stream(side))
+        assert st == 0
+    torch.cuda.synchronize()
+    assert int(dirty.item()) == ref["num_targets"]
+    say(f"  pack_tokens {name}: T={w.total_tokens} nseg={w.nseg}")
+    assert int(meta["dev_error"].item()) == 0 and int(got["dev_error"].item()) == 0
+    assert (meta["cu_seqlens"].cpu().numpy() == ref["cu_seqlens"]).all()
+    assert int(meta["max_seqlen"].item()) == ref["max_seqlen"]
+    for key in ("segment_ids", "position_ids", "shifted_labels", "loss_mask"):
+        assert (got[key].cpu().numpy() == ref[key]).all(), key
+    assert int(got["num_targets"].item()) == ref["num_targets"]
+
+
+def test_pack_tokens_malformed_cu(pvc):
+    """A cu that ends short of T: the tokens past it get segment -1, position 0,
+    an ignored label, and PVC_DEV_TOTAL."""
+    cu = dev_i32([0, 3, 5])
+    toks = dev_i32(np.arange(7) + 10)
+    got = pvc.pack_tokens(cu, toks)
+    torch.cuda.synchronize()
+    assert int(got["dev_error"].item()) & 4
+    seg = got["segment_ids"].cpu().numpy()
+    assert seg.tolist() == [0, 0, 0, 1, 1, -1, -1]
+    assert got["shifted_labels"].cpu().numpy().tolist() == [11, 12, -100, 14, -100, -100, -100]
+    assert int(got["num_targets"].item()) == 3
+
+
 @pytest.mark.parametrize("lengths", [[1], [1] * 3000, [5000], [1, 2047, 1, 1, 3000, 7]])
 def test_edge_lengths(pvc, lengths):
     T = sum(lengths)

@@ -42,7 +42,8 @@ def test_header_declares_the_hot_path():
                  "pvc_attn_workspace_size", "pvc_pack_build_workspace_size", "pvc_status_string",
                  "pvc_varlen_attn_bwd_planned", "pvc_attn_bwd_scratch_size", "pvc_packed_ce_loss",
                  "pvc_ce_workspace_size", "pvc_attn_plan_padded", "pvc_rope_thd_apply_interleaved",
-                 "pvc_attn_plan_qk", "pvc_varlen_attn_fwd_qk_planned", "pvc_rope_thd_apply_ex"):
+                 "pvc_attn_plan_qk", "pvc_varlen_attn_fwd_qk_planned", "pvc_rope_thd_apply_ex",
+                 "pvc_pack_tokens"):
         assert must in names
 
 
@@ -114,6 +115,13 @@ def test_null_and_range_checks_return_before_gpu_work(lib):
     # large nseg needs a workspace
     assert lib.pvc_pack_build(fake, None, None, 1 << 20, 1 << 22, -100, fake, None, None, None, None,
                               None, None, None, None, 0, None) == 4
+
+    lib.pvc_pack_tokens.restype = I32
+    lib.pvc_pack_tokens.argtypes = [P, P, P, I32, I64, I32, P, P, P, P, P, P, P]
+    assert lib.pvc_pack_tokens(None, None, None, 3, 9, -100, fake, None, None, None, None, None, None) == 1
+    assert lib.pvc_pack_tokens(fake, None, None, 3, 9, -100, None, None, fake, None, None, None, None) == 1
+    assert lib.pvc_pack_tokens(fake, None, None, 0, 9, -100, fake, None, None, None, None, None, None) == 2
+    assert lib.pvc_pack_tokens(fake, None, None, 3, 0, -100, fake, None, None, None, None, None, None) == 2
 
     lib.pvc_rope_thd_apply.restype = I32
     lib.pvc_rope_thd_apply.argtypes = [P, P, P, P, I64, I32, I32, P, I32, F32, P, P]
