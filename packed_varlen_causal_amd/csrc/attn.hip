@@ -88,17 +88,24 @@ __global__ __launch_bounds__(kCheckThreads) void plan_check_kernel(
         const int32_t* __restrict__ cu, const int32_t* __restrict__ cu_p, int32_t nseg, int64_t T,
         int32_t max_seqlen, int32_t causal, int32_t* __restrict__ header, int32_t ntiles, uint32_t* dev_error) {
     __shared__ unsigned s_err;
+    __shared__ int s_max;
     const int t = threadIdx.x;
-    if (t == 0) s_err = 0;
+    if (t == 0) {
+        s_err = 0;
+        s_max = 0;
+    }
     __syncthreads();
     // the cu_seqlens contract
     uint32_t err = 0;
+    int64_t mx = 0;
     for (int64_t r = t; r < nseg; r += kCheckThreads) {
         const int64_t a = cu[r], b = cu[r + 1];
         if (b <= a) err |= PVC_DEV_NOT_INCREASING;
         if (b - a > max_seqlen) err |= PVC_DEV_MAXSEQ;
         if (cu_p != nullptr && (int64_t)cu_p[r + 1] - cu_p[r] < b - a) err |= PVC_DEV_PADDED;
+        mx = max(mx, b - a);
     }
+    if (mx > 0) atomicMax(&s_max, (int)min<int64_t>(mx, 0x7fffffff));
     if (t == 0) {
         if (cu[0] != 0) err |= PVC_DEV_CU0;
         if (cu_p == nullptr) {
@@ -119,6 +126,7 @@ __global__ __launch_bounds__(kCheckThreads) void plan_check_kernel(
         header[HDR_VALID] = s_err == 0 ? 1 : 0;
         header[HDR_FOLDED] = 0;
         header[HDR_TK] = (int32_t)T;
+        header[HDR_MAXLEN] = s_max;
         raise_error(dev_error, s_err);
     }
 }
@@ -150,15 +158,22 @@ __global__ __launch_bounds__(kCheckThreads) void plan_check_qk_kernel(
         int32_t max_q, int32_t max_k, int32_t causal, int32_t* __restrict__ header, int32_t ntiles,
         uint32_t* dev_error) {
     __shared__ unsigned s_err;
+    __shared__ int s_max;
     const int t = threadIdx.x;
-    if (t == 0) s_err = 0;
+    if (t == 0) {
+        s_err = 0;
+        s_max = 0;
+    }
     __syncthreads();
     uint32_t err = 0;
+    int64_t mx = 0;
     for (int64_t r = t; r < nseg; r += kCheckThreads) {
         const int64_t a = cu_q[r], b = cu_q[r + 1], ka = cu_k[r], kb = cu_k[r + 1];
         if (b <= a || kb <= ka) err |= PVC_DEV_NOT_INCREASING;
         if (b - a > max_q || kb - ka > max_k) err |= PVC_DEV_MAXSEQ;
+        mx = max(mx, b - a);
     }
+    if (mx > 0) atomicMax(&s_max, (int)min<int64_t>(mx, 0x7fffffff));
     if (t == 0) {
         if (cu_q[0] != 0 || cu_k[0] != 0) err |= PVC_DEV_CU0;
         if ((int64_t)cu_q[nseg] != Tq || (int64_t)cu_k[nseg] != Tk) err |= PVC_DEV_TOTAL;
@@ -174,6 +189,7 @@ __global__ __launch_bounds__(kCheckThreads) void plan_check_qk_kernel(
         header[HDR_VALID] = s_err == 0 ? 1 : 0;
         header[HDR_FOLDED] = 1;
         header[HDR_TK] = (int32_t)Tk;
+        header[HDR_MAXLEN] = s_max;
         raise_error(dev_error, s_err);
     }
 }
@@ -198,6 +214,7 @@ struct AttnParams {
     int32_t causal_flag;       // causal as the caller asked (checked against the plan)
     int32_t ntiles;            // THD: tiles; SBHD: tiles per sample
     int32_t items;             // heads x tiles (x batch for SBHD)
+    int32_t head_block;        // THD: heads interleaved per segment run (item order)
     int32_t B, L;              // SBHD: batch and padded length
     float scale_log2;          // log2(e) / sqrt(d)
     uint32_t* dev_error;
@@ -253,12 +270,49 @@ void attn_fwd_kernel(AttnParams p) {
         // pos of that run takes the tile mirrored in it.
         // (A plan of separate key boundaries keeps the query segments apart:
         // its row ranges are key rows.)
-        head = logical / p.ntiles;
-        const int pos = logical - head * p.ntiles;
-        const int2 sr = (p.folded ? p.qseg : p.rows)[(int64_t)pos * kBM];   // segment of the first row at pos
-        const int ta = (sr.x + kBM - 1) / kBM;
-        const int tb = min((sr.y + kBM - 1) / kBM, p.ntiles);
-        const int tile = (pos >= ta && pos < tb) ? ta + tb - 1 - pos : pos;
+        // Heads go in blocks of head_block (one block per XCD when the head
+        // count is a multiple of 8); inside a block, a segment's tiles for
+        // every head of the block come together, so the heavy tiles of all
+        // of an XCD's heads start early instead of its last head's starting
+        // near the end.  Item i of a block of hx heads: position
+        // p = i / hx lies in the run [ta, tb) of its segment, whose items
+        // are [hx ta, hx tb); the offset in that run gives the head and the
+        // mirrored tile.  Positions the plan does not place in a run (a
+        // padding row's empty range) form runs of one.  Every head and tile
+        // stays in range whatever the plan holds; a plan that is not sealed
+        // computes and writes nothing.
+        // When no segment spans more than two tiles every tile is light and
+        // the blocks are single heads (the plain head-major order).
+        const int hb = p.header[HDR_MAXLEN] > 2 * kBM ? p.head_block : 1;
+        const int2* seg_of = p.folded ? p.qseg : p.rows;
+        int tile;
+        if (hb == 1) {
+            head = logical / p.ntiles;
+            const int pos = logical - head * p.ntiles;
+            const int2 sr = seg_of[(int64_t)pos * kBM];       // segment of the first row at pos
+            const int ta = (sr.x + kBM - 1) / kBM;
+            const int tb = min((sr.y + kBM - 1) / kBM, p.ntiles);
+            tile = (pos >= ta && pos < tb) ? ta + tb - 1 - pos : pos;
+        } else {
+            const int per_block = hb * p.ntiles;
+            const int hblk = logical / per_block;
+            const int h0 = hblk * hb;
+            const int hx = min(hb, p.H - h0);
+            const int i = logical - hblk * per_block;        // < hx * ntiles
+            const int pos = i / hx;
+            const int2 sr = seg_of[(int64_t)pos * kBM];
+            int ta = (sr.x + kBM - 1) / kBM;
+            int tb = min((sr.y + kBM - 1) / kBM, p.ntiles);
+            if (!(pos >= ta && pos < tb)) {
+                ta = pos;
+                tb = pos + 1;
+            }
+            const int run = tb - ta;
+            const int local = i - hx * ta;
+            const int hl = local / run;
+            head = h0 + hl;
+            tile = tb - 1 - (local - hl * run);
+        }
         r0 = tile * kBM;
         r1 = (int)min<int64_t>((int64_t)r0 + kBM, p.T);
         last_row = (int)(p.Tk - 1);
@@ -642,6 +696,10 @@ pvc_status launch_thd(const AttnParams& prm, bool causal, int32_t out_dtype, hip
     return launch_fwd_t<D, false, false>(prm, causal, io_f32(out_dtype), s);
 }
 
+// Heads per block of the item order: one block per XCD when the head count
+// divides by the XCD count, else single heads.
+inline int32_t head_block(int32_t heads) { return heads % kNumXcd == 0 ? heads / kNumXcd : 1; }
+
 // Per-lane staging offsets span one 32-row stage in 32 bits (32 * 2^24 * 2 B).
 constexpr int64_t kMaxRowElems = (int64_t)1 << 24;
 
@@ -741,6 +799,7 @@ extern "C" pvc_status pvc_varlen_attn_fwd_planned(const void* q, const void* k, 
     prm.causal_flag = causal != 0 ? 1 : 0;
     prm.ntiles = (int32_t)L.ntiles;
     prm.items = (int32_t)(L.ntiles * heads);
+    prm.head_block = head_block(heads);
     prm.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
     prm.dev_error = dev_error;
     hipStream_t s = as_stream(stream);
@@ -813,6 +872,7 @@ extern "C" pvc_status pvc_varlen_attn_fwd_qk_planned(const void* q, const void* 
     prm.causal_flag = causal != 0 ? 1 : 0;
     prm.ntiles = (int32_t)L.ntiles;
     prm.items = (int32_t)(L.ntiles * heads);
+    prm.head_block = head_block(heads);
     prm.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
     prm.dev_error = dev_error;
     hipStream_t s = as_stream(stream);

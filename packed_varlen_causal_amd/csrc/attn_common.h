@@ -23,9 +23,10 @@ constexpr int32_t kPlanMagic = 0x31435650;   // "PVC1"
 
 // Plan header (int32 slots).  HDR_FOLDED: the plan of separate query / key
 // boundaries, whose row ranges already hold the causal limit (the kernels
-// then run without their own diagonal); HDR_TK: rows of K and V.
+// then run without their own diagonal); HDR_TK: rows of K and V;
+// HDR_MAXLEN: the longest (query) segment, which picks the forward's item order.
 enum { HDR_MAGIC = 0, HDR_T = 1, HDR_CAUSAL = 2, HDR_NTILES = 3, HDR_ERR = 4, HDR_VALID = 5, HDR_FOLDED = 6,
-       HDR_TK = 7 };
+       HDR_TK = 7, HDR_MAXLEN = 8 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -97,6 +97,23 @@ def test_small_workloads_every_element(pvc, name, causal):
     assert lse_err < 5e-3
 
 
+@pytest.mark.parametrize("heads", [16, 24])
+@pytest.mark.parametrize("causal", [True, False])
+def test_head_counts_divisible_by_the_xcds(pvc, heads, causal):
+    """Head counts that are multiples of 8 take the item order that
+    interleaves a block of heads inside each segment's run of tiles (2 and 3
+    heads per block here): every element of every head against the oracle."""
+    lengths = np.array([700, 3, 129, 1, 250, 512, 64, 1200, 33])
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    T, d = int(cu[-1]), 128
+    say(f"  head blocks: H={heads} causal={causal} T={T}")
+    q, k, v = (_rand_bits((T, heads, d), s) for s in (31, 32, 33))
+    ob, of, ls = _run(pvc, q, k, v, cu, causal)
+    ref, ref_lse = A.attention(q, k, v, cu, causal, threads=THREADS)
+    three_part_check(of, ob, ref)
+    assert np.abs(ls.cpu().numpy().T - ref_lse).max() < 5e-3
+
+
 @pytest.mark.parametrize("lengths", [[1], [1] * 200, [1000], [130, 1, 127, 300, 2, 64, 65],
                                      [33, 31, 32, 64, 96, 129], [4096 + 17]])
 def test_edge_lengths(pvc, lengths):

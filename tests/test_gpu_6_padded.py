@@ -73,6 +73,22 @@ def test_forward_small_workloads(pvc, name, align, causal):
     assert np.abs(lse[real] - ref_lse[real]).max() < 5e-3
 
 
+def test_forward_sixteen_heads(pvc):
+    """16 heads: the item order interleaves two heads per segment run, which
+    must also hold for padding rows (runs of one position)."""
+    w = make_workload("sft", scale="small")
+    cu, cp = _layout(w.lengths, 64)
+    Ts, H, d = int(cp[-1]), 16, w.head_dim
+    q, k, v = (_bits((Ts, H, d), s) for s in (41, 42, 43))
+    _, _, ob, of, ls = _fwd(pvc, q, k, v, cu, cp, True)
+    ref, ref_lse = A.attention_padded(q, k, v, cu, cp, True, threads=16)
+    real = A.storage_rows(cu, cp)
+    gap = np.setdiff1d(np.arange(Ts), real)
+    three_part_check(of, ob, ref[real], rows=real)
+    assert (host_bits(ob)[gap] == 0).all()
+    assert np.abs(ls.cpu().numpy().T[real] - ref_lse[real]).max() < 5e-3
+
+
 def test_padding_content_changes_nothing(pvc):
     w = make_workload("sft", scale="small")
     cu, cp = _layout(w.lengths, 64)

@@ -62,6 +62,7 @@ def test_small_prefill_every_row(pvc, causal):
     ([5, 1, 130, 33, 64], [3, 7, 130, 300, 64], 4, 1),    # Lk < Lq, decode, square, long prefix
     ([1] * 40, [200] * 40, 8, 8),                          # forty single-token decodes
     ([257, 2, 129], [257, 2, 129], 6, 3),                  # square requests, grouped heads
+    ([300, 17, 128, 1, 90], [500, 17, 300, 40, 90], 16, 4),  # two heads per item-order block
 ])
 def test_edge_requests(pvc, lq, lk, hq, hkv):
     d = 128 if hq % 2 == 0 else 64
