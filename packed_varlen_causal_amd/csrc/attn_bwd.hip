@@ -59,6 +59,7 @@ struct BwdParams {
     int32_t H;
     int32_t ntiles;
     int32_t items;
+    int32_t head_block;        // heads interleaved per segment run (item order)
     float scale_log2;          // log2(e) / sqrt(d)
     float scale;               // 1 / sqrt(d)
     uint32_t* dev_error;
@@ -147,6 +148,37 @@ __device__ inline int xcd_logical() {
     return (blockIdx.x % kNumXcd) * per_xcd + blockIdx.x / kNumXcd;
 }
 
+// Logical item -> (head, tile) in the forward's item order: heads in blocks
+// of head_block when some segment spans more than two tiles (else single
+// heads), and inside a block a segment's run of tiles for every head of the
+// block together.  MIRROR takes a run's tiles from last to first (query tiles:
+// the last is the heaviest), else first to last (key tiles: the first is
+// seen by every later query).  Heads and tiles stay in range whatever the
+// plan holds; an unsealed plan computes nothing.
+template <bool MIRROR>
+__device__ inline void item_of(const BwdParams& p, int logical, int& head, int& tile) {
+    const int hb = p.header[HDR_MAXLEN] > 2 * kBM ? p.head_block : 1;
+    const int per_block = hb * p.ntiles;
+    const int hblk = logical / per_block;
+    const int h0 = hblk * hb;
+    const int hx = min(hb, p.H - h0);
+    const int i = logical - hblk * per_block;            // < hx * ntiles
+    const int pos = i / hx;
+    const int2 sr = p.rows[(int64_t)pos * kBM];          // segment of the first row at pos
+    int ta = (sr.x + kBM - 1) / kBM;
+    int tb = min((sr.y + kBM - 1) / kBM, p.ntiles);
+    if (!(pos >= ta && pos < tb)) {
+        ta = pos;
+        tb = pos + 1;
+    }
+    const int run = tb - ta;
+    const int local = i - hx * ta;
+    const int hl = local / run;
+    const int off = local - hl * run;
+    head = h0 + hl;
+    tile = MIRROR ? tb - 1 - off : ta + off;
+}
+
 // Plan header check, read in one piece (see the forward).
 __device__ inline bool plan_sealed(const BwdParams& p, bool causal, bool& sealed) {
     const int4 h0 = *reinterpret_cast<const int4*>(p.header);
@@ -184,14 +216,10 @@ void bwd_dq_kernel(BwdParams p) {
 
     const int logical = xcd_logical();
     if (logical >= p.items) return;
-    // (head, tile) in the forward's order: segments in buffer order, each
-    // segment's tiles mirrored so its heaviest (last) tile starts first
-    const int head = logical / p.ntiles;
-    const int pos = logical - head * p.ntiles;
-    const int2 sr = p.rows[(int64_t)pos * kBM];
-    const int ta = (sr.x + kBM - 1) / kBM;
-    const int tb = min((sr.y + kBM - 1) / kBM, p.ntiles);
-    const int tile = (pos >= ta && pos < tb) ? ta + tb - 1 - pos : pos;
+    // (head, tile) in the forward's order: a segment's heaviest (last) query
+    // tile starts first
+    int head, tile;
+    item_of<true>(p, logical, head, tile);
     const int r0 = tile * kBM;
     const int r1 = (int)min<int64_t>((int64_t)r0 + kBM, p.T);
     const int last_row = (int)(p.T - 1);
@@ -455,10 +483,10 @@ void bwd_dkdv_kernel(BwdParams p) {
 
     const int logical = xcd_logical();
     if (logical >= p.items) return;
-    // key tiles in buffer order: a segment's first key tiles are seen by all
-    // its later queries, so they are its heaviest and start first
-    const int head = logical / p.ntiles;
-    const int tile = logical - head * p.ntiles;
+    // key tiles in buffer order inside each run: a segment's first key tiles
+    // are seen by all its later queries, so they are its heaviest and start first
+    int head, tile;
+    item_of<false>(p, logical, head, tile);
     const int r0 = tile * kBM;
     const int r1 = (int)min<int64_t>((int64_t)r0 + kBM, p.T);
     const int last_row = (int)(p.T - 1);
@@ -846,6 +874,7 @@ extern "C" pvc_status pvc_varlen_attn_bwd_planned(const void* q, const void* k, 
     prm.H = heads;
     prm.ntiles = (int32_t)L.ntiles;
     prm.items = (int32_t)(L.ntiles * heads);
+    prm.head_block = heads % kNumXcd == 0 ? heads / kNumXcd : 1;
     prm.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
     prm.scale = (float)(1.0 / sqrt((double)head_dim));
     prm.dev_error = dev_error;
