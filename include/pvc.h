@@ -232,7 +232,10 @@ size_t pvc_attn_workspace_size(int64_t total_tokens, int32_t nseg);
  * allow(i,j) = same segment and p_j <= p_i; [opworld] "pitfall one":
  * cross-document blocks are pure waste, which the varlen kernel never
  * computes).  Query tiles of 128 rows run segment by segment in buffer order,
- * each segment's tiles from its end (the heaviest) to its start.
+ * each segment's tiles from its end (the heaviest) to its start; with a head
+ * count that is a multiple of 8 and a segment longer than two tiles, each
+ * segment's run of tiles comes once for every head an XCD owns before the
+ * next segment's.  The plan records its longest segment for that choice.
  * cu_seqlens is read on the device only; it is validated as
  * pvc_validate_cu_seqlens would (without lengths) and an invalid cu yields an
  * empty plan plus the error bits.  The plan depends only on
