@@ -252,6 +252,8 @@ void attn_fwd_kernel(AttnParams p) {
     const int logical = (blockIdx.x % kNumXcd) * per_xcd + blockIdx.x / kNumXcd;
     if (logical >= p.items) return;
     int head, b = 0, r0, r1, last_row;
+    int4 hd0 = {0, 0, 0, 0}, hd1 = {0, 0, 0, 0};      // THD: the plan header
+    int seg_lo = 0;
     if constexpr (SBHD) {
         const int per_head = p.B * p.ntiles;
         head = logical / per_head;
@@ -282,37 +284,46 @@ void attn_fwd_kernel(AttnParams p) {
         // stays in range whatever the plan holds; a plan that is not sealed
         // computes and writes nothing.
         // When no segment spans more than two tiles every tile is light and
-        // the blocks are single heads (the plain head-major order).
-        const int hb = p.header[HDR_MAXLEN] > 2 * kBM ? p.head_block : 1;
+        // the blocks are single heads (the plain head-major order).  The
+        // plan header and the segment lookups of both orders are loaded
+        // together, so the decode costs one memory round trip.
+        hd0 = *reinterpret_cast<const int4*>(p.header);
+        hd1 = *reinterpret_cast<const int4*>(p.header + 4);
+        const int maxlen = p.header[HDR_MAXLEN];
         const int2* seg_of = p.folded ? p.qseg : p.rows;
+        const int hm_head = logical / p.ntiles;                 // head-major
+        const int hm_pos = logical - hm_head * p.ntiles;
+        const int per_block = p.head_block * p.ntiles;          // interleaved
+        const int hblk = logical / per_block;
+        const int h0 = hblk * p.head_block;
+        const int hx = min(p.head_block, p.H - h0);
+        const int i = logical - hblk * per_block;               // < hx * ntiles
+        const int il_pos = i / hx;
+        const int2 sr_hm = seg_of[(int64_t)hm_pos * kBM];       // segment of the first row at pos
+        const int2 sr_il = seg_of[(int64_t)il_pos * kBM];
+        const bool il = maxlen > 2 * kBM && p.head_block > 1;
+        const int pos = il ? il_pos : hm_pos;
+        const int2 sr = il ? sr_il : sr_hm;
+        int ta = (sr.x + kBM - 1) / kBM;
+        int tb = min((sr.y + kBM - 1) / kBM, p.ntiles);
+        if (!(pos >= ta && pos < tb)) {
+            ta = pos;
+            tb = pos + 1;
+        }
         int tile;
-        if (hb == 1) {
-            head = logical / p.ntiles;
-            const int pos = logical - head * p.ntiles;
-            const int2 sr = seg_of[(int64_t)pos * kBM];       // segment of the first row at pos
-            const int ta = (sr.x + kBM - 1) / kBM;
-            const int tb = min((sr.y + kBM - 1) / kBM, p.ntiles);
-            tile = (pos >= ta && pos < tb) ? ta + tb - 1 - pos : pos;
-        } else {
-            const int per_block = hb * p.ntiles;
-            const int hblk = logical / per_block;
-            const int h0 = hblk * hb;
-            const int hx = min(hb, p.H - h0);
-            const int i = logical - hblk * per_block;        // < hx * ntiles
-            const int pos = i / hx;
-            const int2 sr = seg_of[(int64_t)pos * kBM];
-            int ta = (sr.x + kBM - 1) / kBM;
-            int tb = min((sr.y + kBM - 1) / kBM, p.ntiles);
-            if (!(pos >= ta && pos < tb)) {
-                ta = pos;
-                tb = pos + 1;
-            }
+        if (il) {
             const int run = tb - ta;
             const int local = i - hx * ta;
             const int hl = local / run;
             head = h0 + hl;
             tile = tb - 1 - (local - hl * run);
+        } else {
+            head = hm_head;
+            tile = ta + tb - 1 - pos;
         }
+        // a self-attention plan: the tile's first row lies in segment sr, so
+        // its keys start at sr.x (the first row's range) with no further load
+        seg_lo = sr.x;
         r0 = tile * kBM;
         r1 = (int)min<int64_t>((int64_t)r0 + kBM, p.T);
         last_row = (int)(p.Tk - 1);
@@ -361,7 +372,7 @@ void attn_fwd_kernel(AttnParams p) {
         k_lo = 0;
         k_hi = CAUSAL ? r1 : p.L;
     } else {
-        k_lo = p.rows[r0].x;
+        k_lo = p.folded ? p.rows[r0].x : seg_lo;
         k_hi = CAUSAL ? r1 : p.rows[r1 - 1].y;
     }
 
@@ -372,17 +383,15 @@ void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
         for (int s = 0; s < NS; ++s) qreg[s] = *reinterpret_cast<const x8*>(qp + 16 * s);
     }
-    // The plan header is read in one piece beside the row ranges (all of
-    // those loads stay inside their buffers whatever the header holds).
-    // A stale or failed plan turns the tile into no stages and no output, so
-    // no address is ever formed from plan data that was not sealed.
+    // The plan header was read with the decode.  Every load so far stays
+    // inside its buffer whatever the plan holds; a stale or failed plan
+    // turns the tile into no stages and no output, so no K/V address is ever
+    // formed from plan data that was not sealed.
     bool plan_ok = true;
     if constexpr (!SBHD) {
-        const int4 h0 = *reinterpret_cast<const int4*>(p.header);
-        const int4 h1 = *reinterpret_cast<const int4*>(p.header + 4);
-        const bool sealed = (h0.x == kPlanMagic) & (h0.y == (int32_t)p.T) & (h0.z == p.causal_flag) &
-                            (h0.w == p.ntiles) & (h1.z == p.folded) & (h1.w == (int32_t)p.Tk);
-        plan_ok = sealed & (h1.y == 1);
+        const bool sealed = (hd0.x == kPlanMagic) & (hd0.y == (int32_t)p.T) & (hd0.z == p.causal_flag) &
+                            (hd0.w == p.ntiles) & (hd1.z == p.folded) & (hd1.w == (int32_t)p.Tk);
+        plan_ok = sealed & (hd1.y == 1);
         if (!sealed && threadIdx.x == 0) raise_error(p.dev_error, PVC_DEV_PLAN);
     }
     const int nstages = plan_ok ? (k_hi - k_lo + kBN - 1) / kBN : 0;
