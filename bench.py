@@ -481,7 +481,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # untimed steps before the timed ones: a fresh process needs about 50
+    # steps (~30 ms of this load) before the forward reaches its sustained
+    # rate (5 warmup steps read 319 TFLOP/s, 50 read 364, 300 read 366)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="sft")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip padded baseline and other workloads")
