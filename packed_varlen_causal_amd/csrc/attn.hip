@@ -6,10 +6,11 @@
 // block-diagonal visibility; [opworld] "pitfall one": the varlen kernel skips
 // cross-document blocks instead of masking them).
 //
-// Plan (two launches, device-side only, no host synchronization):
-//   plan_rows_kernel   every token i gets its segment's key range
-//                      [cu[r], cu[r+1]) by binary search (8 B per token);
-//   plan_check_kernel  one block validates cu_seqlens and seals the header.
+// Plan (device-side only, no host synchronization):
+//   every token i gets its segment's key range [cu[r], cu[r+1]) by binary
+//   search (8 B per token), and one workgroup validates cu_seqlens and seals
+//   the header; one launch (plan_fused_kernel, its last workgroup doing the
+//   check) up to 16,384 segments, else plan_rows_kernel + plan_check_kernel.
 // Query tiles are aligned to the buffer, not to segments: tile w covers rows
 // [128w, 128w+128).  A tile may hold the tail of one segment and the head of
 // the next, or many short segments; every row carries its own key range, so
@@ -57,36 +58,41 @@ using namespace attn;
 
 // ------------------------------------------------------------------ plan
 
-__global__ __launch_bounds__(256) void plan_rows_kernel(const int32_t* __restrict__ cu, int32_t nseg,
-                                                        int64_t T, int2* __restrict__ rows) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= T) return;
+// Row i's key range: its segment [cu[r], cu[r+1]) (clamped into [0, T)), or
+// {i, i+1} for a row outside every segment of a malformed cu.
+__device__ inline int2 plan_row(const int32_t* __restrict__ cu, int32_t nseg, int64_t T, int64_t i) {
     const int32_t r = upper_segment(cu, nseg, i);
     const int64_t st = max<int64_t>(cu[r], 0), en = min<int64_t>(cu[r + 1], T);
     const bool ok = st <= i && i < en;
-    rows[i] = ok ? make_int2((int)st, (int)en) : make_int2((int)i, (int)(i + 1));
+    return ok ? make_int2((int)st, (int)en) : make_int2((int)i, (int)(i + 1));
 }
 
 // Padded storage: segment r's L_r = cu[r+1] - cu[r] tokens sit at rows
 // [cu_p[r], cu_p[r] + L_r) of a slot that ends at cu_p[r+1]; the rest of the
 // slot is padding, whose rows get an empty key range {i, i} (no key, output 0).
-__global__ __launch_bounds__(256) void plan_rows_padded_kernel(const int32_t* __restrict__ cu,
-                                                               const int32_t* __restrict__ cu_p, int32_t nseg,
-                                                               int64_t T, int2* __restrict__ rows) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= T) return;
+__device__ inline int2 plan_row_padded(const int32_t* __restrict__ cu, const int32_t* __restrict__ cu_p,
+                                       int32_t nseg, int64_t T, int64_t i) {
     const int32_t r = upper_segment(cu_p, nseg, i);
     const int64_t st = min<int64_t>(max<int64_t>(cu_p[r], 0), T);
     const int64_t len = (int64_t)cu[r + 1] - cu[r];
     const int64_t en = min<int64_t>(max<int64_t>(st + len, st), T);
     const bool ok = st <= i && i < en;
-    rows[i] = ok ? make_int2((int)st, (int)en) : make_int2((int)i, (int)i);
+    return ok ? make_int2((int)st, (int)en) : make_int2((int)i, (int)i);
 }
 
-// Validates cu (and, for padded storage, cu_p) and seals the plan header.
-__global__ __launch_bounds__(kCheckThreads) void plan_check_kernel(
-        const int32_t* __restrict__ cu, const int32_t* __restrict__ cu_p, int32_t nseg, int64_t T,
-        int32_t max_seqlen, int32_t causal, int32_t* __restrict__ header, int32_t ntiles, uint32_t* dev_error) {
+__global__ __launch_bounds__(256) void plan_rows_kernel(const int32_t* __restrict__ cu,
+                                                        const int32_t* __restrict__ cu_p, int32_t nseg,
+                                                        int64_t T, int2* __restrict__ rows) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= T) return;
+    rows[i] = cu_p == nullptr ? plan_row(cu, nseg, T, i) : plan_row_padded(cu, cu_p, nseg, T, i);
+}
+
+// Validates cu (and, for padded storage, cu_p) and seals the plan header;
+// one workgroup of any size.
+__device__ void plan_check_block(const int32_t* __restrict__ cu, const int32_t* __restrict__ cu_p, int32_t nseg,
+                                 int64_t T, int32_t max_seqlen, int32_t causal, int32_t* __restrict__ header,
+                                 int32_t ntiles, uint32_t* dev_error) {
     __shared__ unsigned s_err;
     __shared__ int s_max;
     const int t = threadIdx.x;
@@ -98,7 +104,7 @@ __global__ __launch_bounds__(kCheckThreads) void plan_check_kernel(
     // the cu_seqlens contract
     uint32_t err = 0;
     int64_t mx = 0;
-    for (int64_t r = t; r < nseg; r += kCheckThreads) {
+    for (int64_t r = t; r < nseg; r += blockDim.x) {
         const int64_t a = cu[r], b = cu[r + 1];
         if (b <= a) err |= PVC_DEV_NOT_INCREASING;
         if (b - a > max_seqlen) err |= PVC_DEV_MAXSEQ;
@@ -128,6 +134,47 @@ __global__ __launch_bounds__(kCheckThreads) void plan_check_kernel(
         header[HDR_TK] = (int32_t)T;
         header[HDR_MAXLEN] = s_max;
         raise_error(dev_error, s_err);
+    }
+}
+
+__global__ __launch_bounds__(kCheckThreads) void plan_check_kernel(
+        const int32_t* __restrict__ cu, const int32_t* __restrict__ cu_p, int32_t nseg, int64_t T,
+        int32_t max_seqlen, int32_t causal, int32_t* __restrict__ header, int32_t ntiles, uint32_t* dev_error) {
+    plan_check_block(cu, cu_p, nseg, T, max_seqlen, causal, header, ntiles, dev_error);
+}
+
+// Rows and check in one launch: workgroups [0, G - 1) write the row ranges,
+// the last one validates and seals (the header and the rows are both complete
+// when the launch ends, before any kernel that reads the plan).
+__global__ __launch_bounds__(256) void plan_fused_kernel(const int32_t* __restrict__ cu,
+                                                         const int32_t* __restrict__ cu_p, int32_t nseg, int64_t T,
+                                                         int32_t max_seqlen, int32_t causal,
+                                                         int32_t* __restrict__ header, int32_t ntiles,
+                                                         int2* __restrict__ rows, uint32_t* dev_error) {
+    if (blockIdx.x == gridDim.x - 1) {
+        plan_check_block(cu, cu_p, nseg, T, max_seqlen, causal, header, ntiles, dev_error);
+        return;
+    }
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= T) return;
+    rows[i] = cu_p == nullptr ? plan_row(cu, nseg, T, i) : plan_row_padded(cu, cu_p, nseg, T, i);
+}
+
+// Up to this many segments the check shares the rows' launch (a 256-thread
+// workgroup); beyond, it runs alone with 1024 threads.
+constexpr int32_t kFusedCheckSegs = 16384;
+
+// The self-attention plan, plain (cu_p NULL) or padded storage.
+void launch_plan(const int32_t* cu, const int32_t* cu_p, int32_t nseg, int64_t T, int32_t max_seqlen,
+                 int32_t causal, int32_t* header, int32_t ntiles, int2* rows, uint32_t* dev_error, hipStream_t s) {
+    const int64_t nblk = (T + 255) / 256;
+    if (nseg <= kFusedCheckSegs) {
+        hipLaunchKernelGGL(plan_fused_kernel, dim3((unsigned)(nblk + 1)), dim3(256), 0, s, cu, cu_p, nseg, T,
+                           max_seqlen, causal, header, ntiles, rows, dev_error);
+    } else {
+        hipLaunchKernelGGL(plan_rows_kernel, dim3((unsigned)nblk), dim3(256), 0, s, cu, cu_p, nseg, T, rows);
+        hipLaunchKernelGGL(plan_check_kernel, dim3(1), dim3(kCheckThreads), 0, s, cu, cu_p, nseg, T, max_seqlen,
+                           causal, header, ntiles, dev_error);
     }
 }
 
@@ -741,12 +788,8 @@ extern "C" pvc_status pvc_attn_plan(const int32_t* cu_seqlens, int32_t nseg, int
     char* ws = static_cast<char*>(workspace);
     auto* header = reinterpret_cast<int32_t*>(ws + L.header);
     auto* rows = reinterpret_cast<int2*>(ws + L.rows);
-    hipStream_t s = as_stream(stream);
-    const int64_t nblk = (total_tokens + 255) / 256;
-    hipLaunchKernelGGL(plan_rows_kernel, dim3((unsigned)nblk), dim3(256), 0, s, cu_seqlens, nseg,
-                       total_tokens, rows);
-    hipLaunchKernelGGL(plan_check_kernel, dim3(1), dim3(kCheckThreads), 0, s, cu_seqlens, nullptr, nseg,
-                       total_tokens, max_seqlen, causal ? 1 : 0, header, (int32_t)L.ntiles, dev_error);
+    launch_plan(cu_seqlens, nullptr, nseg, total_tokens, max_seqlen, causal ? 1 : 0, header, (int32_t)L.ntiles, rows,
+                dev_error, as_stream(stream));
     return launch_status();
 }
 
@@ -761,12 +804,8 @@ extern "C" pvc_status pvc_attn_plan_padded(const int32_t* cu_seqlens, const int3
     char* ws = static_cast<char*>(workspace);
     auto* header = reinterpret_cast<int32_t*>(ws + L.header);
     auto* rows = reinterpret_cast<int2*>(ws + L.rows);
-    hipStream_t s = as_stream(stream);
-    const int64_t nblk = (total_rows + 255) / 256;
-    hipLaunchKernelGGL(plan_rows_padded_kernel, dim3((unsigned)nblk), dim3(256), 0, s, cu_seqlens,
-                       cu_seqlens_padded, nseg, total_rows, rows);
-    hipLaunchKernelGGL(plan_check_kernel, dim3(1), dim3(kCheckThreads), 0, s, cu_seqlens, cu_seqlens_padded,
-                       nseg, total_rows, max_seqlen, causal ? 1 : 0, header, (int32_t)L.ntiles, dev_error);
+    launch_plan(cu_seqlens, cu_seqlens_padded, nseg, total_rows, max_seqlen, causal ? 1 : 0, header,
+                (int32_t)L.ntiles, rows, dev_error, as_stream(stream));
     return launch_status();
 }
 

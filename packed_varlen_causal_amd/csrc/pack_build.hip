@@ -10,7 +10,8 @@
 //
 // Work layout.  The scan runs in chunks of 8192 lengths per 1024-thread block
 // (one block when nseg <= 8192, else reduce / top-scan / apply).  The token
-// kernel gives each 256-thread block 2048 consecutive tokens: the block finds
+// kernel gives each 256-thread block 2048 consecutive tokens (512 up to 2^20
+// tokens, so that small buffers still spread over the chip): the block finds
 // the segments of its first and last token together by a 128-way parallel
 // search of cu_seqlens, stages that slice (at most 2049 entries, because
 // every segment holds a token) in LDS, and each token searches the LDS copy.  Token reads and all
@@ -26,8 +27,10 @@ constexpr int kScanIPT = 8;
 constexpr int kScanChunk = kScanThreads * kScanIPT;
 
 constexpr int kTokThreads = 256;
-constexpr int kTokPerThread = 8;
-constexpr int kTokBlock = kTokThreads * kTokPerThread;
+// Tokens per thread of the per-token pass: 8 for large buffers (fewer
+// segment searches per token), 2 up to kSmallTokens tokens, where 8 would
+// leave most of the chip idle and each thread's tokens in series.
+constexpr int kSmallTokens = 1 << 20;
 
 // Inclusive block scan (Hillis-Steele over shared memory), one value per thread.
 __device__ long long block_inclusive_scan(long long x, long long* sh) {
@@ -196,12 +199,14 @@ __device__ void block_segments_of(const int32_t* __restrict__ cu, int32_t nseg, 
     __syncthreads();
 }
 
+template <int kTokPerThread>
 __global__ __launch_bounds__(kTokThreads) void pack_tokens_kernel(
         const int32_t* __restrict__ cu, const uint8_t* __restrict__ is_pad,
         const int32_t* __restrict__ tokens, int32_t nseg, int64_t T, int32_t ignore_index,
         int32_t* __restrict__ seg_out, int32_t* __restrict__ pos_out,
         int32_t* __restrict__ lab_out, uint8_t* __restrict__ mask_out,
         int64_t* num_targets, uint32_t* dev_error) {
+    constexpr int kTokBlock = kTokThreads * kTokPerThread;
     __shared__ int32_t s_cu[kTokBlock + 2];
     __shared__ int32_t s_lo, s_n;
     __shared__ unsigned s_cnt, s_err;
@@ -291,6 +296,20 @@ __global__ __launch_bounds__(kValThreads) void validate_kernel(
     if (threadIdx.x == 0) raise_error(dev_error, s_err);
 }
 
+void launch_tokens(hipStream_t s, const int32_t* cu, const uint8_t* is_pad, const int32_t* tokens, int32_t nseg,
+                   int64_t T, int32_t ignore_index, int32_t* seg_out, int32_t* pos_out, int32_t* lab_out,
+                   uint8_t* mask_out, int64_t* num_targets, uint32_t* dev_error) {
+    if (T <= kSmallTokens) {
+        const int64_t nblk = (T + kTokThreads * 2 - 1) / (kTokThreads * 2);
+        hipLaunchKernelGGL(pack_tokens_kernel<2>, dim3((unsigned)nblk), dim3(kTokThreads), 0, s, cu, is_pad, tokens,
+                           nseg, T, ignore_index, seg_out, pos_out, lab_out, mask_out, num_targets, dev_error);
+    } else {
+        const int64_t nblk = (T + kTokThreads * 8 - 1) / (kTokThreads * 8);
+        hipLaunchKernelGGL(pack_tokens_kernel<8>, dim3((unsigned)nblk), dim3(kTokThreads), 0, s, cu, is_pad, tokens,
+                           nseg, T, ignore_index, seg_out, pos_out, lab_out, mask_out, num_targets, dev_error);
+    }
+}
+
 }  // namespace
 }  // namespace pvc
 
@@ -332,12 +351,9 @@ extern "C" pvc_status pvc_pack_build(const int32_t* lengths, const uint8_t* is_p
         hipLaunchKernelGGL(scan_apply_kernel, dim3(nch), dim3(kScanThreads), 0, s, lengths, nseg,
                            part_sum, cu_seqlens);
     }
-    if (segment_ids || position_ids || shifted_labels || loss_mask || num_targets) {
-        const int64_t nblk = (total_tokens + kTokBlock - 1) / kTokBlock;
-        hipLaunchKernelGGL(pack_tokens_kernel, dim3((unsigned)nblk), dim3(kTokThreads), 0, s,
-                           cu_seqlens, is_pad, tokens, nseg, total_tokens, ignore_index, segment_ids,
-                           position_ids, shifted_labels, loss_mask, num_targets, dev_error);
-    }
+    if (segment_ids || position_ids || shifted_labels || loss_mask || num_targets)
+        launch_tokens(s, cu_seqlens, is_pad, tokens, nseg, total_tokens, ignore_index, segment_ids, position_ids,
+                      shifted_labels, loss_mask, num_targets, dev_error);
     return launch_status();
 }
 
@@ -351,12 +367,9 @@ extern "C" pvc_status pvc_pack_tokens(const int32_t* cu_seqlens, const uint8_t* 
     if (nseg < 1 || total_tokens < 1 || total_tokens > 0x7fffffffLL) return PVC_ERR_INVALID_ARG;
     hipStream_t s = as_stream(stream);
     if (num_targets != nullptr) hipLaunchKernelGGL(zero_count_kernel, dim3(1), dim3(64), 0, s, num_targets);
-    if (segment_ids || position_ids || shifted_labels || loss_mask || num_targets) {
-        const int64_t nblk = (total_tokens + kTokBlock - 1) / kTokBlock;
-        hipLaunchKernelGGL(pack_tokens_kernel, dim3((unsigned)nblk), dim3(kTokThreads), 0, s, cu_seqlens, is_pad,
-                           tokens, nseg, total_tokens, ignore_index, segment_ids, position_ids, shifted_labels,
-                           loss_mask, num_targets, dev_error);
-    }
+    if (segment_ids || position_ids || shifted_labels || loss_mask || num_targets)
+        launch_tokens(s, cu_seqlens, is_pad, tokens, nseg, total_tokens, ignore_index, segment_ids, position_ids,
+                      shifted_labels, loss_mask, num_targets, dev_error);
     return launch_status();
 }
 

@@ -114,6 +114,23 @@ def test_head_counts_divisible_by_the_xcds(pvc, heads, causal):
     assert np.abs(ls.cpu().numpy().T - ref_lse).max() < 5e-3
 
 
+def test_more_segments_than_the_fused_plan_launch(pvc):
+    """Beyond 16,384 segments the plan's check runs as its own launch: the
+    same results on 20,000 short segments (sampled rows against the oracle,
+    every segment boundary included among them)."""
+    lengths = np.random.default_rng(7).integers(1, 9, 20000)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    T, H, d = int(cu[-1]), 2, 64
+    say(f"  many segments: nseg={lengths.size} T={T}")
+    q, k, v = (_rand_bits((T, H, d), s) for s in (51, 52, 53))
+    ob, of, ls = _run(pvc, q, k, v, cu, True)
+    rows = np.unique(np.concatenate([cu[:-1][::37], cu[1:][::41] - 1,
+                                     np.random.default_rng(8).integers(0, T, 300)]))
+    ref, ref_lse = A.attention_rows(q, k, v, cu, rows, True, threads=THREADS)
+    three_part_check(of, ob, ref, rows=rows)
+    assert np.abs(ls.cpu().numpy().T[rows] - ref_lse).max() < 5e-3
+
+
 @pytest.mark.parametrize("lengths", [[1], [1] * 200, [1000], [130, 1, 127, 300, 2, 64, 65],
                                      [33, 31, 32, 64, 96, 129], [4096 + 17]])
 def test_edge_lengths(pvc, lengths):
