@@ -32,18 +32,26 @@ constexpr int kTokThreads = 256;
 // leave most of the chip idle and each thread's tokens in series.
 constexpr int kSmallTokens = 1 << 20;
 
-// Inclusive block scan (Hillis-Steele over shared memory), one value per thread.
+// Inclusive block scan, one value per thread: a shuffle scan inside each
+// wave, then every thread adds the totals of the waves before its own.  On
+// return sh[blockDim.x - 1] holds the block total (callers read it).
 __device__ long long block_inclusive_scan(long long x, long long* sh) {
     const int t = threadIdx.x;
-    sh[t] = x;
-    __syncthreads();
-    for (int off = 1; off < (int)blockDim.x; off <<= 1) {
-        long long y = (t >= off) ? sh[t - off] : 0;
-        __syncthreads();
-        sh[t] += y;
-        __syncthreads();
+    const int lane = t & 63, wave = t >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const long long y = __shfl_up(x, off);
+        if (lane >= off) x += y;
     }
-    return sh[t];
+    if (lane == 63) sh[wave] = x;
+    __syncthreads();
+    long long carry = 0;
+    for (int w = 0; w < wave; ++w) carry += sh[w];
+    x += carry;
+    __syncthreads();                               // every wave has read the totals
+    if (t == (int)blockDim.x - 1) sh[t] = x;
+    __syncthreads();
+    return x;
 }
 
 struct ChunkResult {
