@@ -40,11 +40,14 @@
 // Grid to hardware: workgroups are dealt round-robin to the 8 XCDs, so the
 // block index is remapped to give each XCD a contiguous range of the
 // (head, tile) space; an XCD then works through a few heads, and the query
-// tiles that share a head's K/V run together on one L2.  Within a head the
-// segments go in buffer order and each segment's tiles from its end to its
-// start, so the heaviest tiles of a segment (its last rows see the most keys)
-// are dispatched first.  A global longest-first order was measured slower: it
-// separates the tiles of a segment and loses their K/V reuse in L2.
+// tiles that share a head's K/V run together on one L2.  The segments go in
+// buffer order and each segment's tiles from its end to its start, so the
+// heaviest tiles of a segment (its last rows see the most keys) are
+// dispatched first; when segments span more than two tiles, each segment's
+// run of tiles comes once for every head of the XCD before the next
+// segment's, so no head's long samples start near the end of the launch.  A
+// global longest-first order was measured slower: it separates the tiles of
+// a segment and loses their K/V reuse in L2.
 #include <math.h>
 
 #include <type_traits>
