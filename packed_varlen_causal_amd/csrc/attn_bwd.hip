@@ -8,7 +8,7 @@
 //   dQ = s dS K,  dK = s dS^T Q.
 // P is recomputed from Q, K and the forward's log-sum-exp, so nothing of size
 // T x T is stored.  Three launches, all on the forward's plan (per-row key
-// ranges, 128-row tiles, the same XCD-contiguous mapping):
+// ranges, 128-row tiles, the forward's XCD-contiguous item order):
 //   bwd_prep_kernel   D_i = dO_i . O_i and lse_i * log2(e) per (head, row)
 //                     into a padded scratch buffer (HBM-bound);
 //   bwd_dq_kernel     query-major like the forward: a wave holds Q^T and dO^T
@@ -28,8 +28,8 @@
 //                     (about 370 registers: the two fp32 accumulators alone
 //                     take 128).
 // Every product rounds its probability operand (P or dS) to the input type
-// (bf16 or fp16) and accumulates in fp32.  No atomics: each output element is written once, so
-// results do not depend on scheduling.  Stages that lie wholly outside a
+// (bf16 or fp16) and accumulates in fp32.  No atomics: each output element is
+// written once, so results do not depend on scheduling.  Stages that lie wholly outside a
 // wave's segments or on the wrong side of its diagonal are skipped, as in the
 // forward.  The dQ kernel recomputes S and dP, which the dK/dV kernel also
 // computes: seven products per score instead of five, the price of writing

@@ -1,6 +1,6 @@
 // Packed cross-entropy over the rows of a THD buffer, for gfx950.
 //
-// For logits z [T, V] (bf16 or fp32, row stride ld) and the pre-shifted labels
+// For logits z [T, V] (bf16, fp16 or fp32, row stride ld) and the pre-shifted labels
 // that pack_build writes (label[i] is the token row i predicts; the ignore
 // index on each segment's last row and on pad segments), this computes what
 // [charlestar] "cross-boundary prediction pairs" keeps for the training loop:
@@ -15,16 +15,17 @@
 //     the caller wants).
 //
 // Kernels:
-//   ce_row_kernel      one 256-thread workgroup per row.  Pass 1 streams the
-//                      row in 16-byte vectors, chunk by chunk: the chunk's
-//                      max, one rescale of the running sum, then exp2 of every
-//                      element against the running max (fp32, the scale
-//                      log2(e) folded into one FMA).  The (max, sum) pairs of
-//                      the 256 threads meet through lane shuffles and LDS.
-//                      loss = max + ln(sum) - z_y.  Pass 2 (gradient only)
-//                      re-reads the row, which is still in L2, and writes the
-//                      gradient.  HBM-bound: 2V bytes per bf16 row read once
-//                      (plus 2V written with the gradient).
+//   ce_row_kernel      one 256-thread workgroup per row.  A row of up to 16
+//                      16-byte vectors per thread is loaded once and kept in
+//                      registers: each thread's max, then exp2 of every
+//                      element against it (fp32, the scale log2(e) folded into
+//                      one FMA), and the gradient from the same registers.
+//                      Longer rows stream in chunks with a running (max, sum)
+//                      and are re-read (from L2) for the gradient.  The
+//                      (max, sum) pairs of the 256 threads meet through lane
+//                      shuffles and LDS; loss = max + ln(sum) - z_y.
+//                      HBM-bound: 2V bytes per bf16 row read once (plus 2V
+//                      written with the gradient).
 //   ce_reduce_kernel   4096 rows per workgroup: fp64 sum of the row losses and
 //                      int64 count of valid labels, in a fixed order.
 //   ce_final_kernel    one workgroup adds the partials in a fixed order.
