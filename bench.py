@@ -512,7 +512,11 @@ def main():
     import packed_varlen_causal_amd as pvc
 
     x = Inputs(args.workload, torch, pvc, keep_host=not args.no_cpu_baseline)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    resident = torch.cuda.memory_allocated()
     ms_step, stage_ms = time_steps(torch, pvc, x, args.steps, args.warmup)
+    peak = torch.cuda.max_memory_allocated()
     pack_ms, rope_ms, plan_ms, attn_ms = (float(v) for v in stage_ms)
     value = x.flops / (ms_step * 1e-3) / 1e12
     attn_tflops = x.flops / (attn_ms * 1e-3) / 1e12
@@ -545,6 +549,11 @@ def main():
         },
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "effective_tokens_per_s": round(x.real_tokens / (ms_step * 1e-3), 1),
+        "device_memory": {
+            "resident_inputs_and_buffers_bytes": int(resident),
+            "peak_during_steps_bytes": int(peak),
+            "note": "q, k, v, rotated q and k, output, plan workspace and packing outputs (PyTorch allocator)",
+        },
         "kernels": {
             "pack_build": {"ms": round(pack_ms, 4), "gbps": round(pack_bytes(x.T, x.w.nseg) / (pack_ms * 1e-3) / 1e9, 1)},
             "rope_thd_apply": {"ms": round(rope_ms, 4),
