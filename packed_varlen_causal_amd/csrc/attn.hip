@@ -812,11 +812,11 @@ extern "C" pvc_status pvc_attn_plan_padded(const int32_t* cu_seqlens, const int3
     return launch_status();
 }
 
-extern "C" pvc_status pvc_varlen_attn_fwd_planned(const void* q, const void* k, const void* v, void* out,
-                                                  float* lse, int64_t total_tokens, int32_t heads,
-                                                  int32_t head_dim, int32_t causal, int32_t out_dtype,
-                                                  const void* workspace, size_t workspace_bytes,
-                                                  uint32_t* dev_error, void* stream) {
+namespace {
+
+// Host checks of the self-attention forward (nothing is enqueued before they pass).
+pvc_status fwd_args(const void* q, const void* k, const void* v, void* out, int64_t total_tokens, int32_t heads,
+                    int32_t head_dim, int32_t out_dtype, const void* workspace, size_t workspace_bytes) {
     if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || workspace == nullptr)
         return PVC_ERR_NULL;
     if (total_tokens < 1 || total_tokens > 0x7fffffffLL || heads < 1) return PVC_ERR_INVALID_ARG;
@@ -832,6 +832,20 @@ extern "C" pvc_status pvc_varlen_attn_fwd_planned(const void* q, const void* k, 
         return PVC_ERR_INVALID_ARG;
     if (L.ntiles * (int64_t)heads > 0x7ffffff0LL) return PVC_ERR_INVALID_ARG;
     if ((int64_t)heads * head_dim > kMaxRowElems) return PVC_ERR_INVALID_ARG;
+    return PVC_OK;
+}
+
+}  // namespace
+
+extern "C" pvc_status pvc_varlen_attn_fwd_planned(const void* q, const void* k, const void* v, void* out,
+                                                  float* lse, int64_t total_tokens, int32_t heads,
+                                                  int32_t head_dim, int32_t causal, int32_t out_dtype,
+                                                  const void* workspace, size_t workspace_bytes,
+                                                  uint32_t* dev_error, void* stream) {
+    const pvc_status chk = fwd_args(q, k, v, out, total_tokens, heads, head_dim, out_dtype, workspace,
+                                    workspace_bytes);
+    if (chk != PVC_OK) return chk;
+    const PlanLayout L = plan_layout(total_tokens);
     const char* ws = static_cast<const char*>(workspace);
     AttnParams prm{};
     prm.q = static_cast<const uint16_t*>(q);
@@ -938,11 +952,11 @@ extern "C" pvc_status pvc_varlen_attn_fwd(const void* q, const void* k, const vo
                                           int32_t head_dim, int32_t causal, int32_t out_dtype,
                                           void* workspace, size_t workspace_bytes, uint32_t* dev_error,
                                           void* stream) {
-    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr) return PVC_ERR_NULL;
-    if (head_dim != 64 && head_dim != 128) return PVC_ERR_UNSUPPORTED;
-    if (heads < 1 || !io_valid(out_dtype)) return PVC_ERR_INVALID_ARG;
-    pvc_status st = pvc_attn_plan(cu_seqlens, nseg, total_tokens, max_seqlen, causal, workspace,
-                                  workspace_bytes, dev_error, stream);
+    // the forward's own checks first, so that a refused call enqueues no plan either
+    pvc_status st = fwd_args(q, k, v, out, total_tokens, heads, head_dim, out_dtype, workspace, workspace_bytes);
+    if (st != PVC_OK) return st;
+    st = pvc_attn_plan(cu_seqlens, nseg, total_tokens, max_seqlen, causal, workspace, workspace_bytes, dev_error,
+                       stream);
     if (st != PVC_OK) return st;
     return pvc_varlen_attn_fwd_planned(q, k, v, out, lse, total_tokens, heads, head_dim, causal,
                                        out_dtype, workspace, workspace_bytes, dev_error, stream);

@@ -173,6 +173,14 @@ def test_null_and_range_checks_return_before_gpu_work(lib):
     assert lib.pvc_varlen_attn_fwd_planned(a, b, c, a, None, 9, 2, 64, 1, 0, fake, 1 << 20, None, None) == 2
     # workspace too small for 9 tokens
     assert lib.pvc_varlen_attn_fwd_planned(a, b, c, o, None, 9, 2, 64, 1, 0, fake, 8, None, None) == 4
+    # plan + forward: the forward's checks come before the plan is enqueued (a
+    # launch here, with no GPU, would report PVC_ERR_HIP instead)
+    lib.pvc_varlen_attn_fwd.restype = I32
+    lib.pvc_varlen_attn_fwd.argtypes = [P, P, P, P, P, P, I32, I64, I32, I32, I32, I32, I32, P, SZ, P, P]
+    assert lib.pvc_varlen_attn_fwd(_vp(0x100002), b, c, o, None, fake, 2, 9, 8, 2, 64, 1, 0, fake, 1 << 20,
+                                   None, None) == 2
+    assert lib.pvc_varlen_attn_fwd(a, b, c, a, None, fake, 2, 9, 8, 2, 64, 1, 0, fake, 1 << 20, None, None) == 2
+    assert lib.pvc_varlen_attn_fwd(a, b, c, o, None, fake, 2, 9, 8, 2, 64, 1, 0, fake, 8, None, None) == 4
 
     lib.pvc_padded_attn_fwd_sbhd.restype = I32
     lib.pvc_padded_attn_fwd_sbhd.argtypes = [P, P, P, P, P, I32, I32, I32, I32, I32, I32, P]
