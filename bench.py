@@ -516,7 +516,7 @@ def main():
     torch.cuda.reset_peak_memory_stats()
     resident = torch.cuda.memory_allocated()
     ms_step, stage_ms = time_steps(torch, pvc, x, args.steps, args.warmup)
-    peak = torch.cuda.max_memory_allocated()
+    mem_peak = torch.cuda.max_memory_allocated()
     pack_ms, rope_ms, plan_ms, attn_ms = (float(v) for v in stage_ms)
     value = x.flops / (ms_step * 1e-3) / 1e12
     attn_tflops = x.flops / (attn_ms * 1e-3) / 1e12
@@ -551,7 +551,7 @@ def main():
         "effective_tokens_per_s": round(x.real_tokens / (ms_step * 1e-3), 1),
         "device_memory": {
             "resident_inputs_and_buffers_bytes": int(resident),
-            "peak_during_steps_bytes": int(peak),
+            "peak_during_steps_bytes": int(mem_peak),
             "note": "q, k, v, rotated q and k, output, plan workspace and packing outputs (PyTorch allocator)",
         },
         "kernels": {
