@@ -165,7 +165,7 @@ def time_attn_only(torch, pvc, x, steps, warmup):
 
 
 def time_backward(torch, pvc, x, steps, warmup):
-    """varlen_attn_bwd (prep + dQ + dK/dV launches) on the step's rotated q, k,
+    """varlen_attn_bwd (dQ + dK/dV launches) on the step's rotated q, k,
     the forward's output and log-sum-exp, and a seeded N(0, 1) upstream
     gradient; bf16 gradients.  Returns ms per backward call."""
     meta = pvc.pack_build(x.lengths, x.tokens, x.is_pad, dev_error=x.err)

@@ -7,13 +7,13 @@
 //   dV = P^T dO,  dP = dO V^T,  D_i = dO_i . O_i,  dS = P o (dP - D),
 //   dQ = s dS K,  dK = s dS^T Q.
 // P is recomputed from Q, K and the forward's log-sum-exp, so nothing of size
-// T x T is stored.  Three launches, all on the forward's plan (per-row key
+// T x T is stored.  Two launches, both on the forward's plan (per-row key
 // ranges, 128-row tiles, the forward's XCD-contiguous item order):
-//   bwd_prep_kernel   D_i = dO_i . O_i and lse_i * log2(e) per (head, row)
-//                     into a padded scratch buffer (HBM-bound);
 //   bwd_dq_kernel     query-major like the forward: a wave holds Q^T and dO^T
-//                     of its 32 rows in registers and streams 32-key stages of
-//                     K and V through LDS; per stage S^T = K Q^T and
+//                     of its 32 rows in registers, forms D_i = dO_i . O_i and
+//                     lse_i * log2(e) for them and stores both in a padded
+//                     scratch buffer for the second launch, and streams
+//                     32-key stages of K and V through LDS; per stage S^T = K Q^T and
 //                     dP^T = V dO^T (MFMA, K and V as A operands),
 //                     dS^T = P^T o (dP^T - D) in registers, and
 //                     dQ^T += K^T dS^T with K^T from the transposing LDS read;
@@ -90,49 +90,6 @@ __device__ __attribute__((always_inline)) inline void wait_stages(int ahead) {
         constexpr int v = decltype(n)::value * LPS;
         if (ahead == decltype(n)::value) __builtin_amdgcn_s_waitcnt(0x0F70 | (v & 15) | ((v >> 4) << 14));
     });
-}
-
-// ------------------------------------------------------------------- prep
-
-template <int D, bool F16>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ out,
-                                                       const uint16_t* __restrict__ dout,
-                                                       const float* __restrict__ lse, float* __restrict__ scratch,
-                                                       int64_t T, int64_t Tp, int32_t H) {
-    constexpr int LPR = D / 8;                     // lanes per (row, head): 16 bytes each
-    constexpr int RPB = 256 / LPR;
-    const int64_t item = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;   // (t, h), h fastest
-    const int part = threadIdx.x % LPR;
-    const int64_t t = item / H;
-    const int h = (int)(item - t * H);
-    float acc = 0.0f;
-    if (t < T) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(out + item * D + part * 8);
-        const u32x4 b = *reinterpret_cast<const u32x4*>(dout + item * D + part * 8);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            if constexpr (F16) {
-                // the elements go through named scalars: a bit cast of a vector
-                // element expression read element 0 whatever the index
-                const uint32_t aw = a[w], bw = b[w];
-                const f16x2 x = __builtin_bit_cast(f16x2, aw), y = __builtin_bit_cast(f16x2, bw);
-                acc = fmaf((float)x[0], (float)y[0], acc);
-                acc = fmaf((float)x[1], (float)y[1], acc);
-            } else {
-                acc = fmaf(__uint_as_float(a[w] << 16), __uint_as_float(b[w] << 16), acc);
-                acc = fmaf(__uint_as_float(a[w] & 0xFFFF0000u), __uint_as_float(b[w] & 0xFFFF0000u), acc);
-            }
-        }
-    }
-#pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (part == 0 && t < Tp) {
-        // a padding row (no key: LSE -inf) gets +inf, so its recomputed
-        // probabilities exp2(s - lse) are 0 rather than NaN
-        const float l = t < T ? lse[(int64_t)h * T + t] : 0.0f;
-        scratch[(int64_t)h * Tp + t] = l == -INFINITY ? INFINITY : l * kLog2e;
-        scratch[((int64_t)H + h) * Tp + t] = t < T ? acc : 0.0f;
-    }
 }
 
 // ------------------------------------------------------------- shared pieces
@@ -253,8 +210,37 @@ void bwd_dq_kernel(BwdParams p) {
             doreg[s] = *reinterpret_cast<const x8*>(gp + 16 * s);
         }
     }
-    const float lse2 = p.scratch[(int64_t)head * p.Tp + row];
-    const float dlt = p.scratch[((int64_t)H + head) * p.Tp + row];
+    // lse in log2 units and D = dO . O of the lane's row (the lane pair holds
+    // the two halves of the row), stored once per row for the dK/dV launch.
+    // A padding row (no key: LSE -inf) gets +inf, so its recomputed
+    // probabilities exp2(s - lse) are 0 rather than NaN.  The scratch rows
+    // past T, which dK/dV stages also read, are zeroed by the workgroups of
+    // the last tile.
+    float lse2, dlt;
+    {
+        const float l = p.lse[(int64_t)head * p.T + row];
+        lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+        const uint16_t* op = p.out + row_off(row) + 8 * g;
+        float part = 0.0f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const x8 o = *reinterpret_cast<const x8*>(op + 16 * s);
+            const x8 d = doreg[s];
+            part = E::dot2(__builtin_shufflevector(o, o, 0, 1), __builtin_shufflevector(d, d, 0, 1), part);
+            part = E::dot2(__builtin_shufflevector(o, o, 2, 3), __builtin_shufflevector(d, d, 2, 3), part);
+            part = E::dot2(__builtin_shufflevector(o, o, 4, 5), __builtin_shufflevector(d, d, 4, 5), part);
+            part = E::dot2(__builtin_shufflevector(o, o, 6, 7), __builtin_shufflevector(d, d, 6, 7), part);
+        }
+        dlt = lane_pair_sum(part);
+        if (g == 0 && wave_active && wr0 + c < r1) {
+            p.scratch[(int64_t)head * p.Tp + row] = lse2;
+            p.scratch[((int64_t)H + head) * p.Tp + row] = dlt;
+        }
+        if (tile == p.ntiles - 1 && tid < p.Tp - p.T) {
+            p.scratch[(int64_t)head * p.Tp + p.T + tid] = 0.0f;
+            p.scratch[((int64_t)H + head) * p.Tp + p.T + tid] = 0.0f;
+        }
+    }
     bool sealed;
     const bool plan_ok = plan_sealed(p, CAUSAL, sealed);
     if (!sealed && tid == 0) raise_error(p.dev_error, PVC_DEV_PLAN);
@@ -757,15 +743,10 @@ void bwd_dkdv_kernel(BwdParams p) {
 // ------------------------------------------------------------------- host
 
 
+// dQ first: it writes the lse / D planes that dK/dV reads.
 template <int D, bool F16>
 pvc_status launch_bwd(const BwdParams& prm, bool causal, bool out_f32, hipStream_t s) {
-    {
-        constexpr int RPB = 256 / (D / 8);
-        const int64_t items = prm.Tp * prm.H;
-        const int64_t nblk = (items + RPB - 1) / RPB;
-        hipLaunchKernelGGL((bwd_prep_kernel<D, F16>), dim3((unsigned)nblk), dim3(256), 0, s, prm.out, prm.dout,
-                           prm.lse, prm.scratch, prm.T, prm.Tp, prm.H);
-    }
+    static_assert(kThreads >= kBN - 1 + kScratchPad, "the last tile's workgroup zeroes every scratch row past T");
     const int64_t grid = ((int64_t)prm.items + kNumXcd - 1) / kNumXcd * kNumXcd;
     if (grid > 0x7fffffffLL) return PVC_ERR_INVALID_ARG;
     dim3 g((unsigned)grid), blk(kThreads);

@@ -103,6 +103,9 @@ struct Elt<false> {
     __device__ static float sum2(const x2& a, float c) {
         return __builtin_amdgcn_fdot2_f32_bf16(a, x2{(__bf16)1.0f, (__bf16)1.0f}, c, false);
     }
+    __device__ static float dot2(const x2& a, const x2& b, float c) {
+        return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+    }
 };
 template <>
 struct Elt<true> {
@@ -115,6 +118,7 @@ struct Elt<true> {
     __device__ static float sum2(const x2& a, float c) {
         return __builtin_amdgcn_fdot2(a, x2{(_Float16)1.0f, (_Float16)1.0f}, c, false);
     }
+    __device__ static float dot2(const x2& a, const x2& b, float c) { return __builtin_amdgcn_fdot2(a, b, c, false); }
 };
 
 // Max over the lane pair (l, l^32): v_permlane32_swap hands each lane its
