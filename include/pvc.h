@@ -374,7 +374,8 @@ pvc_status pvc_varlen_attn_fwd(const void* q, const void* k, const void* v, void
  * head_dim    64 or 128; 2 * heads * (total_tokens + 159) * 4 bytes must stay
  *             below 4 GiB (PVC_ERR_INVALID_ARG otherwise)
  * total_tokens and causal must be those the plan was built with; otherwise
- * PVC_DEV_PLAN is set and nothing is written.  All pointers 16-byte aligned.
+ * PVC_DEV_PLAN is set and no gradient is written (the scratch still is).  All
+ * pointers 16-byte aligned.
  * Arithmetic: MFMA products in the input type with fp32 accumulation; P and
  * dS are rounded to the input type (nearest even) for their products.
  * Deterministic: no atomics.
