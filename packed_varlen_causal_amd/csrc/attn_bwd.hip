@@ -17,9 +17,12 @@
 //                     dP^T = V dO^T (MFMA, K and V as A operands),
 //                     dS^T = P^T o (dP^T - D) in registers, and
 //                     dQ^T += K^T dS^T with K^T from the transposing LDS read;
-//   bwd_dkdv_kernel   key-major: a wave holds K^T and V^T of its 32 keys and
-//                     streams 64-query stages (two 32-query halves) of Q, dO,
-//                     lse and D through a ring of three buffers; per half
+//   bwd_dkdv_kernel   key-major, one workgroup per CU taking its XCD's items
+//                     from a counter (the next item's loads go out before the
+//                     current item's stores): a wave holds K^T and V^T of its
+//                     32 keys and streams 64-query stages (two 32-query
+//                     halves) of Q, dO, lse and D through a ring of three
+//                     buffers; per half
 //                     S = Q K^T and dP = dO V^T (lane = key), P and dS in
 //                     registers, dV^T += dO^T P and dK^T += Q^T dS with Q^T and
 //                     dO^T from the transposing LDS read.  Both halves' S and
@@ -36,6 +39,8 @@
 // every gradient once without atomics.
 #include "attn_common.h"
 
+#include <algorithm>
+
 namespace pvc {
 namespace {
 
@@ -49,6 +54,7 @@ struct BwdParams {
     const uint16_t* dout;
     const float* lse;          // [H, T], natural log (the forward's)
     float* scratch;            // [2][H][Tp]: lse * log2(e), then D
+    int32_t* queue;            // dK/dV item counters, one per XCD (kQueueStride ints apart), after the planes
     void* dq;
     void* dk;
     void* dv;
@@ -71,6 +77,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 // up to 128 rows a stage reads lies inside the plane.
 constexpr int kScratchPad = 4 * kBN;
 inline int64_t scratch_rows(int64_t T) { return (T + kBN - 1) / kBN * kBN + kScratchPad; }
+// The dK/dV work queue: one counter per XCD, 64 bytes apart, after the planes.
+constexpr int kQueueStride = 16;
+constexpr size_t kQueueBytes = (size_t)kNumXcd * kQueueStride * sizeof(int32_t);
+inline size_t planes_bytes(int64_t T, int32_t H) { return align_up((size_t)2 * H * scratch_rows(T) * sizeof(float)); }
 
 // Stage geometry.  Measured alternatives: two key halves per dQ stage and
 // 2- vs 3-deep dQ rings within 2%; one query half per dK/dV stage 6% slower
@@ -168,6 +178,8 @@ void bwd_dq_kernel(BwdParams p) {
 
     const int logical = xcd_logical();
     if (logical >= p.items) return;
+    // the dK/dV launch that follows takes its items from these counters
+    if (blockIdx.x == 0 && threadIdx.x < kNumXcd * kQueueStride) p.queue[threadIdx.x] = 0;
     // (head, tile) in the forward's order: a segment's heaviest (last) query
     // tile starts first
     int head, tile;
@@ -462,68 +474,86 @@ void bwd_dkdv_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(1024))) uint16_t sQO[2 * kDkdvRing * SROWS * D];
     __shared__ __attribute__((aligned(16))) float sLD[kDkdvRing][NH][2][kBN];
 
-    const int logical = xcd_logical();
-    if (logical >= p.items) return;
-    // key tiles in buffer order inside each run: a segment's first key tiles
-    // are seen by all its later queries, so they are its heaviest and start first
-    int head, tile;
-    item_of<false>(p, logical, head, tile);
-    const int r0 = tile * kBM;
-    const int r1 = (int)min<int64_t>((int64_t)r0 + kBM, p.T);
-    const int last_row = (int)(p.T - 1);
-    const int H = p.H;
-
+    // ---- work queue.  One workgroup per CU takes the (head, key tile) items
+    // of its XCD in order from a counter at the end of the scratch buffer
+    // (zeroed by the dQ launch).  After an item's last stage the next item's
+    // decode, K / V registers and first stages are issued before the
+    // current item's epilogue, so those loads overlap its stores and no CU
+    // waits for a new workgroup.  Key tiles go in buffer order inside each
+    // run: a segment's first key tiles are seen by all its later queries,
+    // so they are its heaviest and start first.
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int c = lane & 31;
     const int g = lane >> 5;
-    const int kw0 = r0 + 32 * wave;                  // this wave's keys [kw0, kw1)
-    const int kw1 = min(kw0 + 32, r1);
-    const bool wave_active = kw0 < r1;
-    const int key = min(kw0 + c, r1 - 1);
+    const int last_row = (int)(p.T - 1);
+    const int H = p.H;
+    bool sealed;
+    const bool plan_ok = plan_sealed(p, CAUSAL, sealed);
+    if (!sealed && tid == 0) raise_error(p.dev_error, PVC_DEV_PLAN);
+    if (!plan_ok) return;                                 // uniform: nothing is computed
+    const int xcd = blockIdx.x % kNumXcd;
+    const int per_xcd = (p.items + kNumXcd - 1) / kNumXcd;
+    int* const ctr = p.queue + kQueueStride * xcd;
+    __shared__ int s_tk[2];
+    // ticket j of this XCD's queue -> item, or -1 when the queue is drained
+    auto item_at = [&](int j) -> int {
+        return (unsigned)j < (unsigned)per_xcd && xcd * per_xcd + j < p.items ? xcd * per_xcd + j : -1;
+    };
 
-    // queries that may see key j: [lo_j, hi_j) = [causal ? j : start_j, end_j)
-    const int2 mine = p.rows[key];
-    const int lo_j = CAUSAL ? key : mine.x;
-    const int hi_j = mine.y;
-    const int2 first = p.rows[min(kw0, r1 - 1)];
-    const int2 last = p.rows[max(kw1 - 1, 0)];
-    const int w_qlo = CAUSAL ? kw0 : first.x;        // smallest lo_j of the wave
-    const int w_qhi = last.y;                         // largest hi_j
-    const int full_lo = CAUSAL ? kw1 - 1 : last.x;   // largest lo_j
-    const int full_hi = first.y;                      // smallest hi_j
-    // non-causal stages start on a multiple of 4 rows, so each 16-byte piece
-    // of the lse / D planes a stage loads is aligned
-    const int q_lo = CAUSAL ? r0 : (p.rows[r0].x & ~3);
-    const int q_hi = p.rows[r1 - 1].y;
-
-    auto row_off = [&](int r) -> int64_t { return ((int64_t)r * H + head) * D; };
+    struct Item {
+        int head, r0, r1, kw0, kw1, key, lo_j, hi_j, w_qlo, w_qhi, full_lo, full_hi, q_lo, nstages;
+        bool wave_active;
+    };
+    auto decode = [&](int logical) -> Item {
+        Item it;
+        int tile;
+        item_of<false>(p, logical, it.head, tile);
+        it.r0 = tile * kBM;
+        it.r1 = (int)min<int64_t>((int64_t)it.r0 + kBM, p.T);
+        it.kw0 = it.r0 + 32 * wave;                       // this wave's keys [kw0, kw1)
+        it.kw1 = min(it.kw0 + 32, it.r1);
+        it.wave_active = it.kw0 < it.r1;
+        it.key = min(it.kw0 + c, it.r1 - 1);
+        // queries that may see key j: [lo_j, hi_j) = [causal ? j : start_j, end_j)
+        const int2 mine = p.rows[it.key];
+        it.lo_j = CAUSAL ? it.key : mine.x;
+        it.hi_j = mine.y;
+        const int2 first = p.rows[min(it.kw0, it.r1 - 1)];
+        const int2 last = p.rows[max(it.kw1 - 1, 0)];
+        it.w_qlo = CAUSAL ? it.kw0 : first.x;             // smallest lo_j of the wave
+        it.w_qhi = last.y;                                 // largest hi_j
+        it.full_lo = CAUSAL ? it.kw1 - 1 : last.x;        // largest lo_j
+        it.full_hi = first.y;                              // smallest hi_j
+        // non-causal stages start on a multiple of 4 rows, so each 16-byte
+        // piece of the lse / D planes a stage loads is aligned
+        it.q_lo = CAUSAL ? it.r0 : (p.rows[it.r0].x & ~3);
+        const int q_hi = p.rows[it.r1 - 1].y;
+        it.nstages = (q_hi - it.q_lo + SROWS - 1) / SROWS;
+        return it;
+    };
+    auto row_off = [&](int r, int head) -> int64_t { return ((int64_t)r * H + head) * D; };
     // K^T and V^T B operands: lane (c, g) holds X[key][16s + 8g .. +8]
     x8 kreg[NS], vreg[NS];
-    {
-        const uint16_t* kp = p.k + row_off(key) + 8 * g;
-        const uint16_t* vp = p.v + row_off(key) + 8 * g;
+    auto load_kv = [&](const Item& it) {
+        const uint16_t* kp = p.k + row_off(it.key, it.head) + 8 * g;
+        const uint16_t* vp = p.v + row_off(it.key, it.head) + 8 * g;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             kreg[s] = *reinterpret_cast<const x8*>(kp + 16 * s);
             vreg[s] = *reinterpret_cast<const x8*>(vp + 16 * s);
         }
-    }
-    bool sealed;
-    const bool plan_ok = plan_sealed(p, CAUSAL, sealed);
-    if (!sealed && tid == 0) raise_error(p.dev_error, PVC_DEV_PLAN);
-    const int nstages = plan_ok ? (q_hi - q_lo + SROWS - 1) / SROWS : 0;
+    };
 
     // ---- Q and dO stages (swizzled by t_swz), lse and D blocks (128 bytes each)
     const int64_t row_stride = (int64_t)H * D;
-    const int64_t head_off = (int64_t)head * D;
     const int fetch_rr = wave * ROWS_PER_CHUNK + lane / L16;
     const uint32_t loff =
             (uint32_t)((fetch_rr * row_stride + ((lane % L16) ^ t_swz<D>(fetch_rr)) * 8) * 2);
     char* const qbase = reinterpret_cast<char*>(&sQO[0]);
     char* const obase = qbase + kDkdvRing * NH * TILE_B;
-    auto fetch_rows = [&](const uint16_t* src, lds_char* dst, int kt) {
+    auto fetch_rows = [&](const uint16_t* src, lds_char* dst, int kt, int64_t head_off) {
         const char* base = reinterpret_cast<const char*>(src) + ((int64_t)kt * row_stride + head_off) * 2;
         const int64_t chunk_step = (int64_t)CHUNK_ROWS * row_stride * 2;
         if (kt + kBN - 1 <= last_row) {
@@ -552,14 +582,15 @@ void bwd_dkdv_kernel(BwdParams p) {
     const char* const sbase = reinterpret_cast<const char*>(p.scratch);
     constexpr int PPW = 4 * NH;                      // pieces per wave
     const int piece = PPW * wave + (lane & (PPW - 1));
-    const int64_t piece_row =
-            ((piece >> 3) & 1 ? (int64_t)H + head : (int64_t)head) * p.Tp + (piece >> 4) * kBN + 4 * (piece & 7);
-    auto fetch_stage = [&](int st, int slot) {
-        const int qt = q_lo + st * SROWS;
+    auto fetch_stage = [&](const Item& it, int st, int slot) {
+        const int64_t head_off = (int64_t)it.head * D;
+        const int64_t piece_row = ((piece >> 3) & 1 ? (int64_t)H + it.head : (int64_t)it.head) * p.Tp +
+                                  (piece >> 4) * kBN + 4 * (piece & 7);
+        const int qt = it.q_lo + st * SROWS;
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
-            fetch_rows(p.q, q_lds + (slot * NH + h) * TILE_B, qt + h * kBN);
-            fetch_rows(p.dout, o_lds + (slot * NH + h) * TILE_B, qt + h * kBN);
+            fetch_rows(p.q, q_lds + (slot * NH + h) * TILE_B, qt + h * kBN, head_off);
+            fetch_rows(p.dout, o_lds + (slot * NH + h) * TILE_B, qt + h * kBN, head_off);
         }
         // the LDS destination is wave-uniform; readfirstlane keeps it scalar
         const int ld_dst = __builtin_amdgcn_readfirstlane((slot * NH * 2 * kBN + PPW * 4 * wave) * 4);
@@ -590,18 +621,13 @@ void bwd_dkdv_kernel(BwdParams p) {
     };
 
     f32x16 accV[ND], accK[ND];
-#pragma unroll
-    for (int j = 0; j < ND; ++j) {
-        accV[j] = f32x16(0.0f);
-        accK[j] = f32x16(0.0f);
-    }
     const float sl2 = p.scale_log2;
 
-    auto stage_active = [&](int st) -> bool {
-        const int qt = q_lo + st * SROWS;
-        return wave_active && qt + SROWS > w_qlo && qt < w_qhi;
+    auto stage_active = [&](const Item& it, int st) -> bool {
+        const int qt = it.q_lo + st * SROWS;
+        return it.wave_active && qt + SROWS > it.w_qlo && qt < it.w_qhi;
     };
-    auto half_full = [&](int qt) -> bool { return qt >= full_lo && qt + kBN <= full_hi; };
+    auto half_full = [&](const Item& it, int qt) -> bool { return qt >= it.full_lo && qt + kBN <= it.full_hi; };
     auto pack = [&](const x2 (&pk)[8], x8 (&outp)[2]) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
@@ -610,8 +636,8 @@ void bwd_dkdv_kernel(BwdParams p) {
     };
     // one stage: S = Q K^T and dP = dO V^T for every half first, so the
     // MFMA chains of one half overlap the exp / pack work of the other
-    auto stage = [&](int st, int slot) __attribute__((always_inline)) {
-        const int qt = q_lo + st * SROWS;
+    auto stage = [&](const Item& it, int st, int slot) __attribute__((always_inline)) {
+        const int qt = it.q_lo + st * SROWS;
         f32x16 S[NH], dP[NH];
         static_for<NH>([&](auto H_) {
             constexpr int h = decltype(H_)::value;
@@ -629,9 +655,9 @@ void bwd_dkdv_kernel(BwdParams p) {
             constexpr int h = decltype(H_)::value;
             // lane = key c; register r = query qt + 32h + 8(r/4) + 4g + r%4
             const int qh = qt + h * kBN;
-            if (!half_full(qh)) {
+            if (!half_full(it, qh)) {
                 const int x0 = qh + 4 * g;
-                const int lo = lo_j - x0, hi = hi_j - x0;
+                const int lo = it.lo_j - x0, hi = it.hi_j - x0;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int C = 8 * (r >> 2) + (r & 3);
@@ -671,72 +697,109 @@ void bwd_dkdv_kernel(BwdParams p) {
     };
 
     constexpr int RING = kDkdvRing;
-    static_for<RING - 1>([&](auto i) {
-        if (decltype(i)::value < nstages) fetch_stage(decltype(i)::value, decltype(i)::value);
-    });
-    for (int st0 = 0; st0 < nstages; st0 += RING) {
-        static_for<RING>([&](auto I) {
-            constexpr int SLOT = decltype(I)::value;
-            const int st = st0 + SLOT;
-            if (st >= nstages) return;
-            wait_stages<RING, 2 * NH * CPW + 1>(min(RING - 2, nstages - 1 - st));   // stage st has landed
-            __syncthreads();
-            if (st + RING - 1 < nstages) fetch_stage(st + RING - 1, (SLOT + RING - 1) % RING);
-            if (stage_active(st)) stage(st, SLOT);
-        });
-    }
-
-    // ---- epilogue: lane (c, g) holds rows d = 32j + 8(r/4) + 4g + r%4 of
-    // dV^T and dK^T for key kw0 + c
-    if (!plan_ok) return;
+    static_assert(NH == 2, "the epilogue stages two waves' rows in each Q or dO buffer of the last ring slot");
+    static_assert(kBM * ROW_B <= 2 * NH * TILE_B, "output tile fits one ring slot of Q and dO");
     const float sc = p.scale;
-    const bool key_ok = wave_active && kw0 + c < kw1;
-    if constexpr (OUT_F32) {
-        if (key_ok) {
-            float* ov = static_cast<float*>(p.dv) + row_off(key);
-            float* ok = static_cast<float*>(p.dk) + row_off(key);
+    // one item's dV and dK: lane (c, g) holds rows d = 32j + 8(r/4) + 4g + r%4
+    // of dV^T and dK^T for key kw0 + c.  The bf16 tile goes through the last
+    // ring slot (the next item's first stages fill the others).
+    auto epilogue = [&](const Item& it) {
+        if constexpr (OUT_F32) {
+            if (it.wave_active && it.kw0 + c < it.kw1) {
+                float* ov = static_cast<float*>(p.dv) + row_off(it.key, it.head);
+                float* ok = static_cast<float*>(p.dk) + row_off(it.key, it.head);
 #pragma unroll
-            for (int j = 0; j < ND; ++j)
+                for (int j = 0; j < ND; ++j)
 #pragma unroll
-                for (int rq = 0; rq < 4; ++rq) {
-                    const int d0 = 32 * j + 8 * rq + 4 * g;
-                    *reinterpret_cast<f32x4*>(ov + d0) =
-                            f32x4{accV[j][4 * rq], accV[j][4 * rq + 1], accV[j][4 * rq + 2], accV[j][4 * rq + 3]};
-                    *reinterpret_cast<f32x4*>(ok + d0) =
-                            f32x4{accK[j][4 * rq] * sc, accK[j][4 * rq + 1] * sc, accK[j][4 * rq + 2] * sc,
-                                  accK[j][4 * rq + 3] * sc};
-                }
-        }
-    } else {
-        constexpr int CPR = ROW_B / 16;
-        static_assert(kBM * ROW_B <= 2 * kDkdvRing * NH * TILE_B, "output tile fits the stage buffers");
-        char* const ob = qbase + wave * 32 * ROW_B;
-        auto emit = [&](const f32x16 (&acc)[ND], float mul, uint16_t* dst) {
-            __syncthreads();                           // stage buffers (or the last tile) are free
-#pragma unroll
-            for (int j = 0; j < ND; ++j)
-#pragma unroll
-                for (int rq = 0; rq < 4; ++rq) {
-                    const x2 a = E::pair(acc[j][4 * rq] * mul, acc[j][4 * rq + 1] * mul);
-                    const x2 b = E::pair(acc[j][4 * rq + 2] * mul, acc[j][4 * rq + 3] * mul);
-                    const int chunk = (4 * j + rq) ^ (c & (CPR - 1));
-                    *reinterpret_cast<u32x2*>(ob + c * ROW_B + chunk * 16 + g * 8) =
-                            u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
-                }
-            if (wave_active) {
-                constexpr int RPI = 64 / CPR;
-#pragma unroll
-                for (int i = 0; i < 32 / RPI; ++i) {
-                    const int r = i * RPI + lane / CPR;
-                    const int kk = lane % CPR;
-                    const u32x4 val =
-                            *reinterpret_cast<const u32x4*>(ob + r * ROW_B + ((kk ^ (r & (CPR - 1))) << 4));
-                    if (kw0 + r < kw1) *reinterpret_cast<u32x4*>(dst + row_off(kw0 + r) + kk * 8) = val;
-                }
+                    for (int rq = 0; rq < 4; ++rq) {
+                        const int d0 = 32 * j + 8 * rq + 4 * g;
+                        *reinterpret_cast<f32x4*>(ov + d0) =
+                                f32x4{accV[j][4 * rq], accV[j][4 * rq + 1], accV[j][4 * rq + 2], accV[j][4 * rq + 3]};
+                        *reinterpret_cast<f32x4*>(ok + d0) =
+                                f32x4{accK[j][4 * rq] * sc, accK[j][4 * rq + 1] * sc, accK[j][4 * rq + 2] * sc,
+                                      accK[j][4 * rq + 3] * sc};
+                    }
             }
-        };
-        emit(accV, 1.0f, static_cast<uint16_t*>(p.dv));
-        emit(accK, sc, static_cast<uint16_t*>(p.dk));
+        } else {
+            constexpr int CPR = ROW_B / 16;
+            char* const ob = (wave < 2 ? qbase : obase) + (RING - 1) * NH * TILE_B + (wave & 1) * TILE_B;
+            auto emit = [&](const f32x16 (&acc)[ND], float mul, uint16_t* dst) {
+                __syncthreads();                           // the staging rows are free
+#pragma unroll
+                for (int j = 0; j < ND; ++j)
+#pragma unroll
+                    for (int rq = 0; rq < 4; ++rq) {
+                        const x2 a = E::pair(acc[j][4 * rq] * mul, acc[j][4 * rq + 1] * mul);
+                        const x2 b = E::pair(acc[j][4 * rq + 2] * mul, acc[j][4 * rq + 3] * mul);
+                        const int chunk = (4 * j + rq) ^ (c & (CPR - 1));
+                        *reinterpret_cast<u32x2*>(ob + c * ROW_B + chunk * 16 + g * 8) =
+                                u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+                    }
+                if (it.wave_active) {
+                    constexpr int RPI = 64 / CPR;
+#pragma unroll
+                    for (int i = 0; i < 32 / RPI; ++i) {
+                        const int r = i * RPI + lane / CPR;
+                        const int kk = lane % CPR;
+                        const u32x4 val =
+                                *reinterpret_cast<const u32x4*>(ob + r * ROW_B + ((kk ^ (r & (CPR - 1))) << 4));
+                        if (it.kw0 + r < it.kw1) *reinterpret_cast<u32x4*>(dst + row_off(it.kw0 + r, it.head) + kk * 8) = val;
+                    }
+                }
+            };
+            emit(accV, 1.0f, static_cast<uint16_t*>(p.dv));
+            emit(accK, sc, static_cast<uint16_t*>(p.dk));
+        }
+    };
+    auto prefetch = [&](const Item& it) {
+        static_for<RING - 1>([&](auto i) {
+            if (decltype(i)::value < it.nstages) fetch_stage(it, decltype(i)::value, decltype(i)::value);
+        });
+    };
+
+    if (tid == 0) s_tk[0] = atomicAdd(ctr, 1);
+    __syncthreads();
+    const int first = item_at(s_tk[0]);
+    if (first < 0) return;                                // uniform: the queue is drained
+    int nxt = 0;
+    if (tid == 0) nxt = atomicAdd(ctr, 1);               // ticket of the item after this one
+    Item cur = decode(first);
+    load_kv(cur);
+    prefetch(cur);
+    for (int n = 0;; ++n) {
+#pragma unroll
+        for (int j = 0; j < ND; ++j) {
+            accV[j] = f32x16(0.0f);
+            accK[j] = f32x16(0.0f);
+        }
+        for (int st0 = 0; st0 < cur.nstages; st0 += RING) {
+            static_for<RING>([&](auto I) {
+                constexpr int SLOT = decltype(I)::value;
+                const int st = st0 + SLOT;
+                if (st >= cur.nstages) return;
+                // stage st has landed.  An item's first wait is for every
+                // outstanding load and store: the previous item's stores were
+                // issued after this item's first stages.
+                if (st == 0) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+                else wait_stages<RING, 2 * NH * CPW + 1>(min(RING - 2, cur.nstages - 1 - st));
+                __syncthreads();
+                if (st + RING - 1 < cur.nstages) fetch_stage(cur, st + RING - 1, (SLOT + RING - 1) % RING);
+                if (stage_active(cur, st)) stage(cur, st, SLOT);
+            });
+        }
+        if (tid == 0) s_tk[(n + 1) & 1] = nxt;
+        __syncthreads();                                  // the ring is consumed and the ticket visible
+        const int following = item_at(s_tk[(n + 1) & 1]);
+        Item next = cur;
+        if (following >= 0) {
+            if (tid == 0) nxt = atomicAdd(ctr, 1);
+            next = decode(following);
+            load_kv(next);
+            prefetch(next);
+        }
+        epilogue(cur);
+        if (following < 0) break;
+        cur = next;
     }
 }
 
@@ -747,24 +810,29 @@ void bwd_dkdv_kernel(BwdParams p) {
 template <int D, bool F16>
 pvc_status launch_bwd(const BwdParams& prm, bool causal, bool out_f32, hipStream_t s) {
     static_assert(kThreads >= kBN - 1 + kScratchPad, "the last tile's workgroup zeroes every scratch row past T");
+    static_assert(kThreads >= kNumXcd * kQueueStride, "the first dQ workgroup zeroes the queue");
     const int64_t grid = ((int64_t)prm.items + kNumXcd - 1) / kNumXcd * kNumXcd;
     if (grid > 0x7fffffffLL) return PVC_ERR_INVALID_ARG;
     dim3 g((unsigned)grid), blk(kThreads);
+    // dK/dV: one workgroup per CU (its register use allows no more), a
+    // multiple of the XCD count so every XCD's queue has workgroups
+    const int64_t per_cu = std::max<int64_t>(kNumXcd, device_cu_count() / kNumXcd * kNumXcd);
+    dim3 gk((unsigned)std::min<int64_t>(grid, per_cu));
     if (causal) {
         if (out_f32) {
             hipLaunchKernelGGL((bwd_dq_kernel<D, true, true, F16>), g, blk, 0, s, prm);
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, true, F16, kDkdvHalves>), g, blk, 0, s, prm);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, true, F16, kDkdvHalves>), gk, blk, 0, s, prm);
         } else {
             hipLaunchKernelGGL((bwd_dq_kernel<D, true, false, F16>), g, blk, 0, s, prm);
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false, F16, kDkdvHalves>), g, blk, 0, s, prm);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false, F16, kDkdvHalves>), gk, blk, 0, s, prm);
         }
     } else {
         if (out_f32) {
             hipLaunchKernelGGL((bwd_dq_kernel<D, false, true, F16>), g, blk, 0, s, prm);
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true, F16, kDkdvHalves>), g, blk, 0, s, prm);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true, F16, kDkdvHalves>), gk, blk, 0, s, prm);
         } else {
             hipLaunchKernelGGL((bwd_dq_kernel<D, false, false, F16>), g, blk, 0, s, prm);
-            hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, false, F16, kDkdvHalves>), g, blk, 0, s, prm);
+            hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, false, F16, kDkdvHalves>), gk, blk, 0, s, prm);
         }
     }
     return launch_status();
@@ -787,7 +855,7 @@ using namespace pvc::attn;
 
 extern "C" size_t pvc_attn_bwd_scratch_size(int64_t total_tokens, int32_t heads) {
     if (total_tokens < 1 || total_tokens > 0x7fffffffLL || heads < 1) return 0;
-    return align_up((size_t)2 * heads * scratch_rows(total_tokens) * sizeof(float));
+    return planes_bytes(total_tokens, heads) + kQueueBytes;
 }
 
 extern "C" pvc_status pvc_varlen_attn_bwd_planned(const void* q, const void* k, const void* v, const void* out,
@@ -836,6 +904,7 @@ extern "C" pvc_status pvc_varlen_attn_bwd_planned(const void* q, const void* k, 
     prm.dout = static_cast<const uint16_t*>(dout);
     prm.lse = lse;
     prm.scratch = static_cast<float*>(scratch);
+    prm.queue = reinterpret_cast<int32_t*>(static_cast<char*>(scratch) + planes_bytes(total_tokens, heads));
     prm.dq = dq;
     prm.dk = dk;
     prm.dv = dv;
