@@ -761,8 +761,10 @@ void bwd_dkdv_kernel(BwdParams p) {
     __syncthreads();
     const int first = item_at(s_tk[0]);
     if (first < 0) return;                                // uniform: the queue is drained
+    // The next ticket is taken two stages before an item ends, so the queue
+    // hands items out in the order workgroups finish (as a dispatcher would)
+    // and the XCD's active key tiles stay neighbours that share Q / dO in L2.
     int nxt = 0;
-    if (tid == 0) nxt = atomicAdd(ctr, 1);               // ticket of the item after this one
     Item cur = decode(first);
     load_kv(cur);
     prefetch(cur);
@@ -784,15 +786,16 @@ void bwd_dkdv_kernel(BwdParams p) {
                 else wait_stages<RING, 2 * NH * CPW + 1>(min(RING - 2, cur.nstages - 1 - st));
                 __syncthreads();
                 if (st + RING - 1 < cur.nstages) fetch_stage(cur, st + RING - 1, (SLOT + RING - 1) % RING);
+                if (st == max(cur.nstages - 2, 0) && tid == 0) nxt = atomicAdd(ctr, 1);
                 if (stage_active(cur, st)) stage(cur, st, SLOT);
             });
         }
+        if (cur.nstages == 0 && tid == 0) nxt = atomicAdd(ctr, 1);
         if (tid == 0) s_tk[(n + 1) & 1] = nxt;
         __syncthreads();                                  // the ring is consumed and the ticket visible
         const int following = item_at(s_tk[(n + 1) & 1]);
         Item next = cur;
         if (following >= 0) {
-            if (tid == 0) nxt = atomicAdd(ctr, 1);
             next = decode(following);
             load_kv(next);
             prefetch(next);
