@@ -378,7 +378,8 @@ pvc_status pvc_varlen_attn_fwd(const void* q, const void* k, const void* v, void
  * pointers 16-byte aligned.
  * Arithmetic: MFMA products in the input type with fp32 accumulation; P and
  * dS are rounded to the input type (nearest even) for their products.
- * Deterministic: no atomics.
+ * Deterministic: every gradient element is written once by one workgroup and
+ * no atomic touches a value (the only atomic hands out dK/dV work items).
  */
 size_t pvc_attn_bwd_scratch_size(int64_t total_tokens, int32_t heads);
 pvc_status pvc_varlen_attn_bwd_planned(const void* q, const void* k, const void* v, const void* out,

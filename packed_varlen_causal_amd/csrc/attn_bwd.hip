@@ -31,12 +31,13 @@
 //                     (about 370 registers: the two fp32 accumulators alone
 //                     take 128).
 // Every product rounds its probability operand (P or dS) to the input type
-// (bf16 or fp16) and accumulates in fp32.  No atomics: each output element is
-// written once, so results do not depend on scheduling.  Stages that lie wholly outside a
-// wave's segments or on the wrong side of its diagonal are skipped, as in the
-// forward.  The dQ kernel recomputes S and dP, which the dK/dV kernel also
-// computes: seven products per score instead of five, the price of writing
-// every gradient once without atomics.
+// (bf16 or fp16) and accumulates in fp32.  Each output element is written
+// once by one workgroup and no atomic touches a value (the only atomic is the
+// dK/dV ticket), so results do not depend on scheduling.  Stages that lie
+// wholly outside a wave's segments or on the wrong side of its diagonal are
+// skipped, as in the forward.  The dQ kernel recomputes S and dP, which the
+// dK/dV kernel also computes: seven products per score instead of five, the
+// price of writing every gradient once without accumulating atomics.
 #include "attn_common.h"
 
 #include <algorithm>
