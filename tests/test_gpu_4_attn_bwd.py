@@ -123,6 +123,32 @@ def test_deterministic(pvc):
             assert (a == b).all()
 
 
+def test_scratch_reused_across_calls(pvc):
+    """One scratch buffer, filled with 0xFF, serves a large and then a small
+    backward.  The dK/dV work counters sit after the lse / D planes, at an
+    offset that depends on the call's size, and the dQ launch zeroes them on
+    every call: left at 0xFF they would read as a drained queue and no dK / dV
+    would be written.  Both calls must match calls with fresh buffers bit for bit."""
+    say("  bwd scratch reused across calls")
+    cases = []
+    for name, seed in (("pretrain", 31), ("sft", 32)):
+        w = make_workload(name, scale="small")
+        q, k, v, g = (_rand_bits((w.total_tokens, w.heads, w.head_dim), seed + i) for i in range(4))
+        cu = P.pack_build(w.lengths)["cu_seqlens"]
+        qd, kd, vd, gd = (dev_bf16(x) for x in (q, k, v, g))
+        plan = pvc.attn_plan(dev_i32(cu), w.total_tokens, int(w.lengths.max()))
+        out, lse = pvc.varlen_attn_fwd(qd, kd, vd, plan=plan, return_lse=True)
+        cases.append((w, (qd, kd, vd, out, gd, lse, plan)))
+    size = max(pvc.attn_bwd_scratch_size(w.total_tokens, w.heads) for w, _ in cases)
+    shared = torch.full((size,), 0xFF, dtype=torch.uint8, device="cuda")
+    reused = [[host_bits(t) for t in pvc.varlen_attn_bwd(*args, scratch=shared)] for _, args in cases]
+    fresh = [[host_bits(t) for t in pvc.varlen_attn_bwd(*args)] for _, args in cases]
+    torch.cuda.synchronize()
+    for r, f in zip(reused, fresh):
+        for a, b in zip(r, f):
+            assert (a == b).all()
+
+
 @pytest.mark.parametrize("name", ["sft", "pretrain", "longctx", "short"])
 def test_full_size_sampled_segments(pvc, name):
     """The benchmark's launch configuration; the oracle on sampled segments and heads."""
