@@ -197,6 +197,11 @@ def time_backward(torch, pvc, x, steps, warmup):
             "pct_bf16_peak": round(100 * bflops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
 
 
+# Untimed backward calls before the timed ones.  Right after the forward
+# steps the backward's first dozen calls run about 8% slower (1.41-1.46 ms on
+# the SFT packs after 2 calls, 1.31-1.33 ms after 30).
+BWD_WARMUP = 30
+
 CE_VOCAB = 32000          # the token recipe's id range [3, 32000)
 
 
@@ -579,7 +584,7 @@ def main():
         },
     }
     torch.cuda.synchronize()
-    res["kernels"]["varlen_attn_bwd"] = time_backward(torch, pvc, x, max(3, args.steps // 2), 2)
+    res["kernels"]["varlen_attn_bwd"] = time_backward(torch, pvc, x, max(3, args.steps // 2), BWD_WARMUP)
     res["kernels"]["packed_ce_loss"] = time_ce(torch, pvc, x, max(3, args.steps // 2), 2)
 
     if not args.no_extras:
@@ -607,7 +612,7 @@ def main():
                 "rope_gbps": round(rope_bytes(y.T, y.H, y.D) / (float(st[1]) * 1e-3) / 1e9, 1),
                 "effective_tokens_per_s": round(int(y.w.real_lengths.sum()) / (ms_s * 1e-3), 1),
             }
-            others[name]["backward"] = time_backward(torch, pvc, y, max(3, args.steps // 2), 2)
+            others[name]["backward"] = time_backward(torch, pvc, y, max(3, args.steps // 2), BWD_WARMUP)
             pad = padded_baseline(torch, pvc, y)
             pad["speedup_of_varlen"] = round(pad["ms"] / a_ms, 2)
             others[name]["padded_sbhd"] = pad
