@@ -91,8 +91,10 @@ const char* pvc_version(void);
 
 /* ------------------------------------------------------------ pack_build */
 
-/* Bytes of device workspace pvc_pack_build needs for `nseg` samples. */
-size_t pvc_pack_build_workspace_size(int32_t nseg);
+/* Bytes of device workspace pvc_pack_build needs for `nseg` samples and
+ * `total_tokens` tokens (0: no workspace needed; the scan's per-chunk
+ * partials are needed above 8192 samples and depend on nseg only). */
+size_t pvc_pack_build_workspace_size(int32_t nseg, int64_t total_tokens);
 
 /*
  * Packing metadata for one buffer of `nseg` samples laid end to end.
@@ -224,6 +226,13 @@ enum { PVC_OUT_BF16 = 0, PVC_OUT_F32 = 1, PVC_OUT_F16 = 2, PVC_OUT_F16_F32 = 3 }
 
 /* Bytes of workspace for a plan over `total_tokens` tokens in `nseg` segments. */
 size_t pvc_attn_workspace_size(int64_t total_tokens, int32_t nseg);
+
+/* The workspace query of pvc_varlen_attn_fwd with the arguments of that call
+ * ([charlestar] "varlen interface": total tokens, segments, max_seqlen, heads,
+ * head_dim).  The workspace is the plan, which depends on total_tokens only:
+ * the result equals pvc_attn_workspace_size(total_tokens, nseg). */
+size_t pvc_varlen_attn_fwd_workspace_size(int64_t total_tokens, int32_t nseg, int32_t max_seqlen,
+                                          int32_t heads, int32_t head_dim);
 
 /*
  * Build the tile plan for one cu_seqlens: every row's key range (its
@@ -438,7 +447,9 @@ size_t pvc_ce_workspace_size(int64_t total_tokens);
  *              loss is computed in fp32 (log-sum-exp with the row max
  *              subtracted); the sums run in fp64 in a fixed order, so the
  *              result does not depend on scheduling.
- * target_count [1] int64 out: the number of rows with a label in [0, vocab).
+ * target_count [1] int64 out: the number of target rows, those whose label
+ *              is not ignore_index and lies in [0, vocab) (an ignore_index
+ *              inside [0, vocab) still marks a row as ignored).
  * row_loss     [total_tokens] fp32 out, nullable: each row's loss, 0 for a
  *              row that is not a target.
  * seg_loss, seg_count  [nseg] fp64 / int64 out, nullable: the sums over

@@ -27,6 +27,7 @@ Entry points (same names as the C ABI without the ``pvc_`` prefix):
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 
 import torch
@@ -63,7 +64,7 @@ def _load() -> ctypes.CDLL:
     sig = {
         "pvc_status_string": ([I32], ctypes.c_char_p),
         "pvc_version": ([], ctypes.c_char_p),
-        "pvc_pack_build_workspace_size": ([I32], SZ),
+        "pvc_pack_build_workspace_size": ([I32, I64], SZ),
         "pvc_pack_build": ([P, P, P, I32, I64, I32, P, P, P, P, P, P, P, P, P, SZ, P], I32),
         "pvc_pack_tokens": ([P, P, P, I32, I64, I32, P, P, P, P, P, P, P], I32),
         "pvc_validate_cu_seqlens": ([P, I32, I64, I32, P, P, P], I32),
@@ -111,6 +112,21 @@ def _ptr(t: torch.Tensor | None):
 def _stream(stream=None):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _on_stream(fn):
+    """Run ``fn`` with ``stream`` (when given) as torch's current stream, so
+    that every tensor it allocates (outputs, plan workspaces, scratch, error
+    words) belongs to the stream the library enqueues on.  Temporaries freed
+    on return then go back to that stream's pool and are not handed to other
+    work while the enqueued kernels still read them."""
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kw):
+        if stream is None:
+            return fn(*args, **kw)
+        with torch.cuda.stream(stream):
+            return fn(*args, stream=stream, **kw)
+    return wrapper
 
 
 def _io_code(in_dtype: torch.dtype, out_dtype: torch.dtype) -> int:
@@ -161,6 +177,7 @@ def _new_error_word(device) -> torch.Tensor:
 
 # ------------------------------------------------------------------ packing
 
+@_on_stream
 def pack_build(lengths: torch.Tensor, tokens: torch.Tensor | None = None,
                is_pad: torch.Tensor | None = None, ignore_index: int = -100,
                total_tokens: int | None = None, dev_error: torch.Tensor | None = None,
@@ -202,7 +219,7 @@ def pack_build(lengths: torch.Tensor, tokens: torch.Tensor | None = None,
         out["shifted_labels"] = torch.empty(T, dtype=torch.int32, device=dev)
         out["loss_mask"] = torch.empty(T, dtype=torch.uint8, device=dev)
         out["num_targets"] = torch.empty(1, dtype=torch.int64, device=dev)
-    ws_bytes = _lib.pvc_pack_build_workspace_size(nseg)
+    ws_bytes = _lib.pvc_pack_build_workspace_size(nseg, T)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     st = _lib.pvc_pack_build(
         _ptr(lengths), _ptr(is_pad), _ptr(tokens), nseg, T, ignore_index, _ptr(out["cu_seqlens"]),
@@ -215,6 +232,7 @@ def pack_build(lengths: torch.Tensor, tokens: torch.Tensor | None = None,
     return out
 
 
+@_on_stream
 def pack_tokens(cu_seqlens: torch.Tensor, tokens: torch.Tensor | None = None, is_pad: torch.Tensor | None = None,
                 ignore_index: int = -100, total_tokens: int | None = None, dev_error: torch.Tensor | None = None,
                 check: bool = False, stream=None) -> dict:
@@ -257,6 +275,7 @@ def pack_tokens(cu_seqlens: torch.Tensor, tokens: torch.Tensor | None = None, is
     return out
 
 
+@_on_stream
 def validate_cu_seqlens(cu_seqlens: torch.Tensor, total_tokens: int, max_seqlen: int,
                         lengths: torch.Tensor | None = None, dev_error: torch.Tensor | None = None,
                         stream=None) -> torch.Tensor:
@@ -273,6 +292,7 @@ def validate_cu_seqlens(cu_seqlens: torch.Tensor, total_tokens: int, max_seqlen:
 
 # --------------------------------------------------------------------- RoPE
 
+@_on_stream
 def rope_thd_apply(q: torch.Tensor, k: torch.Tensor | None, cu_seqlens: torch.Tensor,
                    base: float = 10000.0, q_out: torch.Tensor | None = None,
                    k_out: torch.Tensor | None = None, dev_error: torch.Tensor | None = None,
@@ -317,6 +337,7 @@ class AttnPlan:
     tokens at rows [cu_seqlens_padded[r], + L_r) and ``total_tokens`` is the
     number of storage rows (see pvc_attn_plan_padded)."""
 
+    @_on_stream
     def __init__(self, cu_seqlens: torch.Tensor, total_tokens: int, max_seqlen: int,
                  causal: bool = True, dev_error: torch.Tensor | None = None, stream=None,
                  workspace: torch.Tensor | None = None, cu_seqlens_padded: torch.Tensor | None = None):
@@ -354,6 +375,7 @@ def attn_plan(cu_seqlens, total_tokens, max_seqlen, causal=True, **kw) -> AttnPl
 class AttnPlanQK:
     """Plan for separate query / key boundaries (pvc_attn_plan_qk)."""
 
+    @_on_stream
     def __init__(self, cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, total_q: int, total_k: int,
                  max_seqlen_q: int, max_seqlen_k: int, causal: bool = True,
                  dev_error: torch.Tensor | None = None, stream=None, workspace: torch.Tensor | None = None):
@@ -382,6 +404,7 @@ def attn_plan_qk(cu_seqlens_q, cu_seqlens_k, total_q, total_k, max_seqlen_q, max
     return AttnPlanQK(cu_seqlens_q, cu_seqlens_k, total_q, total_k, max_seqlen_q, max_seqlen_k, causal, **kw)
 
 
+@_on_stream
 def varlen_attn_fwd_qk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                        cu_seqlens_q: torch.Tensor | None = None, cu_seqlens_k: torch.Tensor | None = None,
                        max_seqlen_q: int | None = None, max_seqlen_k: int | None = None, causal: bool = True,
@@ -422,6 +445,7 @@ def varlen_attn_fwd_qk(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return (out, lse) if return_lse else out
 
 
+@_on_stream
 def varlen_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                     cu_seqlens: torch.Tensor | None = None, max_seqlen: int | None = None,
                     causal: bool = True, return_lse: bool = False,
@@ -465,6 +489,7 @@ def attn_bwd_scratch_size(total_tokens: int, heads: int) -> int:
     return int(_lib.pvc_attn_bwd_scratch_size(total_tokens, heads))
 
 
+@_on_stream
 def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
                     dout: torch.Tensor, lse: torch.Tensor, plan: AttnPlan, causal: bool = True,
                     grad_dtype: torch.dtype | None = None, grads=None, scratch: torch.Tensor | None = None,
@@ -514,6 +539,7 @@ def varlen_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torc
     return dq, dk, dv
 
 
+@_on_stream
 def padded_attn_fwd_sbhd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seqlens: torch.Tensor,
                          causal: bool = True, out_dtype: torch.dtype = torch.bfloat16,
                          out: torch.Tensor | None = None, stream=None):
@@ -545,6 +571,7 @@ def ce_workspace_size(total_tokens: int) -> int:
     return int(_lib.pvc_ce_workspace_size(total_tokens))
 
 
+@_on_stream
 def packed_ce_loss(logits: torch.Tensor, labels: torch.Tensor, cu_seqlens: torch.Tensor | None = None,
                    ignore_index: int = -100, row_loss: bool = False, segments: bool = False,
                    grad: torch.Tensor | str | None = None, grad_dtype: torch.dtype | None = None,

@@ -193,7 +193,10 @@ __global__ __launch_bounds__(256) void plan_rows_qk_kernel(const int32_t* __rest
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= Tq) return;
     const int32_t r = upper_segment(cu_q, nseg, i);
-    const int64_t qs = cu_q[r], qe = cu_q[r + 1];
+    // the request's query rows, clamped into [0, Tq] like every range read
+    // from device data: the forward's tile order is decoded from them
+    const int64_t qs = min<int64_t>(max<int64_t>(cu_q[r], 0), Tq);
+    const int64_t qe = min<int64_t>(max<int64_t>(cu_q[r + 1], qs), Tq);
     const int64_t ks = min<int64_t>(max<int64_t>(cu_k[r], 0), Tk);
     const int64_t ke = min<int64_t>(max<int64_t>(cu_k[r + 1], ks), Tk);
     const int64_t Lk = ke - ks;
@@ -354,7 +357,8 @@ void attn_fwd_kernel(AttnParams p) {
         const bool il = maxlen > 2 * kBM && p.head_block > 1;
         const int pos = il ? il_pos : hm_pos;
         const int2 sr = il ? sr_il : sr_hm;
-        int ta = (sr.x + kBM - 1) / kBM;
+        // (plan ranges lie in [0, T]; the clamp keeps ta >= 0 regardless)
+        int ta = max((sr.x + kBM - 1) / kBM, 0);
         int tb = min((sr.y + kBM - 1) / kBM, p.ntiles);
         if (!(pos >= ta && pos < tb)) {
             ta = pos;
@@ -780,6 +784,15 @@ extern "C" size_t pvc_attn_workspace_size(int64_t total_tokens, int32_t nseg) {
     return plan_layout(total_tokens).total;
 }
 
+// The forward's workspace is its plan, which depends on the tokens only.
+extern "C" size_t pvc_varlen_attn_fwd_workspace_size(int64_t total_tokens, int32_t nseg, int32_t max_seqlen,
+                                                     int32_t heads, int32_t head_dim) {
+    (void)max_seqlen;
+    (void)heads;
+    (void)head_dim;
+    return pvc_attn_workspace_size(total_tokens, nseg);
+}
+
 extern "C" pvc_status pvc_attn_plan(const int32_t* cu_seqlens, int32_t nseg, int64_t total_tokens,
                                     int32_t max_seqlen, int32_t causal, void* workspace,
                                     size_t workspace_bytes, uint32_t* dev_error, void* stream) {
@@ -1001,3 +1014,4 @@ extern "C" pvc_status pvc_padded_attn_fwd_sbhd(const void* q, const void* k, con
     if (head_dim == 128) return launch_fwd_t<128, true, false>(prm, causal != 0, f32, s);
     return launch_fwd_t<64, true, false>(prm, causal != 0, f32, s);
 }
+

@@ -128,7 +128,7 @@ __device__ inline void item_of(const BwdParams& p, int logical, int& head, int& 
     const int i = logical - hblk * per_block;            // < hx * ntiles
     const int pos = i / hx;
     const int2 sr = p.rows[(int64_t)pos * kBM];          // segment of the first row at pos
-    int ta = (sr.x + kBM - 1) / kBM;
+    int ta = max((sr.x + kBM - 1) / kBM, 0);
     int tb = min((sr.y + kBM - 1) / kBM, p.ntiles);
     if (!(pos >= ta && pos < tb)) {
         ta = pos;

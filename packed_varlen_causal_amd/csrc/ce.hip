@@ -136,6 +136,11 @@ __device__ inline MaxSum block_merge(MaxSum v, float* shm, float* shs) {
     return r;
 }
 
+// A row is a target when its label is not the ignore index and names a
+// class: the rule of pack_build's loss mask (label != ignore index), with
+// out-of-range labels excluded as well.
+__device__ inline bool ce_target(int32_t y, int32_t ignore, int32_t V) { return y != ignore && y >= 0 && y < V; }
+
 struct CeParams {
     const void* logits;
     int64_t ld;
@@ -174,8 +179,8 @@ __global__ __launch_bounds__(kCeThreads) void ce_row_kernel(CeParams p, bool vec
     const int V = p.V;
     const char* rowp = static_cast<const char*>(p.logits) + row * p.ld * (IN_F32 ? 4 : 2);
     const int32_t y = p.labels[row];
-    const bool valid = y >= 0 && y < V;
-    if (tid == 0 && !valid && y != p.ignore) raise_error(p.dev_error, PVC_DEV_LABEL);
+    const bool valid = ce_target(y, p.ignore, V);
+    if (tid == 0 && y != p.ignore && !(y >= 0 && y < V)) raise_error(p.dev_error, PVC_DEV_LABEL);
 
     // ---- pass 1: running max and sum of exp
     MaxSum acc;
@@ -322,7 +327,7 @@ __device__ inline void block_sum(double& s, long long& c, double* shs, long long
 
 __global__ __launch_bounds__(kCeThreads) void ce_reduce_kernel(const float* __restrict__ row_loss,
                                                                const int32_t* __restrict__ labels, int64_t T,
-                                                               int32_t V, double* __restrict__ psum,
+                                                               int32_t V, int32_t ignore, double* __restrict__ psum,
                                                                long long* __restrict__ pcount) {
     __shared__ double shs[kCeThreads / 64];
     __shared__ long long shc[kCeThreads / 64];
@@ -334,7 +339,7 @@ __global__ __launch_bounds__(kCeThreads) void ce_reduce_kernel(const float* __re
         if (r < T) {
             const int32_t y = labels[r];
             s += (double)row_loss[r];
-            c += (y >= 0 && y < V) ? 1 : 0;
+            c += ce_target(y, ignore, V) ? 1 : 0;
         }
     }
     block_sum(s, c, shs, shc);
@@ -367,7 +372,7 @@ __global__ __launch_bounds__(kCeThreads) void ce_final_kernel(const double* __re
 // entries set the usual error bits.
 __global__ __launch_bounds__(kCeThreads) void ce_segment_kernel(const float* __restrict__ row_loss,
                                                                 const int32_t* __restrict__ labels, int64_t T,
-                                                                int32_t V, const int32_t* __restrict__ cu,
+                                                                int32_t V, int32_t ignore, const int32_t* __restrict__ cu,
                                                                 int32_t nseg, double* __restrict__ seg_loss,
                                                                 int64_t* __restrict__ seg_count,
                                                                 uint32_t* dev_error) {
@@ -389,7 +394,7 @@ __global__ __launch_bounds__(kCeThreads) void ce_segment_kernel(const float* __r
     for (int64_t i = a + lane; i < b; i += 64) {
         const int32_t y = labels[i];
         s += (double)row_loss[i];
-        c += (y >= 0 && y < V) ? 1 : 0;
+        c += ce_target(y, ignore, V) ? 1 : 0;
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
@@ -509,13 +514,13 @@ extern "C" pvc_status pvc_packed_ce_loss(const void* logits, int32_t logits_dtyp
     double* psum = reinterpret_cast<double*>(ws + L.psum);
     long long* pcount = reinterpret_cast<long long*>(ws + L.pcount);
     hipLaunchKernelGGL(ce_reduce_kernel, dim3((unsigned)L.nblk), dim3(kCeThreads), 0, s, prm.row_loss, labels,
-                       total_tokens, vocab, psum, pcount);
+                       total_tokens, vocab, ignore_index, psum, pcount);
     hipLaunchKernelGGL(ce_final_kernel, dim3(1), dim3(kCeThreads), 0, s, psum, pcount, L.nblk, loss_sum,
                        target_count);
     if (seg_loss != nullptr || seg_count != nullptr) {
         const unsigned blocks = (unsigned)((nseg + kCeThreads / 64 - 1) / (kCeThreads / 64));
         hipLaunchKernelGGL(ce_segment_kernel, dim3(blocks), dim3(kCeThreads), 0, s, prm.row_loss, labels,
-                           total_tokens, vocab, cu_seqlens, nseg, seg_loss, seg_count, dev_error);
+                           total_tokens, vocab, ignore_index, cu_seqlens, nseg, seg_loss, seg_count, dev_error);
     }
     return launch_status();
 }

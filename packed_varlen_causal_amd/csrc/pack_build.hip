@@ -323,7 +323,11 @@ void launch_tokens(hipStream_t s, const int32_t* cu, const uint8_t* is_pad, cons
 
 using namespace pvc;
 
-extern "C" size_t pvc_pack_build_workspace_size(int32_t nseg) {
+// total_tokens is part of the query so that callers size the workspace from
+// the same arguments they pass to pvc_pack_build; the scan's partials depend
+// on the segment count only.
+extern "C" size_t pvc_pack_build_workspace_size(int32_t nseg, int64_t total_tokens) {
+    (void)total_tokens;
     if (nseg <= kScanChunk) return 0;
     const size_t nch = ((size_t)nseg + kScanChunk - 1) / kScanChunk;
     return align_up(nch * sizeof(long long)) + align_up(nch * sizeof(int));
@@ -340,7 +344,7 @@ extern "C" pvc_status pvc_pack_build(const int32_t* lengths, const uint8_t* is_p
     if ((shifted_labels != nullptr || loss_mask != nullptr || num_targets != nullptr) && tokens == nullptr)
         return PVC_ERR_NULL;
     if (nseg < 1 || total_tokens < 1 || total_tokens > 0x7fffffffLL) return PVC_ERR_INVALID_ARG;
-    const size_t need = pvc_pack_build_workspace_size(nseg);
+    const size_t need = pvc_pack_build_workspace_size(nseg, total_tokens);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return PVC_ERR_WORKSPACE;
     hipStream_t s = as_stream(stream);
 

@@ -149,6 +149,39 @@ def test_scratch_reused_across_calls(pvc):
             assert (a == b).all()
 
 
+def test_explicit_side_stream_with_library_temporaries(pvc):
+    """Forward with plan=None and backward with scratch=None, both on an
+    explicit stream that is not torch's current one: the plan workspace, the
+    error word and the backward scratch are allocated on that stream, so the
+    allocator does not hand their memory to the current stream's work (here
+    a stream of fills of fresh tensors) while the kernels still read them.
+    Results must equal the current-stream calls bit for bit."""
+    w = make_workload("sft", scale="small")
+    say("  fwd / bwd on a side stream with library temporaries")
+    q, k, v, g = (_rand_bits((w.total_tokens, w.heads, w.head_dim), 40 + i) for i in range(4))
+    cu = P.pack_build(w.lengths)["cu_seqlens"]
+    qd, kd, vd, gd, cud = (*(dev_bf16(x) for x in (q, k, v, g)), dev_i32(cu))
+    mx = int(w.lengths.max())
+    out0, lse0 = pvc.varlen_attn_fwd(qd, kd, vd, cud, mx, return_lse=True)
+    plan0 = pvc.attn_plan(cud, w.total_tokens, mx)
+    grads0 = pvc.varlen_attn_bwd(qd, kd, vd, out0, gd, lse0, plan0)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    out1, lse1 = pvc.varlen_attn_fwd(qd, kd, vd, cud, mx, return_lse=True, stream=side)
+    plan1 = pvc.attn_plan(cud, w.total_tokens, mx, stream=side)
+    grads1 = pvc.varlen_attn_bwd(qd, kd, vd, out1, gd, lse1, plan1, stream=side)
+    junk = [torch.full((1 << 20,), 0x7F, dtype=torch.uint8, device="cuda") for _ in range(32)]
+    side.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    assert int(plan1.dev_error.item()) == 0
+    assert (host_bits(out1) == host_bits(out0)).all()
+    assert torch.equal(lse1, lse0)
+    for a, b in zip(grads1, grads0):
+        assert (host_bits(a) == host_bits(b)).all()
+
+
 @pytest.mark.parametrize("name", ["sft", "pretrain", "longctx", "short"])
 def test_full_size_sampled_segments(pvc, name):
     """The benchmark's launch configuration; the oracle on sampled segments and heads."""

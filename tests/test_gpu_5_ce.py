@@ -179,6 +179,35 @@ def test_bad_labels_are_flagged_and_skipped(pvc):
     _check_loss(out, ref, _f64(bits))
 
 
+def test_ignore_index_inside_the_vocabulary(pvc):
+    """An ignore index that is itself a class id (7 here) still marks its rows
+    as ignored: no loss, no count, no gradient, as pack_build's loss mask
+    (label != ignore index) and the oracle read it; per-segment counts too."""
+    T, V, IGN = 200, 1001, 7
+    rng = np.random.default_rng(9)
+    bits = f32_to_bf16_bits(rng.standard_normal((T, V), dtype=np.float32) * 2)
+    lab = rng.integers(0, V, T).astype(np.int32)
+    lab[::4] = IGN
+    lab[5] = -100                   # another class-free label: not a target, flagged
+    cu = np.array([0, 50, 51, 130, 200], np.int32)
+    scale = float(np.float32(1.0 / 128))
+    out = pvc.packed_ce_loss(_dev_logits(bits), dev_i32(lab), dev_i32(cu), ignore_index=IGN, row_loss=True,
+                             segments=True, grad="new", grad_dtype=torch.float32, grad_scale=scale)
+    torch.cuda.synchronize()
+    ref = L.packed_loss(bits, lab, cu, ignore_index=IGN)
+    assert int(out["dev_error"].item()) == ref["err"] == L.ERR_LABEL
+    assert int(out["target_count"].item()) == ref["target_count"] == int(((lab != IGN) & (lab >= 0)).sum())
+    rl = out["row_loss"].cpu().numpy()
+    assert (rl[lab == IGN] == 0).all()
+    _check_loss(out, ref, _f64(bits), cu)
+    g = out["grad"].cpu().numpy().astype(np.float64)
+    gref = L.loss_grad(bits, lab, scale, ignore_index=IGN)
+    bnd = grad_bound(_f64(bits), lab, scale)
+    bnd[lab == IGN] = 0.0
+    assert (g[lab == IGN] == 0).all()
+    assert (np.abs(g - gref) <= bnd).all()
+
+
 def test_large_logits_stay_finite(pvc):
     T, V = 16, 256
     rng = np.random.default_rng(4)

@@ -127,3 +127,21 @@ def test_plans_are_not_interchangeable(pvc):
         ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     torch.cuda.synchronize()
     assert st == 0 and int(selfp.dev_error.item()) & 128 and (out2.float() == 7.0).all()
+
+
+@pytest.mark.parametrize("cu_q,Tq", [([-300, 40, 64], 64), ([-1000, -500, 300], 300)])
+def test_malformed_query_boundaries_write_nothing(pvc, cu_q, Tq):
+    """A cu_seqlens_q with a negative first entry: the plan clamps the query
+    ranges it decodes the tile order from (an unclamped range once gave tile
+    -1), flags PVC_DEV_CU0 and the forward writes nothing."""
+    cu_k = [0, 30, 64]
+    H, d = 16, 128
+    say(f"  prefill malformed cu_q={cu_q} Tq={Tq}")
+    q = dev_bf16(_bits((Tq, H, d), 1))
+    k, v = dev_bf16(_bits((64, 4, d), 2)), dev_bf16(_bits((64, 4, d), 3))
+    plan = pvc.attn_plan_qk(dev_i32(cu_q), dev_i32(cu_k), Tq, 64, Tq, 64, True)
+    out = torch.full((Tq, H, d), 7.0, dtype=torch.bfloat16, device="cuda")
+    pvc.varlen_attn_fwd_qk(q, k, v, plan=plan, out=out)
+    torch.cuda.synchronize()
+    assert int(plan.dev_error.item()) & 1
+    assert (out.float() == 7.0).all()

@@ -43,8 +43,24 @@ def test_header_declares_the_hot_path():
                  "pvc_varlen_attn_bwd_planned", "pvc_attn_bwd_scratch_size", "pvc_packed_ce_loss",
                  "pvc_ce_workspace_size", "pvc_attn_plan_padded", "pvc_rope_thd_apply_interleaved",
                  "pvc_attn_plan_qk", "pvc_varlen_attn_fwd_qk_planned", "pvc_rope_thd_apply_ex",
-                 "pvc_pack_tokens"):
+                 "pvc_pack_tokens", "pvc_varlen_attn_fwd_workspace_size"):
         assert must in names
+
+
+def test_scoped_boundary_names_and_arities():
+    """The entry points of the scoped boundary exist with the argument counts
+    it lists (the departures in argument lists are supersets: RoPE takes
+    separate in / out pointers, validation optional lengths, the padded
+    baseline an output dtype and no workspace)."""
+    with open(HEADER) as f:
+        text = re.sub(r"/\*.*?\*/", " ", f.read(), flags=re.S)
+    arity = {m.group(1): len([a for a in m.group(2).split(",") if a.strip() not in ("", "void")])
+             for m in re.finditer(r"\b(pvc_\w+)\s*\(([^;{]*?)\)\s*;", text, flags=re.S)}
+    want = {"pvc_pack_build_workspace_size": 2, "pvc_pack_build": 17, "pvc_validate_cu_seqlens": 7,
+            "pvc_rope_thd_apply": 12, "pvc_varlen_attn_fwd_workspace_size": 5, "pvc_varlen_attn_fwd": 17,
+            "pvc_padded_attn_fwd_sbhd": 12, "pvc_status_string": 1}
+    for name, n in want.items():
+        assert arity.get(name) == n, (name, arity.get(name), n)
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -81,14 +97,14 @@ def test_workspace_queries(lib):
     lib.pvc_attn_workspace_size.restype = ctypes.c_size_t
     lib.pvc_attn_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int32]
     lib.pvc_pack_build_workspace_size.restype = ctypes.c_size_t
-    lib.pvc_pack_build_workspace_size.argtypes = [ctypes.c_int32]
+    lib.pvc_pack_build_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int64]
     small = lib.pvc_attn_workspace_size(9, 3)
     big = lib.pvc_attn_workspace_size(131072, 57)
     assert 0 < small < big
     assert big >= 131072 * 8            # per-row key ranges
     assert lib.pvc_attn_workspace_size(0, 1) == 0
-    assert lib.pvc_pack_build_workspace_size(100) == 0
-    assert lib.pvc_pack_build_workspace_size(1 << 20) > 0
+    assert lib.pvc_pack_build_workspace_size(100, 9000) == 0
+    assert lib.pvc_pack_build_workspace_size(1 << 20, 1 << 22) > 0
 
 
 def _vp(x):
