@@ -59,7 +59,9 @@ enum {
     PVC_ERR_INVALID_ARG = 2,   /* a size or flag is out of range */
     PVC_ERR_UNSUPPORTED = 3,   /* a shape the kernels do not implement (e.g. head_dim) */
     PVC_ERR_WORKSPACE = 4,     /* workspace NULL or smaller than the size query */
-    PVC_ERR_HIP = 5            /* the HIP runtime reported an error (launch, device) */
+    PVC_ERR_HIP = 5,           /* the HIP runtime reported an error (launch, device) */
+    PVC_ERR_SCRATCH_LIMIT = 6  /* an allocation-free entry point got more tokens than
+                                  its library-owned scratch holds */
 };
 
 /* Bits of the device error word.  The cu_seqlens contract is the one listed
@@ -360,6 +362,27 @@ pvc_status pvc_varlen_attn_fwd(const void* q, const void* k, const void* v, void
                                int32_t head_dim, int32_t causal, int32_t out_dtype,
                                void* workspace, size_t workspace_bytes, uint32_t* dev_error,
                                void* stream);
+
+/*
+ * pvc_varlen_attn_fwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same plan and forward, with the plan kept in a
+ * library-owned static device array instead of a caller workspace.  No
+ * hipMalloc, hipFree or other allocating call is made; the first call on a
+ * device looks the array's address up (hipGetSymbolAddress) and caches it.
+ * Limit: total_tokens <= pvc_noalloc_max_tokens() (2^20), else
+ * PVC_ERR_SCRATCH_LIMIT before any HIP call.  Each GPU holds one 16 MiB
+ * array until the process ends, shared by every call on that GPU: calls that
+ * overlap on one GPU (other streams, other host threads) race on it and must
+ * be serialised by the caller; calls in order on one stream are safe.
+ * Arguments, results, determinism and the other errors are those of
+ * pvc_varlen_attn_fwd; its outputs are bit-identical to that call's.
+ */
+int64_t pvc_noalloc_max_tokens(void);
+pvc_status pvc_varlen_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                                       const int32_t* cu_seqlens, int32_t nseg, int64_t total_tokens,
+                                       int32_t max_seqlen, int32_t heads, int32_t head_dim, int32_t causal,
+                                       int32_t out_dtype, uint32_t* dev_error, void* stream);
 
 /*
  * Attention backward with an existing plan (the one the forward used): the

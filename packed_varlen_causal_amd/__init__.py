@@ -37,12 +37,13 @@ __all__ = [
     "rope_thd_apply", "AttnPlan", "attn_plan", "varlen_attn_fwd", "varlen_attn_bwd",
     "padded_attn_fwd_sbhd", "error_names", "attn_workspace_size", "attn_bwd_scratch_size",
     "packed_ce_loss", "ce_workspace_size", "AttnPlanQK", "attn_plan_qk", "varlen_attn_fwd_qk",
+    "varlen_attn_fwd_noalloc", "noalloc_max_tokens",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libpvc.so")
 
-OK, ERR_NULL, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(6)
+OK, ERR_NULL, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH_LIMIT = range(7)
 OUT_BF16, OUT_F32, OUT_F16, OUT_F16_F32 = 0, 1, 2, 3
 DEV_ERROR_BITS = {
     1: "CU0", 2: "NOT_INCREASING", 4: "TOTAL", 8: "MAXSEQ", 16: "LENGTH",
@@ -78,6 +79,9 @@ def _load() -> ctypes.CDLL:
         "pvc_varlen_attn_fwd_qk_planned": ([P, P, P, P, P, I64, I64, I32, I32, I32, I32, I32, P, SZ, P, P], I32),
         "pvc_varlen_attn_fwd_planned": ([P, P, P, P, P, I64, I32, I32, I32, I32, P, SZ, P, P], I32),
         "pvc_varlen_attn_fwd": ([P, P, P, P, P, P, I32, I64, I32, I32, I32, I32, I32, P, SZ, P, P], I32),
+        "pvc_varlen_attn_fwd_workspace_size": ([I64, I32, I32, I32, I32], SZ),
+        "pvc_noalloc_max_tokens": ([], I64),
+        "pvc_varlen_attn_fwd_noalloc": ([P, P, P, P, P, P, I32, I64, I32, I32, I32, I32, I32, P, P], I32),
         "pvc_padded_attn_fwd_sbhd": ([P, P, P, P, P, I32, I32, I32, I32, I32, I32, P], I32),
         "pvc_attn_bwd_scratch_size": ([I64, I32], SZ),
         "pvc_varlen_attn_bwd_planned": ([P, P, P, P, P, P, P, P, P, I64, I32, I32, I32, I32, P, SZ, P, SZ,
@@ -483,6 +487,43 @@ def varlen_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if check:
         _raise_dev(plan.dev_error, "varlen_attn_fwd")
     return (out, lse) if return_lse else out
+
+
+def noalloc_max_tokens() -> int:
+    return int(_lib.pvc_noalloc_max_tokens())
+
+
+@_on_stream
+def varlen_attn_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
+                            max_seqlen: int, causal: bool = True, out: torch.Tensor | None = None,
+                            lse: torch.Tensor | None = None, dev_error: torch.Tensor | None = None,
+                            stream=None):
+    """varlen_attn_fwd through pvc_varlen_attn_fwd_noalloc: the plan lives in
+    the library's own static device memory, so the C call allocates nothing.
+    Pass ``out`` (and ``lse`` [H, T] fp32, ``dev_error``) to allocate nothing
+    here either; a missing ``out`` is allocated in the inputs' dtype."""
+    in_dt = _require16((q, k, v), ("q", "k", "v"))
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must share the shape [T, H, d]")
+    _require(cu_seqlens, "cu_seqlens", torch.int32, 1)
+    T, H, D = q.shape
+    if out is None:
+        out = torch.empty((T, H, D), dtype=in_dt, device=q.device)
+    elif out.dtype not in (in_dt, torch.float32):
+        raise TypeError("out must be the inputs' dtype or torch.float32")
+    _require(out, "out", out.dtype, 3)
+    if tuple(out.shape) != (T, H, D):
+        raise ValueError("out must be [T, H, d] like q")
+    if lse is not None:
+        _require(lse, "lse", torch.float32, 2)
+        if tuple(lse.shape) != (H, T):
+            raise ValueError("lse must be [H, T]")
+    code = _io_code(in_dt, out.dtype)
+    st = _lib.pvc_varlen_attn_fwd_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens), cu_seqlens.numel() - 1, T,
+        int(max_seqlen), H, D, int(bool(causal)), code, _ptr(dev_error), _stream(stream))
+    _check(st, "varlen_attn_fwd_noalloc")
+    return out
 
 
 def attn_bwd_scratch_size(total_tokens: int, heads: int) -> int:

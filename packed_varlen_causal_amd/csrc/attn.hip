@@ -50,6 +50,8 @@
 // a segment and loses their K/V reuse in L2.
 #include <math.h>
 
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "attn_common.h"
@@ -1015,3 +1017,70 @@ extern "C" pvc_status pvc_padded_attn_fwd_sbhd(const void* q, const void* k, con
     return launch_fwd_t<64, true, false>(prm, causal != 0, f32, s);
 }
 
+// ------------------------------------------------ allocation-free forward
+//
+// pvc_varlen_attn_fwd with its plan in a library-owned device array instead
+// of a caller workspace, for callers that cannot allocate.  The array holds
+// the plan layout of kNoAllocMaxTokens tokens (16 MiB + 256 B); each GPU the
+// library runs on gets its own copy,
+// kept until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the device symbol): the
+// device address comes from hipGetSymbolAddress, once per device, and is
+// cached per device.  Every call on one GPU shares that GPU's array, so
+// calls that overlap on one GPU (different streams, or other host threads)
+// race on the plan; calls ordered on one stream do not.  Nothing in it needs
+// clearing: each call's plan launch rewrites the header and every row the
+// forward reads before the forward runs.
+
+namespace {
+constexpr int64_t kNoAllocMaxTokens = (int64_t)1 << 20;
+// plan_layout(kNoAllocMaxTokens).total: the header, then two int2 planes
+constexpr size_t kNoAllocBytes = kAlign + 2 * (size_t)kNoAllocMaxTokens * sizeof(int2);
+constexpr int kNoAllocMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+static_assert(kNoAllocBytes % kAlign == 0, "the plan layout's regions are 256-byte aligned");
+
+namespace {
+std::atomic<void*> g_scratch_ptr[kNoAllocMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device (with that device current) and cached.
+pvc_status noalloc_scratch(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoAllocMaxDevices) return PVC_ERR_HIP;
+    void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (ptr == nullptr) {
+            if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return PVC_ERR_HIP;
+            g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+        }
+    }
+    *out = ptr;
+    return PVC_OK;
+}
+}  // namespace
+
+extern "C" int64_t pvc_noalloc_max_tokens(void) { return kNoAllocMaxTokens; }
+
+extern "C" pvc_status pvc_varlen_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* out,
+                                                  float* lse, const int32_t* cu_seqlens, int32_t nseg,
+                                                  int64_t total_tokens, int32_t max_seqlen, int32_t heads,
+                                                  int32_t head_dim, int32_t causal, int32_t out_dtype,
+                                                  uint32_t* dev_error, void* stream) {
+    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || cu_seqlens == nullptr) return PVC_ERR_NULL;
+    if (total_tokens < 1) return PVC_ERR_INVALID_ARG;
+    // the size limit before any HIP call
+    if (total_tokens > kNoAllocMaxTokens || plan_layout(total_tokens).total > kNoAllocBytes)
+        return PVC_ERR_SCRATCH_LIMIT;
+    void* ws = nullptr;
+    const pvc_status st = noalloc_scratch(&ws);
+    if (st != PVC_OK) return st;
+    // the remaining checks, the plan and the forward: pvc_varlen_attn_fwd
+    return pvc_varlen_attn_fwd(q, k, v, out, lse, cu_seqlens, nseg, total_tokens, max_seqlen, heads, head_dim,
+                               causal, out_dtype, ws, kNoAllocBytes, dev_error, stream);
+}

@@ -30,6 +30,7 @@ extern "C" const char* pvc_status_string(pvc_status status) {
         case PVC_ERR_UNSUPPORTED: return "unsupported shape (head_dim or layout)";
         case PVC_ERR_WORKSPACE: return "workspace missing or too small";
         case PVC_ERR_HIP: return "HIP runtime error";
+        case PVC_ERR_SCRATCH_LIMIT: return "more tokens than the allocation-free entry point's static scratch holds";
         default: return "unknown status";
     }
 }

@@ -261,3 +261,21 @@ def test_python_binding_imports_without_gpu():
     import packed_varlen_causal_amd as pvc
     assert "gfx950" in pvc.version()
     assert pvc.error_names(1 | 32) == ["CU0", "MISMATCH"]
+
+
+def test_noalloc_forward_refuses_beyond_its_static_scratch_before_gpu_work(lib):
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.pvc_varlen_attn_fwd_noalloc.restype = I32
+    lib.pvc_varlen_attn_fwd_noalloc.argtypes = [P, P, P, P, P, P, I32, I64, I32, I32, I32, I32, I32, P, P]
+    lib.pvc_noalloc_max_tokens.restype = I64
+    limit = lib.pvc_noalloc_max_tokens()
+    assert limit == 1 << 20
+    fake = _vp(0x100000)       # never dereferenced: the calls below return before any HIP call
+    assert lib.pvc_varlen_attn_fwd_noalloc(fake, fake, fake, fake, None, fake, 1, limit + 1, limit + 1, 32, 128,
+                                           1, 0, None, None) == 6
+    assert lib.pvc_varlen_attn_fwd_noalloc(None, fake, fake, fake, None, fake, 1, 9, 9, 2, 64, 1, 0, None,
+                                           None) == 1
+    assert lib.pvc_varlen_attn_fwd_noalloc(fake, fake, fake, fake, None, fake, 1, 0, 9, 2, 64, 1, 0, None,
+                                           None) == 2
+    lib.pvc_status_string.restype = ctypes.c_char_p
+    assert b"static scratch" in lib.pvc_status_string(6)
