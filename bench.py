@@ -617,6 +617,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (HBM counter calibration)")
+    ap.add_argument("--only", choices=("pack_build_2^28", "prefill"),
+                    help="only time one side measurement (for kernel traces and counters) and print it")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -636,6 +638,13 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": n, "reps": 5}), flush=True)
         return
     import packed_varlen_causal_amd as pvc
+
+    if args.only == "pack_build_2^28":
+        print(json.dumps({"pack_build_2^28": pack_build_large(torch, pvc, reps=args.steps)}), flush=True)
+        return
+    if args.only == "prefill":
+        print(json.dumps({"prefill": time_prefill(torch, pvc, args.steps, args.warmup)}), flush=True)
+        return
 
     x = Inputs(args.workload, torch, pvc, keep_host=not args.no_cpu_baseline)
     torch.cuda.synchronize()

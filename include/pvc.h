@@ -94,8 +94,10 @@ const char* pvc_version(void);
 /* ------------------------------------------------------------ pack_build */
 
 /* Bytes of device workspace pvc_pack_build needs for `nseg` samples and
- * `total_tokens` tokens (0: no workspace needed; the scan's per-chunk
- * partials are needed above 8192 samples and depend on nseg only). */
+ * `total_tokens` tokens (0: no workspace needed).  Above 8192 samples it
+ * holds the scan's per-chunk partials; above 2^20 tokens, the segment at
+ * which each 2048-token block of the per-token pass starts (written by the
+ * scan, so those blocks need not search cu_seqlens). */
 size_t pvc_pack_build_workspace_size(int32_t nseg, int64_t total_tokens);
 
 /*

@@ -267,8 +267,9 @@ struct AttnParams {
     int32_t group;             // query heads per key / value head
     int32_t folded;            // the plan's row ranges hold the causal limit
     int32_t causal_flag;       // causal as the caller asked (checked against the plan)
-    int32_t ntiles;            // THD: tiles; SBHD: tiles per sample
-    int32_t items;             // heads x tiles (x batch for SBHD)
+    int32_t ntiles;            // THD: 128-row tiles (the plan's); SBHD: tiles per sample
+    int32_t ntiles_q;          // grouped heads (QH > 1): 32-row query tiles
+    int32_t items;             // heads x tiles (x batch for SBHD); head groups x 32-row tiles (QH > 1)
     int32_t head_block;        // THD: heads interleaved per segment run (item order)
     int32_t B, L;              // SBHD: batch and padded length
     float scale_log2;          // log2(e) / sqrt(d)
@@ -279,10 +280,18 @@ struct AttnParams {
 // accumulator is rescaled: probabilities stay below 2^8.
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D, bool CAUSAL, bool OUT_F32, bool SBHD, bool F16>
+// QH > 1 (grouped key / value heads, QH a divisor of the group size): the
+// workgroup's waves are QH = 4 query heads of one key / value head on the
+// same 32 query rows, so each K / V stage is staged once for four heads, the
+// waves see identical key ranges (no wave waits at a stage barrier with
+// nothing to compute), and a tile is 32 rows.  QH == 1: four waves of one
+// head on 128 rows.
+template <int D, bool CAUSAL, bool OUT_F32, bool SBHD, bool F16, int QH = 1>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void attn_fwd_kernel(AttnParams p) {
     static_assert(D == 64 || D == 128, "head_dim");
+    static_assert(QH == 1 || (QH == kWaves && !SBHD), "grouped heads: one wave per query head");
+    constexpr int BM = QH == 1 ? kBM : 32;    // query rows per tile
     using E = Elt<F16>;                      // bf16 or fp16 inputs
     using x8 = typename E::x8;
     using x2 = typename E::x2;
@@ -306,6 +315,7 @@ void attn_fwd_kernel(AttnParams p) {
     const int per_xcd = nblk / kNumXcd;
     const int logical = (blockIdx.x % kNumXcd) * per_xcd + blockIdx.x / kNumXcd;
     if (logical >= p.items) return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int head, b = 0, r0, r1, last_row;
     int4 hd0 = {0, 0, 0, 0}, hd1 = {0, 0, 0, 0};      // THD: the plan header
     int seg_lo = 0;
@@ -318,6 +328,30 @@ void attn_fwd_kernel(AttnParams p) {
         r0 = tile * kBM;
         r1 = min(r0 + kBM, p.L);
         last_row = p.L - 1;
+    } else if constexpr (QH > 1) {
+        // Head groups in order; inside a group the query segments in buffer
+        // order, each segment's 32-row tiles from its end (the heaviest) to
+        // its start, as for single heads.  With as many groups as XCDs each
+        // XCD runs one group, so the group's K / V stays in one L2.
+        hd0 = *reinterpret_cast<const int4*>(p.header);
+        hd1 = *reinterpret_cast<const int4*>(p.header + 4);
+        const int nt = p.ntiles_q;
+        const int grp = logical / nt;
+        const int pos = logical - grp * nt;
+        const int2* seg_of = p.folded ? p.qseg : p.rows;
+        const int2 sr = seg_of[(int64_t)pos * BM];
+        int ta = max((sr.x + BM - 1) / BM, 0);
+        int tb = min((sr.y + BM - 1) / BM, nt);
+        if (!(pos >= ta && pos < tb)) {
+            ta = pos;
+            tb = pos + 1;
+        }
+        const int tile = ta + tb - 1 - pos;
+        head = grp * QH + wave;
+        seg_lo = sr.x;
+        r0 = tile * BM;
+        r1 = (int)min<int64_t>((int64_t)r0 + BM, p.T);
+        last_row = (int)(p.Tk - 1);
     } else {
         // Segments in buffer order, and inside each segment its tiles from
         // last to first: a segment's later tiles have the longer key ranges,
@@ -394,13 +428,12 @@ void attn_fwd_kernel(AttnParams p) {
     };
 
     const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int c = lane & 31;
     const int g = lane >> 5;
 
-    // ---- wave and lane row ranges
-    const int wr0 = r0 + 32 * wave;
+    // ---- wave and lane row ranges (grouped heads: every wave on the tile's rows)
+    const int wr0 = QH == 1 ? r0 + 32 * wave : r0;
     const int wr1 = min(wr0 + 32, r1);
     const bool wave_active = wr0 < r1;
     const int row = min(wr0 + c, r1 - 1);
@@ -703,7 +736,7 @@ void attn_fwd_kernel(AttnParams p) {
         // own 32-row slice of the stage buffers, free once all waves are past
         // the last stage; 16-byte chunks are XOR-swizzled by row.
         constexpr int CPR = ROW_B / 16;                    // 16-byte chunks per row
-        static_assert(kBM * ROW_B <= 2 * kRing * TILE_B, "output tile fits the stage buffers");
+        static_assert(kWaves * 32 * ROW_B <= 2 * kRing * TILE_B, "output tile fits the stage buffers");
         __syncthreads();
         char* const ob_lds = kbase + wave * 32 * ROW_B;
 #pragma unroll
@@ -734,11 +767,18 @@ void attn_fwd_kernel(AttnParams p) {
     }
 }
 
-template <int D, bool SBHD, bool F16>
+template <int D, bool SBHD, bool F16, int QH = 1>
 pvc_status launch_fwd_t(const AttnParams& prm, bool causal, bool out_f32, hipStream_t s) {
     const int64_t grid = ((int64_t)prm.items + kNumXcd - 1) / kNumXcd * kNumXcd;
     if (grid > 0x7fffffffLL) return PVC_ERR_INVALID_ARG;
     dim3 g((unsigned)grid), blk(kThreads);
+    if constexpr (QH > 1) {
+        // folded plans only: the causal limit is in the row ranges
+        if (causal) return PVC_ERR_INVALID_ARG;
+        if (out_f32) hipLaunchKernelGGL((attn_fwd_kernel<D, false, true, SBHD, F16, QH>), g, blk, 0, s, prm);
+        else hipLaunchKernelGGL((attn_fwd_kernel<D, false, false, SBHD, F16, QH>), g, blk, 0, s, prm);
+        return launch_status();
+    }
     if (causal) {
         if (out_f32) hipLaunchKernelGGL((attn_fwd_kernel<D, true, true, SBHD, F16>), g, blk, 0, s, prm);
         else hipLaunchKernelGGL((attn_fwd_kernel<D, true, false, SBHD, F16>), g, blk, 0, s, prm);
@@ -755,10 +795,10 @@ inline bool io_valid(int32_t t) { return t == PVC_OUT_BF16 || t == PVC_OUT_F32 |
 inline bool io_f16(int32_t t) { return t == PVC_OUT_F16 || t == PVC_OUT_F16_F32; }
 inline bool io_f32(int32_t t) { return t == PVC_OUT_F32 || t == PVC_OUT_F16_F32; }
 
-template <int D>
+template <int D, int QH = 1>
 pvc_status launch_thd(const AttnParams& prm, bool causal, int32_t out_dtype, hipStream_t s) {
-    if (io_f16(out_dtype)) return launch_fwd_t<D, false, true>(prm, causal, io_f32(out_dtype), s);
-    return launch_fwd_t<D, false, false>(prm, causal, io_f32(out_dtype), s);
+    if (io_f16(out_dtype)) return launch_fwd_t<D, false, true, QH>(prm, causal, io_f32(out_dtype), s);
+    return launch_fwd_t<D, false, false, QH>(prm, causal, io_f32(out_dtype), s);
 }
 
 // Heads per block of the item order: one block per XCD when the head count
@@ -957,6 +997,13 @@ extern "C" pvc_status pvc_varlen_attn_fwd_qk_planned(const void* q, const void* 
     prm.dev_error = dev_error;
     hipStream_t s = as_stream(stream);
     // the causal limit is in the plan's row ranges: the kernel runs without its own diagonal
+    if (prm.group % kWaves == 0) {
+        // four query heads of one key / value head per workgroup, 32-row tiles
+        prm.ntiles_q = (int32_t)((total_q + 31) / 32);
+        prm.items = (int32_t)((int64_t)prm.ntiles_q * (heads / kWaves));
+        if (head_dim == 128) return launch_thd<128, kWaves>(prm, false, out_dtype, s);
+        return launch_thd<64, kWaves>(prm, false, out_dtype, s);
+    }
     if (head_dim == 128) return launch_thd<128>(prm, false, out_dtype, s);
     return launch_thd<64>(prm, false, out_dtype, s);
 }

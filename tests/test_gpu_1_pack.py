@@ -75,6 +75,19 @@ def test_many_segments_multi_chunk_scan(pvc):
     _compare(got, P.pack_build(w.lengths, toks, w.is_pad))
 
 
+@pytest.mark.parametrize("total,lo,hi", [((1 << 21) + 777, 8, 128), ((1 << 21) + 5, 1, 3), ((1 << 21) + 1, 1500, 6000)])
+def test_large_buffer_block_map(pvc, total, lo, hi):
+    """Above 2^20 tokens the scan writes, for every 2048-token block of the
+    per-token pass, the segment its first token lies in (the workspace's
+    block map); segments shorter than a 4-token group, and longer than a
+    block, against the oracle bit for bit."""
+    w = make_workload("short", total=total, lo=lo, hi=hi)
+    say(f"  pack_build block map: T={w.total_tokens} nseg={w.nseg} lengths [{lo}, {hi}]")
+    toks = token_ids(w)
+    got = _run_pack(pvc, w.lengths, toks, w.is_pad)
+    _compare(got, P.pack_build(w.lengths, toks, w.is_pad))
+
+
 @pytest.mark.parametrize("name", CONFIG_NAMES)
 def test_pack_tokens_on_given_cu(pvc, name):
     """The per-token pass alone, on pack_build's cu_seqlens (computed without
@@ -170,3 +183,37 @@ def test_validate_bits(pvc, golden):
         err = pvc.validate_cu_seqlens(dev_i32(cu), T, mx, None if lens is None else dev_i32(lens))
         torch.cuda.synchronize()
         assert int(err.item()) == P.validate_cu(cu, T, mx, lens), (cu, T, mx, lens)
+
+
+@pytest.mark.parametrize("name", ["sft", "short"])
+def test_pack_tokens_unaligned_outputs(pvc, name):
+    """Outputs that do not start on a 16-byte boundary take the per-token
+    kernel's element-at-a-time path (the vector path needs 16-byte aligned
+    token ids and int32 outputs, a 4-byte aligned mask): same bits."""
+    import ctypes
+    w = make_workload(name, scale="small")
+    T = w.total_tokens
+    toks = token_ids(w)
+    ref = P.pack_build(w.lengths, toks, w.is_pad)
+    cu = dev_i32(ref["cu_seqlens"])
+    pt = torch.from_numpy(np.asarray(w.is_pad, np.uint8)).cuda()
+    tbuf = torch.zeros(T + 1, dtype=torch.int32, device="cuda")
+    tbuf[1:] = dev_i32(toks)
+    bufs = [torch.full((T + 1,), 77, dtype=torch.int32, device="cuda") for _ in range(3)]
+    mbuf = torch.full((T + 1,), 9, dtype=torch.uint8, device="cuda")
+    count = torch.zeros(1, dtype=torch.int64, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    off = lambda t, n: ctypes.c_void_p(t.data_ptr() + n)          # noqa: E731
+    say(f"  pack_tokens unaligned {name}: T={T}")
+    st = pvc._lib.pvc_pack_tokens(pvc._ptr(cu), pvc._ptr(pt), off(tbuf, 4), w.nseg, T, -100, off(bufs[0], 4),
+                                  off(bufs[1], 4), off(bufs[2], 4), off(mbuf, 1), pvc._ptr(count), pvc._ptr(err),
+                                  pvc._stream())
+    assert st == 0
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    got = [b.cpu().numpy()[1:] for b in bufs]
+    assert (got[0] == ref["segment_ids"]).all()
+    assert (got[1] == ref["position_ids"]).all()
+    assert (got[2] == ref["shifted_labels"]).all()
+    assert (mbuf.cpu().numpy()[1:] == ref["loss_mask"]).all()
+    assert int(count.item()) == ref["num_targets"]

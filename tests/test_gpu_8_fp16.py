@@ -106,8 +106,12 @@ def test_backward_fp16_refuses_mixed_types(pvc):
         pvc.varlen_attn_bwd(q, q, q, out, q, lse, plan, grad_dtype=torch.bfloat16)
 
 
-def test_prefill_fp16(pvc):
+@pytest.mark.parametrize("heads,kv_heads", [(4, 2), (8, 2)])
+def test_prefill_fp16(pvc, heads, kv_heads):
+    """The small prefill in fp16, with 2 query heads per key / value head
+    and with 4 (four query heads per workgroup)."""
     pw = make_prefill(scale="small")
+    pw.heads, pw.kv_heads = heads, kv_heads
     q = _f16((pw.total_q, pw.heads, pw.head_dim), 4)
     k, v = _f16((pw.total_k, pw.kv_heads, pw.head_dim), 5), _f16((pw.total_k, pw.kv_heads, pw.head_dim), 6)
     cu_q = np.concatenate([[0], np.cumsum(pw.lq)])

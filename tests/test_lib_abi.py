@@ -104,6 +104,7 @@ def test_workspace_queries(lib):
     assert big >= 131072 * 8            # per-row key ranges
     assert lib.pvc_attn_workspace_size(0, 1) == 0
     assert lib.pvc_pack_build_workspace_size(100, 9000) == 0
+    assert lib.pvc_pack_build_workspace_size(100, (1 << 20) + 1) >= 4 * ((1 << 20) + 1) // 2048
     assert lib.pvc_pack_build_workspace_size(1 << 20, 1 << 22) > 0
 
 
