@@ -339,18 +339,35 @@ void bwd_dq_kernel(BwdParams p) {
     // overlap the other's exponentials
     auto stage = [&](int st, int slot) __attribute__((always_inline)) {
         f32x16 S[NH], dP[NH];
+        x8 ka[NH][NS], va[NH][NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            static_for<NH>([&](auto H_) {
+                constexpr int h = decltype(H_)::value;
+                ka[h][s] = rop(kbase + (slot * NH + h) * TILE_B, s);
+                va[h][s] = rop(vbase + (slot * NH + h) * TILE_B, s);
+            });
         static_for<NH>([&](auto H_) {
             constexpr int h = decltype(H_)::value;
-            const char* kb = kbase + (slot * NH + h) * TILE_B;
-            const char* vb = vbase + (slot * NH + h) * TILE_B;
             S[h] = f32x16(0.0f);
             dP[h] = f32x16(0.0f);
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                S[h] = E::mfma(rop(kb, s), qreg[s], S[h]);          // S^T = K Q^T
-                dP[h] = E::mfma(rop(vb, s), doreg[s], dP[h]);       // dP^T = V dO^T
-            }
         });
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            static_for<NH>([&](auto H_) {
+                constexpr int h = decltype(H_)::value;
+                S[h] = E::mfma(ka[h][s], qreg[s], S[h]);
+                dP[h] = E::mfma(va[h][s], doreg[s], dP[h]);
+            });
+        // the K and V operand reads run 4 ahead of their MFMAs (mask 0x100 =
+        // LDS read, 0x008 = MFMA); with two waves per SIMD a shorter lead
+        // than the dK/dV kernel's suffices (8 measured slower here)
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        static_for<2 * NH * NS - 4>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        });
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         static_for<NH>([&](auto H_) {
             constexpr int h = decltype(H_)::value;
             const int kt = k_lo + st * SKEYS + h * kBN;
@@ -640,18 +657,36 @@ void bwd_dkdv_kernel(BwdParams p) {
     auto stage = [&](const Item& it, int st, int slot) __attribute__((always_inline)) {
         const int qt = it.q_lo + st * SROWS;
         f32x16 S[NH], dP[NH];
+        x8 qa[NH][NS], oa[NH][NS];
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            static_for<NH>([&](auto H_) {
+                constexpr int h = decltype(H_)::value;
+                qa[h][s] = rop(qbase + (slot * NH + h) * TILE_B, s);
+                oa[h][s] = rop(obase + (slot * NH + h) * TILE_B, s);
+            });
         static_for<NH>([&](auto H_) {
             constexpr int h = decltype(H_)::value;
-            const char* qb = qbase + (slot * NH + h) * TILE_B;
-            const char* ob = obase + (slot * NH + h) * TILE_B;
             S[h] = f32x16(0.0f);
             dP[h] = f32x16(0.0f);
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                S[h] = E::mfma(rop(qb, s), kreg[s], S[h]);      // S = Q K^T
-                dP[h] = E::mfma(rop(ob, s), vreg[s], dP[h]);    // dP = dO V^T
-            }
         });
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            static_for<NH>([&](auto H_) {
+                constexpr int h = decltype(H_)::value;
+                S[h] = E::mfma(qa[h][s], kreg[s], S[h]);
+                dP[h] = E::mfma(oa[h][s], vreg[s], dP[h]);
+            });
+        // schedule: the LDS reads of the A operands run 8 ahead of the MFMAs
+        // that take them (mask 0x100 = LDS read, 0x008 = MFMA), so one wave
+        // per SIMD does not stall on each read's latency; without the fence
+        // the compiler issues each read just before its product
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        static_for<2 * NH * NS - 8>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        });
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         static_for<NH>([&](auto H_) {
             constexpr int h = decltype(H_)::value;
             // lane = key c; register r = query qt + 32h + 8(r/4) + 4g + r%4
