@@ -296,8 +296,12 @@ pvc_status pvc_attn_plan_padded(const int32_t* cu_seqlens, const int32_t* cu_seq
  * [nseg + 1] int32 on the device, strictly increasing from 0 to total_q /
  * total_k, segments at most max_seqlen_q / max_seqlen_k (else the usual error
  * bits and an empty plan).  Workspace pvc_attn_workspace_size(total_q, nseg).
- * Query tiles run request by request, each request's from its end (the
- * heaviest) to its start.  Used by pvc_varlen_attn_fwd_qk_planned
+ * The plan also fixes the start order of the forward's 32-row query tiles:
+ * each request's tiles in chunks of 8 from its end (the heaviest) down, the
+ * chunks longest-first by the keys of their heaviest tile (with more than
+ * 2,048 chunks: request by request, each from its end to its start).  The
+ * order changes when work starts, never a result.  Used by
+ * pvc_varlen_attn_fwd_qk_planned
  * only (a forward: the backward entry refuses this plan).
  */
 pvc_status pvc_attn_plan_qk(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t nseg,

@@ -208,9 +208,139 @@ __global__ __launch_bounds__(256) void plan_rows_qk_kernel(const int32_t* __rest
     qseg[i] = ok ? make_int2((int)qs, (int)qe) : make_int2((int)i, (int)i);
 }
 
+// ---- start order of the grouped-head forward's 32-row query tiles.
+// A tile belongs to the request of its first row.  Each request's run of
+// tiles is cut into chunks of kOrderChunk tiles from its last (heaviest)
+// tile down, and the chunks start in decreasing order of the key span of
+// their heaviest tile (ties in buffer order): the longest tiles start first,
+// as in longest-processing-time-first list scheduling, while a chunk's tiles
+// stay neighbours that read their request's K / V together through L2.
+// Inference prefills mix requests whose tiles differ in length by 100x
+// (cached prefixes); in buffer order a long request near the end of the
+// buffer starts its tiles last and the XCD finishes on them alone.
+constexpr int kOrderChunk = 8;
+constexpr int kOrderMaxChunks = 2048;    // beyond: the buffer order below
+
+// The buffer order: requests in buffer order, each request's tiles from its
+// last to its first (a position outside every run is a run of one).
+__device__ inline int mirrored_tile(const int2* __restrict__ qseg, int nt, int pos) {
+    const int2 sr = qseg[(int64_t)pos * 32];
+    int64_t ta = max<int64_t>((sr.x + 31LL) / 32, 0);
+    int64_t tb = min<int64_t>((sr.y + 31LL) / 32, nt);
+    if (!(pos >= ta && pos < tb)) {
+        ta = pos;
+        tb = pos + 1;
+    }
+    return (int)(ta + tb - 1 - pos);
+}
+
+// Keys a 32-row tile's waves stream: from its first row's range start to
+// its last row's range end (ranges of a folded plan grow with the row).
+__device__ inline int tile_span(const int2* __restrict__ rows, int64_t Tq, int64_t tile) {
+    const int64_t a = tile * 32, b = min<int64_t>(a + 31, Tq - 1);
+    return max(rows[b].y - rows[a].x, 0);
+}
+
+// Exclusive prefix sum of v over the workgroup's threads (thread order),
+// and the total.  Every thread of the kCheckThreads-thread workgroup calls it.
+__device__ inline int block_excl_sum(int v, int* s_wave, int& total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) s_wave[wave] = x;
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kCheckThreads / 64; ++w) {
+        const int cw = s_wave[w];
+        off += w < wave ? cw : 0;
+        tot += cw;
+    }
+    __syncthreads();
+    total = tot;
+    return off + x - v;
+}
+
+// order[pos] = the tile that starts at position pos, for every position of
+// [0, nt): a permutation of the tiles.  Sorted when the plan is valid and it
+// has at most kOrderMaxChunks chunks, else the buffer order.
+__device__ void build_tile_order(const int2* __restrict__ rows, const int2* __restrict__ qseg, int64_t Tq, int nt,
+                                 bool valid, int32_t* __restrict__ order) {
+    __shared__ int s_w[kOrderMaxChunks], s_hi[kOrderMaxChunks], s_n[kOrderMaxChunks], s_rank[kOrderMaxChunks],
+            s_off[kOrderMaxChunks];
+    __shared__ int s_wave[kCheckThreads / 64];
+    const int t = threadIdx.x;
+    // more tiles than chunks x chunk size leave too many chunks anyway
+    if (valid && (int64_t)nt <= (int64_t)kOrderChunk * kOrderMaxChunks) {
+        // tile x heads a chunk when it lies a multiple of kOrderChunk below
+        // its run's last tile; the chunk is [x - n + 1, x]
+        int nc = 0, covered = 0;                          // workgroup-uniform
+        for (int base = 0; base < nt; base += kCheckThreads) {
+            const int x = base + t;
+            bool head = false;
+            int n = 0, w = 0;
+            if (x < nt) {
+                const int2 sr = qseg[(int64_t)x * 32];
+                const int64_t ta = max<int64_t>((sr.x + 31LL) / 32, 0);
+                const int64_t tb = min<int64_t>((sr.y + 31LL) / 32, nt);
+                if (x >= ta && x < tb && (tb - 1 - x) % kOrderChunk == 0) {
+                    head = true;
+                    n = (int)min<int64_t>(kOrderChunk, x + 1 - ta);
+                    for (int i = 0; i < n; ++i) w = max(w, tile_span(rows, Tq, x - i));
+                }
+            }
+            int heads, tiles;
+            const int slot = nc + block_excl_sum(head ? 1 : 0, s_wave, heads);
+            block_excl_sum(n, s_wave, tiles);
+            if (head && slot < kOrderMaxChunks) {
+                s_w[slot] = w;
+                s_hi[slot] = x + 1;
+                s_n[slot] = n;
+            }
+            nc += heads;
+            covered += tiles;
+        }
+        // the chunks cover every tile once when the plan is valid
+        if (nc <= kOrderMaxChunks && covered == nt) {
+            __syncthreads();
+            // rank: larger span first, ties by buffer position (a permutation)
+            for (int ci = t; ci < nc; ci += kCheckThreads) {
+                const int w = s_w[ci];
+                int r = 0;
+                for (int d = 0; d < nc; ++d) {
+                    const int wd = s_w[d];
+                    r += (wd > w) | ((wd == w) & (d < ci));
+                }
+                s_rank[ci] = r;
+                s_off[r] = s_n[ci];
+            }
+            __syncthreads();
+            // first position of each rank: exclusive sum, two ranks per thread
+            const int a0 = 2 * t < nc ? s_off[2 * t] : 0;
+            const int a1 = 2 * t + 1 < nc ? s_off[2 * t + 1] : 0;
+            int total;
+            const int e = block_excl_sum(a0 + a1, s_wave, total);
+            if (2 * t < nc) s_off[2 * t] = e;
+            if (2 * t + 1 < nc) s_off[2 * t + 1] = e + a0;
+            __syncthreads();
+            for (int ci = t; ci < nc; ci += kCheckThreads) {
+                const int b = s_off[s_rank[ci]], hi = s_hi[ci], n = s_n[ci];
+                for (int i = 0; i < n; ++i) order[b + i] = hi - 1 - i;
+            }
+            return;
+        }
+    }
+    for (int pos = t; pos < nt; pos += kCheckThreads) order[pos] = mirrored_tile(qseg, nt, pos);
+}
+
 __global__ __launch_bounds__(kCheckThreads) void plan_check_qk_kernel(
         const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int32_t nseg, int64_t Tq, int64_t Tk,
         int32_t max_q, int32_t max_k, int32_t causal, int32_t* __restrict__ header, int32_t ntiles,
+        const int2* __restrict__ rows, const int2* __restrict__ qseg, int32_t* __restrict__ order,
         uint32_t* dev_error) {
     __shared__ unsigned s_err;
     __shared__ int s_max;
@@ -235,6 +365,8 @@ __global__ __launch_bounds__(kCheckThreads) void plan_check_qk_kernel(
     }
     if (err) atomicOr(&s_err, err);
     __syncthreads();
+    // (the row ranges are complete: plan_rows_qk_kernel ran before on the stream)
+    build_tile_order(rows, qseg, Tq, (int)((Tq + 31) / 32), s_err == 0, order);
     if (t == 0) {
         header[HDR_MAGIC] = kPlanMagic;
         header[HDR_T] = (int32_t)Tq;
@@ -260,6 +392,7 @@ struct AttnParams {
     const int32_t* header;     // THD: plan header
     const int2* rows;          // THD: per-row key range
     const int2* qseg;          // THD: per-row query segment (tile order of folded plans)
+    const int32_t* order;      // grouped heads: start order of the 32-row tiles
     const int32_t* seqlens;    // SBHD: valid length per sample
     int64_t T;                 // THD: query rows
     int64_t Tk;                // THD: key / value rows
@@ -313,7 +446,7 @@ void attn_fwd_kernel(AttnParams p) {
     // ---- which (head, tile): XCD-contiguous remap of the block index
     const int nblk = gridDim.x;
     const int per_xcd = nblk / kNumXcd;
-    const int logical = (blockIdx.x % kNumXcd) * per_xcd + blockIdx.x / kNumXcd;
+    const int logical = QH > 1 ? (int)blockIdx.x : (blockIdx.x % kNumXcd) * per_xcd + blockIdx.x / kNumXcd;
     if (logical >= p.items) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int head, b = 0, r0, r1, last_row;
@@ -329,26 +462,21 @@ void attn_fwd_kernel(AttnParams p) {
         r1 = min(r0 + kBM, p.L);
         last_row = p.L - 1;
     } else if constexpr (QH > 1) {
-        // Head groups in order; inside a group the query segments in buffer
-        // order, each segment's 32-row tiles from its end (the heaviest) to
-        // its start, as for single heads.  With as many groups as XCDs each
-        // XCD runs one group, so the group's K / V stays in one L2.
+        // Items position-major: block b runs head group b % G at position
+        // b / G of the plan's tile order (heaviest chunks first).  Blocks go
+        // to the XCDs round-robin, so with a multiple of 8 groups an XCD runs
+        // whole groups (their K / V stays in one L2) and with fewer it runs
+        // an even share of every group's positions.  Grouped heads run on
+        // plans of separate boundaries only (folded: each row's keys are its
+        // own range, k_lo below), so no segment start is needed here.
         hd0 = *reinterpret_cast<const int4*>(p.header);
         hd1 = *reinterpret_cast<const int4*>(p.header + 4);
         const int nt = p.ntiles_q;
-        const int grp = logical / nt;
-        const int pos = logical - grp * nt;
-        const int2* seg_of = p.folded ? p.qseg : p.rows;
-        const int2 sr = seg_of[(int64_t)pos * BM];
-        int ta = max((sr.x + BM - 1) / BM, 0);
-        int tb = min((sr.y + BM - 1) / BM, nt);
-        if (!(pos >= ta && pos < tb)) {
-            ta = pos;
-            tb = pos + 1;
-        }
-        const int tile = ta + tb - 1 - pos;
+        const int G = p.H / QH;
+        const int grp = logical % G;
+        const int pos = logical / G;
+        const int tile = min(max(p.order[pos], 0), nt - 1);
         head = grp * QH + wave;
-        seg_lo = sr.x;
         r0 = tile * BM;
         r1 = (int)min<int64_t>((int64_t)r0 + BM, p.T);
         last_row = (int)(p.Tk - 1);
@@ -947,7 +1075,7 @@ extern "C" pvc_status pvc_attn_plan_qk(const int32_t* cu_seqlens_q, const int32_
                        nseg, total_q, total_k, causal ? 1 : 0, rows, qseg);
     hipLaunchKernelGGL(plan_check_qk_kernel, dim3(1), dim3(kCheckThreads), 0, s, cu_seqlens_q, cu_seqlens_k, nseg,
                        total_q, total_k, max_seqlen_q, max_seqlen_k, causal ? 1 : 0, header, (int32_t)L.ntiles,
-                       dev_error);
+                       rows, qseg, reinterpret_cast<int32_t*>(ws + L.order), dev_error);
     return launch_status();
 }
 
@@ -984,6 +1112,7 @@ extern "C" pvc_status pvc_varlen_attn_fwd_qk_planned(const void* q, const void* 
     prm.header = reinterpret_cast<const int32_t*>(ws + L.header);
     prm.rows = reinterpret_cast<const int2*>(ws + L.rows);
     prm.qseg = reinterpret_cast<const int2*>(ws + L.qseg);
+    prm.order = reinterpret_cast<const int32_t*>(ws + L.order);
     prm.T = total_q;
     prm.Tk = total_k;
     prm.H = heads;
@@ -1081,8 +1210,10 @@ extern "C" pvc_status pvc_padded_attn_fwd_sbhd(const void* q, const void* k, con
 
 namespace {
 constexpr int64_t kNoAllocMaxTokens = (int64_t)1 << 20;
-// plan_layout(kNoAllocMaxTokens).total: the header, then two int2 planes
-constexpr size_t kNoAllocBytes = kAlign + 2 * (size_t)kNoAllocMaxTokens * sizeof(int2);
+// plan_layout(kNoAllocMaxTokens).total: the header, two int2 planes and the
+// tile order (one int32 per 32 rows)
+constexpr size_t kNoAllocBytes =
+        kAlign + 2 * (size_t)kNoAllocMaxTokens * sizeof(int2) + (size_t)kNoAllocMaxTokens / 32 * sizeof(int32_t);
 constexpr int kNoAllocMaxDevices = 64;
 }  // namespace
 

@@ -36,7 +36,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct PlanLayout {
-    size_t header, rows, qseg, total;
+    size_t header, rows, qseg, order, total;
     int64_t ntiles;
 };
 
@@ -52,6 +52,10 @@ inline PlanLayout plan_layout(int64_t T) {
     // (tile order only)
     L.qseg = off;
     off += align_up((size_t)T * sizeof(int2));
+    // the start order of the 32-row query tiles (grouped-head forward over a
+    // plan of separate query / key boundaries)
+    L.order = off;
+    off += align_up((size_t)((T + 31) / 32) * sizeof(int32_t));
     L.total = off;
     return L;
 }

@@ -174,3 +174,96 @@ def test_four_query_heads_per_kv_head_every_row(pvc, d, causal):
         fin = np.isfinite(ref_lse)
         assert np.abs(ls.cpu().numpy().T[fin] - ref_lse[fin]).max() < 5e-3
         assert np.isneginf(ls.cpu().numpy().T[~fin]).all()
+
+
+def _align(x, a=256):
+    return (x + a - 1) // a * a
+
+
+def _plan_tile_order(plan):
+    """The plan's tile-order table: the workspace holds a 256-byte header, the
+    per-row key ranges and query segments (int2 per query row each, every
+    region 256-byte aligned), then one int32 per 32-row query tile."""
+    T = plan.total_q
+    off = 256 + 2 * _align(8 * T)
+    nt = (T + 31) // 32
+    return plan.workspace[off:off + 4 * nt].cpu().numpy().view(np.int32).copy()
+
+
+def _expected_tile_order(cu_q, cu_k, causal, chunk=8, max_chunks=2048):
+    """The start order of the 32-row tiles, written from its definition: a
+    tile belongs to the request of its first row; each request's tiles are cut
+    into chunks of 8 from its last tile down; chunks go in decreasing order of
+    the key span of their heaviest tile (first row's range start to last
+    row's range end), ties by the chunk's last tile; more than 2048 chunks:
+    requests in buffer order, each request's tiles last to first."""
+    cu_q, cu_k = np.asarray(cu_q, np.int64), np.asarray(cu_k, np.int64)
+    Tq = int(cu_q[-1])
+    nt = (Tq + 31) // 32
+    x = np.zeros(Tq, np.int64)
+    y = np.zeros(Tq, np.int64)
+    for r in range(len(cu_q) - 1):
+        qs, qe, ks, ke = cu_q[r], cu_q[r + 1], cu_k[r], cu_k[r + 1]
+        i = np.arange(qs, qe)
+        n = np.minimum(ke - ks, i - qs + (ke - ks) - (qe - qs) + 1) if causal else np.full(i.size, ke - ks)
+        x[i] = ks
+        y[i] = ks + np.maximum(n, 0)
+    span = [max(int(y[min(32 * t + 31, Tq - 1)] - x[32 * t]), 0) for t in range(nt)]
+    chunks = []
+    for r in range(len(cu_q) - 1):
+        ta, tb = -(-int(cu_q[r]) // 32), -(-int(cu_q[r + 1]) // 32)
+        for hi in range(tb, ta, -chunk):
+            lo = max(ta, hi - chunk)
+            chunks.append((hi, hi - lo, max(span[lo:hi])))
+    if len(chunks) > max_chunks:
+        order = []
+        for r in range(len(cu_q) - 1):
+            ta, tb = -(-int(cu_q[r]) // 32), -(-int(cu_q[r + 1]) // 32)
+            order += list(range(tb - 1, ta - 1, -1))
+        return np.asarray(order, np.int32)
+    chunks.sort(key=lambda c: (-c[2], c[0]))
+    return np.asarray([hi - 1 - i for hi, n, _ in chunks for i in range(n)], np.int32)
+
+
+@pytest.mark.parametrize("which", ["prefill", "many_short"])
+def test_tile_order_is_the_sorted_chunk_permutation(pvc, which):
+    """The plan's tile order equals the one written from its definition (the
+    full prefill: sorted chunks; 3,000 short requests: more than 2,048 chunks,
+    the buffer order), so every tile is run exactly once."""
+    if which == "prefill":
+        pw = make_prefill()
+        lq, lk = pw.lq, pw.lk
+    else:
+        rng = np.random.default_rng(5)
+        lq = rng.integers(20, 45, size=3000)
+        lk = lq + rng.integers(0, 100, size=3000)
+    cu_q, cu_k = _cu(lq), _cu(lk)
+    say(f"  tile order {which}: Tq={int(cu_q[-1])} requests={len(lq)}")
+    plan = pvc.attn_plan_qk(dev_i32(cu_q), dev_i32(cu_k), int(cu_q[-1]), int(cu_k[-1]), int(np.max(lq)),
+                            int(np.max(lk)), True)
+    torch.cuda.synchronize()
+    assert int(plan.dev_error.item()) == 0
+    got = _plan_tile_order(plan)
+    want = _expected_tile_order(cu_q, cu_k, True)
+    nt = (int(cu_q[-1]) + 31) // 32
+    assert np.array_equal(np.sort(got), np.arange(nt))
+    assert np.array_equal(got, want)
+
+
+def test_full_prefill_writes_every_row(pvc):
+    """Every query row of the full prefill is written (output prefilled with
+    NaN), in the launch the bench times."""
+    pw = make_prefill()
+    cu_q, cu_k = _cu(pw.lq), _cu(pw.lk)
+    g = torch.Generator(device="cuda").manual_seed(3)
+    q = torch.randn((pw.total_q, pw.heads, pw.head_dim), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn((pw.total_k, pw.kv_heads, pw.head_dim), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn_like(k)
+    plan = pvc.attn_plan_qk(dev_i32(cu_q), dev_i32(cu_k), pw.total_q, pw.total_k, int(pw.lq.max()),
+                            int(pw.lk.max()), True)
+    out = torch.full_like(q, float("nan"))
+    say(f"  prefill full coverage Tq={pw.total_q} Tk={pw.total_k}")
+    pvc.varlen_attn_fwd_qk(q, k, v, plan=plan, out=out)
+    torch.cuda.synchronize()
+    assert int(plan.dev_error.item()) == 0
+    assert not torch.isnan(out.float()).any()
