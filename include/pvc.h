@@ -297,7 +297,7 @@ pvc_status pvc_attn_plan_padded(const int32_t* cu_seqlens, const int32_t* cu_seq
  * total_k, segments at most max_seqlen_q / max_seqlen_k (else the usual error
  * bits and an empty plan).  Workspace pvc_attn_workspace_size(total_q, nseg).
  * The plan also fixes the start order of the forward's 32-row query tiles:
- * each request's tiles in chunks of 8 from its end (the heaviest) down, the
+ * each request's tiles in chunks of 16 from its end (the heaviest) down, the
  * chunks longest-first by the keys of their heaviest tile (with more than
  * 2,048 chunks: request by request, each from its end to its start).  The
  * order changes when work starts, never a result.  Used by

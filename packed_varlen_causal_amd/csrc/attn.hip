@@ -218,7 +218,7 @@ __global__ __launch_bounds__(256) void plan_rows_qk_kernel(const int32_t* __rest
 // Inference prefills mix requests whose tiles differ in length by 100x
 // (cached prefixes); in buffer order a long request near the end of the
 // buffer starts its tiles last and the XCD finishes on them alone.
-constexpr int kOrderChunk = 8;
+constexpr int kOrderChunk = 16;
 constexpr int kOrderMaxChunks = 2048;    // beyond: the buffer order below
 
 // The buffer order: requests in buffer order, each request's tiles from its

@@ -190,10 +190,10 @@ def _plan_tile_order(plan):
     return plan.workspace[off:off + 4 * nt].cpu().numpy().view(np.int32).copy()
 
 
-def _expected_tile_order(cu_q, cu_k, causal, chunk=8, max_chunks=2048):
+def _expected_tile_order(cu_q, cu_k, causal, chunk=16, max_chunks=2048):
     """The start order of the 32-row tiles, written from its definition: a
     tile belongs to the request of its first row; each request's tiles are cut
-    into chunks of 8 from its last tile down; chunks go in decreasing order of
+    into chunks of 16 from its last tile down; chunks go in decreasing order of
     the key span of their heaviest tile (first row's range start to last
     row's range end), ties by the chunk's last tile; more than 2048 chunks:
     requests in buffer order, each request's tiles last to first."""
