@@ -718,7 +718,7 @@ def main():
             del y
             torch.cuda.empty_cache()
         res["other_workloads"] = others
-        res["prefill"] = time_prefill(torch, pvc, max(3, args.steps // 2), 2)
+        res["prefill"] = time_prefill(torch, pvc, max(20, args.steps), max(50, args.warmup))
 
     if not args.no_cpu_baseline:
         cb = cpu_baseline(x, args.cpu_seconds)
