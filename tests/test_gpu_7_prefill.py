@@ -225,11 +225,11 @@ def _expected_tile_order(cu_q, cu_k, causal, chunk=16, max_chunks=2048):
     return np.asarray([hi - 1 - i for hi, n, _ in chunks for i in range(n)], np.int32)
 
 
-@pytest.mark.parametrize("which", ["prefill", "many_short"])
-def test_tile_order_is_the_sorted_chunk_permutation(pvc, which):
+@pytest.mark.parametrize("which,causal", [("prefill", True), ("prefill", False), ("many_short", True)])
+def test_tile_order_is_the_sorted_chunk_permutation(pvc, which, causal):
     """The plan's tile order equals the one written from its definition (the
-    full prefill: sorted chunks; 3,000 short requests: more than 2,048 chunks,
-    the buffer order), so every tile is run exactly once."""
+    full prefill, causal and not: sorted chunks; 3,000 short requests: more
+    than 2,048 chunks, the buffer order), so every tile is run exactly once."""
     if which == "prefill":
         pw = make_prefill()
         lq, lk = pw.lq, pw.lk
@@ -238,13 +238,13 @@ def test_tile_order_is_the_sorted_chunk_permutation(pvc, which):
         lq = rng.integers(20, 45, size=3000)
         lk = lq + rng.integers(0, 100, size=3000)
     cu_q, cu_k = _cu(lq), _cu(lk)
-    say(f"  tile order {which}: Tq={int(cu_q[-1])} requests={len(lq)}")
+    say(f"  tile order {which} causal={causal}: Tq={int(cu_q[-1])} requests={len(lq)}")
     plan = pvc.attn_plan_qk(dev_i32(cu_q), dev_i32(cu_k), int(cu_q[-1]), int(cu_k[-1]), int(np.max(lq)),
-                            int(np.max(lk)), True)
+                            int(np.max(lk)), causal)
     torch.cuda.synchronize()
     assert int(plan.dev_error.item()) == 0
     got = _plan_tile_order(plan)
-    want = _expected_tile_order(cu_q, cu_k, True)
+    want = _expected_tile_order(cu_q, cu_k, causal)
     nt = (int(cu_q[-1]) + 31) // 32
     assert np.array_equal(np.sort(got), np.arange(nt))
     assert np.array_equal(got, want)
